@@ -1,0 +1,165 @@
+"""ctypes wrapper of the float64 GDN oracle (``gdn_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py``. The HIP library never imports or links it, and it
+imports nothing from the HIP library.
+
+All functions take and return NumPy arrays in the logical layouts of
+``gdn_oracle.h`` (states as S[i][j], key index first). Inputs are the stored values
+(bf16 / fp32 widened exactly to float64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (strict IEEE float64, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("pool_slots", ctypes.c_int32), ("state_bf16", ctypes.c_int32),
+                ("scale", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int32)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_softplus.argtypes = [ctypes.c_double]
+        L.oracle_softplus.restype = ctypes.c_double
+        L.oracle_gates.argtypes = [ctypes.c_double] * 4 + [_D, _D]
+        L.oracle_gates.restype = None
+        L.oracle_round_bf16.argtypes = [ctypes.c_double]
+        L.oracle_round_bf16.restype = ctypes.c_double
+        L.oracle_round_bf16_f32bits.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
+        L.oracle_round_bf16_f32bits.restype = None
+        L.oracle_verify.argtypes = [ctypes.POINTER(Dims)] + [_D] * 7 + [_D, _I, _D, ctypes.c_int32,
+                                                                         ctypes.c_int32, _I, _D, ctypes.c_int32]
+        L.oracle_verify.restype = ctypes.c_int32
+        L.oracle_decode.argtypes = [ctypes.POINTER(Dims)] + [_D] * 7 + [_D, _I, _D, ctypes.c_int32]
+        L.oracle_decode.restype = ctypes.c_int32
+        L.oracle_commit.argtypes = [ctypes.POINTER(Dims), _D, ctypes.c_int32, _I, _I, _D, ctypes.c_int32]
+        L.oracle_commit.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _p(x: np.ndarray | None, t=_D):
+    return None if x is None else x.ctypes.data_as(t)
+
+
+def _nthreads(n):
+    return int(n) if n else (os.cpu_count() or 1)
+
+
+def softplus(x: float) -> float:
+    return lib().oracle_softplus(float(x))
+
+
+def gates(a: float, b: float, A_log: float, dt_bias: float) -> tuple[float, float]:
+    g, beta = ctypes.c_double(), ctypes.c_double()
+    lib().oracle_gates(float(a), float(b), float(A_log), float(dt_bias), ctypes.byref(g), ctypes.byref(beta))
+    return g.value, beta.value
+
+
+def round_bf16(x: float) -> float:
+    return lib().oracle_round_bf16(float(x))
+
+
+def round_bf16_f32bits(bits: np.ndarray, nthreads: int | None = None) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    out = np.empty(bits.shape, dtype=np.uint16)
+    lib().oracle_round_bf16_f32bits(bits.ctypes.data, out.ctypes.data, bits.size, _nthreads(nthreads))
+    return out
+
+
+def make_dims(batch, T, Hk, Hv, dk, dv, pool, state_bf16, scale=None, eps=1e-6) -> Dims:
+    return Dims(batch, T, Hk, Hv, dk, dv, pool, int(bool(state_bf16)),
+                float(dk ** -0.5 if scale is None else scale), float(eps))
+
+
+def verify(dims: Dims, q, k, v, a, b, A_log, dt_bias, pool, idx, *, cache_T: int = 0,
+           write_final: bool = False, prev_accept=None, cache_in=None,
+           nthreads: int | None = None) -> dict:
+    """Run T verify tokens per row. Returns dict(o, pool, cache) (new arrays).
+
+    ``cache_in`` is the cache content before the call (the previous step's
+    intermediates for a fused commit); rows the call does not write keep it.
+    """
+    B, T, Hv, dk, dv = dims.batch, dims.T, dims.num_v_heads, dims.d_k, dims.d_v
+    q, k, v, a, b = map(_f64, (q, k, v, a, b))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    pool = _f64(pool).copy()
+    idx = _i32(idx)
+    o = np.zeros((B, T, Hv, dv), dtype=np.float64)
+    cache = None
+    if cache_T:
+        cache = (_f64(cache_in).copy() if cache_in is not None
+                 else np.zeros((B, cache_T, Hv, dk, dv), dtype=np.float64))
+    pa = None if prev_accept is None else _i32(prev_accept)
+    rc = lib().oracle_verify(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log),
+                             _p(dt_bias), _p(pool), _p(idx, _I), _p(cache), int(cache_T),
+                             int(bool(write_final)), _p(pa, _I), _p(o), _nthreads(nthreads))
+    if rc:
+        raise ValueError("oracle_verify: invalid dimensions")
+    return dict(o=o, pool=pool, cache=cache)
+
+
+def decode(dims: Dims, q, k, v, a, b, A_log, dt_bias, pool, idx, *, nthreads: int | None = None) -> dict:
+    """One token per row; the state is updated in its pool slot. Returns dict(o, pool)."""
+    B, Hv, dv = dims.batch, dims.num_v_heads, dims.d_v
+    q, k, v, a, b = map(_f64, (q, k, v, a, b))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    pool = _f64(pool).copy()
+    idx = _i32(idx)
+    o = np.zeros((B, 1, Hv, dv), dtype=np.float64)
+    rc = lib().oracle_decode(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log),
+                             _p(dt_bias), _p(pool), _p(idx, _I), _p(o), _nthreads(nthreads))
+    if rc:
+        raise ValueError("oracle_decode: invalid dimensions")
+    return dict(o=o, pool=pool)
+
+
+def commit(dims: Dims, cache, cache_T: int, idx, accept, pool, *, nthreads: int | None = None) -> np.ndarray:
+    """Accepted-prefix commit. Returns the new pool."""
+    cache = _f64(cache)
+    pool = _f64(pool).copy()
+    rc = lib().oracle_commit(ctypes.byref(dims), _p(cache), int(cache_T), _p(_i32(idx), _I),
+                             _p(_i32(accept), _I), _p(pool), _nthreads(nthreads))
+    if rc:
+        raise ValueError("oracle_commit: invalid dimensions")
+    return pool

@@ -1,0 +1,197 @@
+"""Seeded synthetic workloads for the Gated DeltaNet (GDN) decode / speculative-verify path.
+
+This module only draws inputs. It holds none of the method's arithmetic: no gates,
+no recurrence, no rounding rule of the state. It serves the float64 oracle and the
+HIP path alike, which is the only thing the two share.
+
+Shapes and value distributions follow the serving workloads on the pages:
+- "[NVIDIA] [GDN] Enable FlashInfer MTP verify on SM100+ (Blackwell)", Throughput
+  Benchmark: 4 verify tokens per MTP step (3 drafts + 1), bf16 SSM state, batches of
+  tens to hundreds of running requests;
+- the TensorRT-LLM GB300 Qwen3.8-Flash-Next NVFP4 PR (20937), Results / What changes:
+  bf16 recurrent pools, MTP3 and MTP7 widths, concurrency 1..256;
+- the pool addressing (per-request slot index, -1 for padding) of the first page's
+  Summary and Requirements sections.
+
+Recipe (the same for every workload; one ``numpy.random.default_rng(seed)`` each,
+draws in this fixed order):
+1. slot indices: the first ``batch`` entries of a permutation of the pool, then
+   ``n_pad`` distinct rows set to -1 (padding);
+2. q, k ~ N(0,1), each (row, token, k-head) vector L2-normalised in float64 (the
+   workload is defined on unit-norm inputs); v, a, b ~ N(0,1);
+3. A_log = log U[1,16) and dt_bias ~ N(0, 0.1) per v-head (kept fp32);
+4. the state pool ~ N(0, 0.1), drawn in float32;
+5. accept lengths ~ U{1..T} (commit) and, for the fused-commit workload, the
+   previous step's accept lengths ~ U{1..cache_T} plus the previous step's cached
+   state at [row, n-1] ~ N(0, 0.1).
+Values are stored in the workload's io / state dtype (bf16 by round-to-nearest-even
+through torch). The stored values are the inputs; nobody re-derives them.
+
+Logical layouts (row-major): q, k [B,T,Hk,dk]; v [B,T,Hv,dv]; a, b [B,T,Hv];
+A_log, dt_bias [Hv]; pool [P,Hv,dk,dv] holding S[i][j] (i: key index, j: value
+index); cache [B,cache_T,Hv,dk,dv]. The device keeps states transposed
+([..., dv, dk]); ``to_device_state`` / ``from_device_state`` convert.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    T: int
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    pool: int
+    state_dtype: str          # "f32" | "bf16"
+    io_dtype: str             # "f32" | "bf16"
+    mode: str                 # "decode" | "verify" | "verify_fused"
+    cache_T: int = 0          # intermediate-state cache depth (0: none)
+    write_final: bool = False
+    commit: bool = False      # a separate commit follows the verify
+    n_pad: int = 0
+    fixed_indices: tuple | None = None
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dk)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the GDN hot path. Index 2 is the headline (MTP verify, T=4,
+# bf16 state); index 0 is small enough for brute force.
+WORKLOADS: list[Workload] = [
+    Workload("tiny-verify-t2-f32", batch=2, T=2, Hk=1, Hv=2, dk=16, dv=16, pool=4,
+             state_dtype="f32", io_dtype="f32", mode="verify", cache_T=2,
+             write_final=True, commit=True, fixed_indices=(2, 0),
+             description="tiny verify: B=2, Hk=1, Hv=2, d=16, T=2, fp32 state, pool of 4, slots [2,0]"),
+    Workload("decode-t1-f32", batch=64, T=1, Hk=4, Hv=8, dk=128, dv=128, pool=256,
+             state_dtype="f32", io_dtype="f32", mode="decode", n_pad=8,
+             description="single-token decode: B=64 (8 padding rows), Hk=4, Hv=8, d=128, fp32 state, pool of 256"),
+    Workload("mtp-verify-t4-bf16", batch=64, T=4, Hk=4, Hv=8, dk=128, dv=128, pool=256,
+             state_dtype="bf16", io_dtype="bf16", mode="verify", cache_T=4, commit=True,
+             description="MTP verify T=4: B=64, Hk=4, Hv=8, d=128, bf16 state, pool of 256, 4 intermediates + commit"),
+    Workload("verify-t4-b256-f32", batch=256, T=4, Hk=16, Hv=32, dk=128, dv=128, pool=512,
+             state_dtype="f32", io_dtype="f32", mode="verify", cache_T=4, commit=True,
+             description="high-concurrency verify T=4: B=256, Hk=16, Hv=32, d=128, fp32 state, pool of 512, 4 intermediates + commit"),
+    Workload("verify-t8-bf16-fused", batch=128, T=8, Hk=16, Hv=32, dk=128, dv=128, pool=1024,
+             state_dtype="bf16", io_dtype="bf16", mode="verify_fused", cache_T=8, n_pad=13,
+             description="long-draft verify T=8: B=128 (13 padding rows), Hk=16, Hv=32, d=128, bf16 state, pool of 1024, 8 intermediates, fused commit"),
+]
+
+HEADLINE = 2
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def _store(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """float64/float32 draw -> stored tensor of the given dtype (CPU)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch_dtype(dtype))
+
+
+def _unit(x: np.ndarray) -> np.ndarray:
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+
+
+def make_inputs(w: Workload, seed: int = 0) -> dict:
+    """Draw one batch of inputs for workload ``w``. Returns CPU torch tensors."""
+    rng = np.random.default_rng(seed)
+    B, T, Hk, Hv, dk, dv, P = w.batch, w.T, w.Hk, w.Hv, w.dk, w.dv, w.pool
+    # 1. slot indices
+    if w.fixed_indices is not None:
+        idx = np.asarray(w.fixed_indices, dtype=np.int32)
+        assert idx.shape == (B,)
+    else:
+        assert B <= P, "more rows than pool slots"
+        idx = rng.permutation(P)[:B].astype(np.int32)
+        if w.n_pad:
+            pad = rng.choice(B, size=w.n_pad, replace=False)
+            idx[pad] = -1
+    # 2. per-token inputs
+    q = _unit(rng.standard_normal((B, T, Hk, dk)))
+    k = _unit(rng.standard_normal((B, T, Hk, dk)))
+    v = rng.standard_normal((B, T, Hv, dv))
+    a = rng.standard_normal((B, T, Hv))
+    b = rng.standard_normal((B, T, Hv))
+    # 3. per-head parameters (fp32)
+    A_log = np.log(rng.uniform(1.0, 16.0, Hv))
+    dt_bias = rng.normal(0.0, 0.1, Hv)
+    # 4. state pool
+    pool = rng.standard_normal((P, Hv, dk, dv), dtype=np.float32)
+    pool *= np.float32(0.1)
+    out = dict(
+        idx=torch.from_numpy(idx),
+        q=_store(q, w.io_dtype), k=_store(k, w.io_dtype), v=_store(v, w.io_dtype),
+        a=_store(a, w.io_dtype), b=_store(b, w.io_dtype),
+        A_log=torch.from_numpy(A_log.astype(np.float32)),
+        dt_bias=torch.from_numpy(dt_bias.astype(np.float32)),
+        pool=_store(pool, w.state_dtype),
+    )
+    del pool
+    # 5. accept lengths and, for the fused commit, the previous step's cache
+    if w.commit:
+        out["accept"] = torch.from_numpy(rng.integers(1, T + 1, B).astype(np.int32))
+    if w.mode == "verify_fused":
+        prev = rng.integers(1, w.cache_T + 1, B).astype(np.int32)
+        out["prev_accept"] = torch.from_numpy(prev)
+        cache = torch.zeros((B, w.cache_T, Hv, dk, dv), dtype=torch_dtype(w.state_dtype))
+        for r in range(B):
+            if 0 <= idx[r] < P:
+                s = rng.standard_normal((Hv, dk, dv), dtype=np.float32) * np.float32(0.1)
+                cache[r, prev[r] - 1] = _store(s, w.state_dtype)
+        out["cache_prev"] = cache
+    return out
+
+
+def to_device_state(s: torch.Tensor) -> torch.Tensor:
+    """[..., dk, dv] logical state -> [..., dv, dk] device layout (contiguous)."""
+    return s.transpose(-1, -2).contiguous()
+
+
+def from_device_state(s: torch.Tensor) -> torch.Tensor:
+    """[..., dv, dk] device layout -> [..., dk, dv] logical state."""
+    return s.transpose(-1, -2)
+
+
+def algorithmic_bytes(w: Workload, idx: np.ndarray, kind: str) -> int:
+    """Bytes the method must move for one call: each valid (row, v-head) state tile
+    read once and written once per stored state, plus the per-token io.
+
+    kind: "verify" (this workload's verify/decode call) or "commit".
+    """
+    ssz = 4 if w.state_dtype == "f32" else 2
+    isz = 4 if w.io_dtype == "f32" else 2
+    valid = int(np.sum((idx >= 0) & (idx < w.pool)))
+    tile = w.dk * w.dv * ssz
+    tiles = valid * w.Hv
+    if kind == "commit":
+        return tiles * tile * 2 + valid * 4 * 2
+    writes = 0
+    if w.mode == "decode":
+        writes = 1
+    else:
+        writes = (w.T if w.cache_T else 0) + (1 if w.write_final else 0)
+        if w.mode == "verify_fused":
+            writes += 1
+    state = tiles * tile * (1 + writes)
+    B, T = w.batch, w.T
+    io = valid * T * (2 * w.Hk * w.dk + w.Hv * w.dv + 2 * w.Hv) * isz  # q, k, v, a, b of valid rows
+    io += B * T * w.Hv * w.dv * isz                                     # o, every row
+    io += B * 4 + 2 * w.Hv * 4                                          # indices, A_log, dt_bias
+    if w.mode == "verify_fused":
+        io += B * 4
+    return state + io
