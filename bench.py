@@ -1,0 +1,266 @@
+"""Benchmark of the GDN hot path on one MI355X.
+
+A step is one pass of the path over one batch: ``gdn_verify`` (T=4 tokens per
+request, every intermediate state stored) followed by ``gdn_commit`` of the accepted
+prefix, on the MTP verify workload (B=64, Hk=4, Hv=8, d=128, bf16 state, pool of
+256 slots; synthetic seeded inputs). Inputs are resident in HBM before timing starts.
+
+Timing: the steps run from a HIP graph (launch cost off the clock) over R rotating
+buffer sets whose combined footprint exceeds the 256 MB Infinity Cache, so every
+launch reads and writes HBM. W warm-up steps, then exactly K timed steps between two
+synchronisations; value = B*T*K / elapsed (tokens/s). The dominant kernel (verify) is
+also timed on its own the same way to give its average launch duration, from which
+the roofline fraction is computed with the algorithmic bytes of one call.
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published figure
+INFINITY_CACHE_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "csrc", "gdn_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload_name: str):
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"gdn_verify_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s: float) -> dict:
+    """The float64 oracle, as it stands, on the same inputs: full verify + commit calls,
+    repeated until the time budget is spent (at least once)."""
+    import oracle
+    import numpy as np
+    nthreads = min(16, os.cpu_count() or 1)
+    f = {n: x[n].double().numpy() for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "pool")}
+    idx, acc = x["idx"].numpy(), x["accept"].numpy()
+    d = oracle.make_dims(w.batch, w.T, w.Hk, w.Hv, w.dk, w.dv, w.pool, w.state_dtype == "bf16", scale=w.scale)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        r = oracle.verify(d, f["q"], f["k"], f["v"], f["a"], f["b"], f["A_log"], f["dt_bias"], f["pool"], idx,
+                          cache_T=w.cache_T, write_final=w.write_final, nthreads=nthreads)
+        oracle.commit(d, r["cache"], w.cache_T, idx, acc, r["pool"], nthreads=nthreads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    del np
+    return {"value": reps * w.batch * w.T / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{reps} full verify+commit calls of the workload (B*T={w.batch * w.T} tokens each) "
+                      f"in {el:.1f} s, float64, OpenMP over (row, v-head) tiles"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--workload", type=int, default=None, help="workload index (default: the MTP verify T=4 one)")
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the GDN state "
+              "update shards by head or request with no collective, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import linear_attention_speculative_gdn_amd as gdn
+    import workloads
+
+    wi = workloads.HEADLINE if args.workload is None else args.workload
+    w = workloads.WORKLOADS[wi]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wi}: {w.description}")
+    x = workloads.make_inputs(w, seed=0)
+    idx = x["idx"].numpy()
+    v_bytes = workloads.algorithmic_bytes(w, idx, "verify")
+    c_bytes = workloads.algorithmic_bytes(w, idx, "commit") if w.commit else 0
+
+    # rotating buffer sets: each launch touches memory the previous ones evicted
+    touched = v_bytes + c_bytes
+    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / touched))
+    base = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx")}
+    for n in ("accept", "prev_accept"):
+        if n in x:
+            base[n] = x[n].to(dev)
+    pool0 = workloads.to_device_state(x["pool"]).to(dev)
+    cache0 = None
+    if w.cache_T:
+        cache0 = (workloads.to_device_state(x["cache_prev"]).to(dev) if "cache_prev" in x else
+                  torch.zeros((w.batch, w.cache_T, w.Hv, w.dv, w.dk), dtype=pool0.dtype, device=dev))
+    sets = []
+    for _ in range(R):
+        s = {n: t.clone() for n, t in base.items()}
+        s["pool"] = pool0.clone()
+        s["cache"] = None if cache0 is None else cache0.clone()
+        s["o"] = torch.empty((w.batch, w.T, w.Hv, w.dv), dtype=x["v"].dtype, device=dev)
+        sets.append(s)
+    del pool0, cache0
+    torch.cuda.synchronize()
+    log(f"[bench] {R} rotating buffer sets, {touched / 1e6:.2f} MB touched per step")
+
+    def verify(s):
+        if w.mode == "decode":
+            gdn.gdn_decode(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"], s["pool"],
+                           s["idx"], scale=w.scale)
+        else:
+            gdn.gdn_verify(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"], s["pool"],
+                           s["idx"], s["cache"], w.write_final, s.get("prev_accept"), scale=w.scale)
+
+    def commit(s):
+        if w.commit:
+            gdn.gdn_commit(s["cache"], s["idx"], s["accept"], s["pool"])
+
+    def step(s):
+        verify(s)
+        commit(s)
+
+    stream = torch.cuda.Stream()
+
+    def make_runner(fn, n_per_replay):
+        """Returns run(n): n calls of fn over the rotating sets, from HIP graphs."""
+        if args.eager:
+            def run(n, start=[0]):
+                for i in range(n):
+                    fn(sets[(start[0] + i) % R])
+                start[0] += n
+            return run
+        graphs = {}
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    fn(sets[i % R])
+            return g
+
+        def run(n):
+            full, rest = divmod(n, n_per_replay)
+            if full and n_per_replay not in graphs:
+                graphs[n_per_replay] = capture(n_per_replay)
+            if rest and rest not in graphs:
+                graphs[rest] = capture(rest)
+            for _ in range(full):
+                graphs[n_per_replay].replay()
+            if rest:
+                graphs[rest].replay()
+        return run
+
+    step(sets[0])  # first launches load the code objects, outside any capture
+    torch.cuda.synchronize()
+    per_replay = R * max(1, 200 // R)
+    run_step = make_runner(step, per_replay)
+    run_verify = make_runner(verify, per_replay)
+
+    def timed(run, n):
+        cs = stream if not args.eager else torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cs):
+            e0.record(cs)
+            run(n)
+            e1.record(cs)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    with torch.cuda.stream(stream):
+        run_step(args.warmup)
+    torch.cuda.synchronize()
+    t_step = timed(run_step, args.steps)
+    log(f"[bench] {args.steps} steps in {t_step * 1e3:.3f} ms -> {t_step / args.steps * 1e6:.2f} us/step")
+
+    # the dominant kernel on its own, same protocol
+    with torch.cuda.stream(stream):
+        run_verify(args.warmup)
+    t_ver = timed(run_verify, args.steps)
+    us_ver = t_ver / args.steps * 1e6
+    achieved = v_bytes / (us_ver * 1e-6) / 1e9
+    log(f"[bench] verify alone: {us_ver:.2f} us/launch, {achieved:.1f} GB/s algorithmic "
+        f"({v_bytes / 1e6:.2f} MB), {achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s")
+
+    # practical ceiling: a plain device copy of 1 GiB, same event protocol
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    log(f"[bench] device copy ceiling: {copy_gbps:.1f} GB/s")
+
+    tokens = w.batch * w.T
+    value = tokens * args.steps / t_step
+    res = {
+        "metric": "GDN verify tokens/s (batch x T) + achieved HBM GB/s vs peak, T=4 bf16 state",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "T": w.T, "num_k_heads": w.Hk, "num_v_heads": w.Hv,
+                   "d_k": w.dk, "d_v": w.dv, "pool_slots": w.pool, "state_dtype": w.state_dtype,
+                   "io_dtype": w.io_dtype, "step": ("verify" if w.mode != "decode" else "decode") +
+                   (" + commit" if w.commit else ""), "rotating_buffer_sets": R,
+                   "launch": "eager" if args.eager else "hip_graph", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_profiles(w.name),
+                     "kernel": "gdn_verify (recurrent_kernel)", "algorithmic_bytes_per_launch": v_bytes,
+                     "avg_launch_us": us_ver},
+        "verify_tokens_per_s": tokens / (us_ver * 1e-6),
+        "copy_ceiling_GBps": copy_gbps,
+    }
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline ...")
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {res['cpu_baseline']['value']:.1f} tokens/s on {res['cpu_baseline']['cores']} threads")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

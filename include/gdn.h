@@ -1,0 +1,147 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet (GDN) state-update library:
+ * pooled-state decode, multi-token (MTP / speculative) verify with an intermediate-
+ * state cache, and accepted-prefix commit.
+ *
+ * Sources (pages by title, section):
+ * [P1] "[NVIDIA] [GDN] Enable FlashInfer MTP verify on SM100+ (Blackwell)" (SGLang PR
+ *      23273): Summary -- the verify kernel addresses each request's recurrent state in
+ *      a pool through initial_state_indices, and A_log is passed as fp32; Requirements
+ *      -- padding index guard for bf16 decode, bf16-state MTP beyond 4 tokens with
+ *      intermediate caching.
+ * [P2] "[GDN] Honor configured linear-attn verify backend in the kernel dispatcher"
+ *      (SGLang PR 34592): Motivation -- fp32 and bf16 SSM state must both work with MTP.
+ * [P3] TensorRT-LLM PR 20937, GB300 Qwen3.8-Flash-Next NVFP4 target: Per-File QA
+ *      Perspective and Moved out of this PR -- bf16 or fp32 recurrent pools, commit of
+ *      the accepted prefix in-kernel (below 16 requests) or by a separate all-layer
+ *      commit, duplicate rows, graph capture and replay.
+ *
+ * The update (the pages name the gated delta rule without printing it; this is its
+ * standard form). For request row r, v-head h, k-head kh = h / (Hv/Hk), token t:
+ *     q^ = q / sqrt(|q|^2 + eps),  k^ = k / sqrt(|k|^2 + eps)
+ *     g = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])),  beta = sigmoid(b)
+ *     S <- g S;  S <- S + beta k^ (v - S^T k^)^T;  o = scale * S^T q^
+ * S is a d_k x d_v matrix per (slot, v-head). With a bf16 state every stored state is
+ * rounded to nearest even and the rounded value is carried to the next token, so a
+ * T-token verify equals T single-token decodes and commit(n) equals intermediate n.
+ *
+ * Layouts (row-major, every pointer a device pointer owned by the caller):
+ *   q, k           [B][T][Hk][d_k]      io dtype
+ *   v, o           [B][T][Hv][d_v]      io dtype
+ *   a, b           [B][T][Hv]           io dtype
+ *   A_log, dt_bias [Hv]                 fp32
+ *   state_pool     [P][Hv][d_v][d_k]    state dtype: element [s][h][j][i] holds S[i][j]
+ *                                       (each value column of S is a contiguous row)
+ *   inter_cache    [B][cache_T][Hv][d_v][d_k]   state dtype, same per-tile layout
+ *   state_indices, accept lengths       [B] int32
+ *
+ * Conventions shared by every entry point:
+ * - A slot index outside [0, P) (the padding index -1 included) marks a padding row:
+ *   no state is read or written for it and its o rows are zeroed.
+ * - batch == 0 is a no-op that returns GDN_OK.
+ * - Host-checkable faults return an error before anything is launched; nothing is
+ *   written. A failed launch returns GDN_ERR_LAUNCH.
+ * - The library allocates nothing, never synchronises, keeps no global state and
+ *   launches exactly one kernel per call on `stream` (a hipStream_t; NULL is the
+ *   default stream). Calls are therefore thread-safe and may be captured in a HIP
+ *   graph.
+ * - Supported geometry: d_k in {16, 32, 64, 128, 256}; d_v a multiple of 16 in
+ *   [16, 256]; Hv a multiple of Hk; 1 <= T <= GDN_MAX_T.
+ * - Alignment: q, k, v, o, state_pool and inter_cache 16-byte aligned; the others
+ *   aligned to their element size.
+ * - Writing calls (decode, verify with write_final or a fused commit, commit) need
+ *   the valid indices of one call to be distinct; read-only verify allows repeats.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_API __attribute__((visibility("default")))
+#define GDN_MAX_T 16
+
+typedef enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype;
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* inconsistent or negative sizes */
+  GDN_ERR_DTYPE = 3,       /* unknown dtype value */
+  GDN_ERR_ALIGN = 4,       /* a pointer misses its alignment */
+  GDN_ERR_UNSUPPORTED = 5, /* valid but outside the supported geometry */
+  GDN_ERR_LAUNCH = 6       /* the kernel launch failed */
+} gdn_status;
+
+typedef struct {
+  int32_t batch;        /* B: request rows of this call (padding rows included) */
+  int32_t T;            /* tokens per row (1 for decode) */
+  int32_t num_k_heads;  /* Hk */
+  int32_t num_v_heads;  /* Hv, a multiple of Hk; v-head h uses k-head h / (Hv/Hk) */
+  int32_t d_k;          /* key dimension */
+  int32_t d_v;          /* value dimension */
+  int32_t pool_slots;   /* P */
+  gdn_dtype state_dtype;
+  gdn_dtype io_dtype;
+  float scale;          /* output scale, normally d_k^-1/2 */
+  float l2norm_eps;     /* q and k are L2-normalised in-kernel: x / sqrt(|x|^2 + eps) */
+} gdn_dims;
+
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  void* o;
+} gdn_io;
+
+/* Single-token decode [P1, Summary; Requirements]: for each row, the state of its
+ * slot is advanced by one token and written back in place; o receives the read-out.
+ * Needs dims->T == 1. Identical arithmetic to gdn_verify with T = 1, no cache and
+ * write_final = 1. */
+GDN_API gdn_status gdn_decode(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                      const int32_t* state_indices, void* stream);
+
+/* Multi-token verify [P1, Summary; Requirements; P2, Motivation]: T draft tokens per
+ * row run through the update, starting from the row's pool slot.
+ * inter_cache  NULL, or a cache of depth cache_T >= T: entry [r][t] receives the
+ *              state after token t (the intermediate-state cache that lets any
+ *              accepted prefix be restored). Entries t >= T and padding rows are
+ *              left untouched.
+ * write_final  1: the state after the last token is written back to the slot.
+ *              0: the pool is only read, so a rejected draft needs no rollback.
+ * prev_accept_len  NULL, or [B] accept lengths of the previous verify whose
+ *              intermediates are in inter_cache [P3, in-kernel commit]: for rows with
+ *              1 <= n <= cache_T the state starts from inter_cache[r][n-1], which is
+ *              also committed to the slot; other rows start from the slot. Exactly
+ *              gdn_commit(prev) followed by gdn_verify. Needs inter_cache; row r must
+ *              be the same request as in the previous verify. */
+GDN_API gdn_status gdn_verify(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                      const int32_t* state_indices, void* inter_cache, int32_t cache_T,
+                      int32_t write_final, const int32_t* prev_accept_len, void* stream);
+
+/* Accepted-prefix commit [P3, Per-File QA Perspective; Moved out of this PR]:
+ * state_pool[idx[r]] <- inter_cache[r][n-1] for every row with a valid slot and
+ * 1 <= n = accept_len[r] <= cache_T; all other rows leave the pool untouched.
+ * Reads dims->batch, num_v_heads, d_k, d_v, pool_slots and state_dtype only. */
+GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cache_T,
+                      const int32_t* state_indices, const int32_t* accept_len,
+                      void* state_pool, void* stream);
+
+/* Static text for a status code (never NULL). */
+GDN_API const char* gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library. */
+GDN_API int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

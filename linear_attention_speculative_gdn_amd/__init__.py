@@ -1,0 +1,191 @@
+"""Python binding of libgdn.so, the gfx950 Gated DeltaNet state-update library.
+
+Argument marshalling only: shapes, dtypes, devices and contiguity of torch tensors
+are turned into the plain pointers and sizes of ``include/gdn.h``, and the calls go
+through ctypes on the current HIP stream. Every step of decode, verify and commit
+runs in the HIP kernels; there is no other code path. If the library has not been
+built, importing works but the first call raises.
+
+Layouts (see include/gdn.h): q, k [B,T,Hk,dk]; v, o [B,T,Hv,dv]; a, b [B,T,Hv];
+A_log, dt_bias [Hv] fp32; state_pool [P,Hv,dv,dk]; inter_cache [B,cache_T,Hv,dv,dk];
+state_indices, accept lengths [B] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
+          5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
+EXPORTED = ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_status_string", "gdn_abi_version")
+GDN_MAX_T = 16
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("T", ctypes.c_int32), ("num_k_heads", ctypes.c_int32),
+                ("num_v_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("pool_slots", ctypes.c_int32), ("state_dtype", ctypes.c_int), ("io_dtype", ctypes.c_int),
+                ("scale", ctypes.c_float), ("l2norm_eps", ctypes.c_float)]
+
+
+class GdnIo(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with its C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        D, I = ctypes.POINTER(GdnDims), ctypes.POINTER(GdnIo)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.gdn_decode.argtypes = [D, I, vp, vp, vp]
+        L.gdn_verify.argtypes = [D, I, vp, vp, vp, i32, i32, vp, vp]
+        L.gdn_commit.argtypes = [D, vp, i32, vp, vp, vp, vp]
+        for f in ("gdn_decode", "gdn_verify", "gdn_commit"):
+            getattr(L, f).restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+def _raise(status: int, what: str):
+    if status != 0:
+        raise GdnError(status, f"{what}: {status_string(status)}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GDN_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, ndim: int, device: torch.device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, has {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims_io(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, scale, l2norm_eps):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    _need(q, "q", 4, dev); _need(k, "k", 4, dev); _need(v, "v", 4, dev); _need(o, "o", 4, dev)
+    _need(a, "a", 3, dev); _need(b, "b", 3, dev); _need(A_log, "A_log", 1, dev); _need(dt_bias, "dt_bias", 1, dev)
+    _need(state_pool, "state_pool", 4, dev); _need(state_indices, "state_indices", 1, dev)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    P = state_pool.shape[0]
+    if k.shape != q.shape or v.shape != (B, T, Hv, dv) or o.shape != v.shape:
+        raise ValueError("q/k/v/o shapes disagree")
+    if a.shape != (B, T, Hv) or b.shape != (B, T, Hv):
+        raise ValueError("a and b must be [B, T, Hv]")
+    if A_log.shape != (Hv,) or dt_bias.shape != (Hv,):
+        raise ValueError("A_log and dt_bias must be [Hv]")
+    if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise TypeError("A_log and dt_bias must be float32")
+    if state_pool.shape[1:] != (Hv, dv, dk):
+        raise ValueError(f"state_pool must be [P, Hv, dv, dk] = [P, {Hv}, {dv}, {dk}]")
+    if state_indices.shape != (B,) or state_indices.dtype != torch.int32:
+        raise ValueError("state_indices must be int32 [B]")
+    io_dt = _dt(q)
+    for name, t in (("k", k), ("v", v), ("a", a), ("b", b), ("o", o)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have the io dtype {q.dtype}")
+    dims = GdnDims(B, T, Hk, Hv, dk, dv, P, _dt(state_pool), io_dt,
+                   float(dk ** -0.5 if scale is None else scale), float(l2norm_eps))
+    io = GdnIo(q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
+               dt_bias.data_ptr(), o.data_ptr())
+    return dims, io
+
+
+def gdn_decode(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, *, scale=None,
+               l2norm_eps=1e-6, stream=None) -> None:
+    """One token per row; the state of each valid slot is updated in place; o is written."""
+    dims, io = _dims_io(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, scale, l2norm_eps)
+    st = lib().gdn_decode(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
+                          _stream(q.device, stream))
+    _raise(st, "gdn_decode")
+
+
+def gdn_verify(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, inter_cache=None,
+               write_final=False, prev_accept_len=None, *, scale=None, l2norm_eps=1e-6, stream=None) -> None:
+    """T tokens per row from its pool slot; see include/gdn.h for the cache, write_final
+    and fused-commit (prev_accept_len) semantics."""
+    dims, io = _dims_io(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, scale, l2norm_eps)
+    cache_T = 0
+    if inter_cache is not None:
+        _need(inter_cache, "inter_cache", 5, q.device)
+        if inter_cache.shape[0] != dims.batch or inter_cache.shape[2:] != state_pool.shape[1:]:
+            raise ValueError("inter_cache must be [B, cache_T, Hv, dv, dk]")
+        if inter_cache.dtype != state_pool.dtype:
+            raise TypeError("inter_cache must have the state dtype")
+        cache_T = inter_cache.shape[1]
+    if prev_accept_len is not None:
+        _need(prev_accept_len, "prev_accept_len", 1, q.device)
+        if prev_accept_len.shape != (dims.batch,) or prev_accept_len.dtype != torch.int32:
+            raise ValueError("prev_accept_len must be int32 [B]")
+    st = lib().gdn_verify(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
+                          _ptr(inter_cache), cache_T, int(bool(write_final)), _ptr(prev_accept_len),
+                          _stream(q.device, stream))
+    _raise(st, "gdn_verify")
+
+
+def gdn_commit(inter_cache, state_indices, accept_len, state_pool, *, stream=None) -> None:
+    """state_pool[idx[r]] <- inter_cache[r, n-1] for rows with a valid slot and 1 <= n <= cache_T."""
+    dev = inter_cache.device
+    _need(inter_cache, "inter_cache", 5, dev); _need(state_indices, "state_indices", 1, dev)
+    _need(accept_len, "accept_len", 1, dev); _need(state_pool, "state_pool", 4, dev)
+    B, cache_T, Hv, dv, dk = inter_cache.shape
+    if state_pool.shape[1:] != (Hv, dv, dk) or state_pool.dtype != inter_cache.dtype:
+        raise ValueError("state_pool must be [P, Hv, dv, dk] in the cache's dtype")
+    for name, t in (("state_indices", state_indices), ("accept_len", accept_len)):
+        if t.shape != (B,) or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32 [B]")
+    dims = GdnDims(B, 1, 1, Hv, dk, dv, state_pool.shape[0], _dt(state_pool), _dt(state_pool), 1.0, 0.0)
+    st = lib().gdn_commit(ctypes.byref(dims), _ptr(inter_cache), cache_T, _ptr(state_indices), _ptr(accept_len),
+                          _ptr(state_pool), _stream(dev, stream))
+    _raise(st, "gdn_commit")

@@ -1,0 +1,132 @@
+// gdn_api.cpp -- the C ABI of include/gdn.h: argument validation, kernel choice and
+// launch. No allocation, no synchronisation, no global state; one launch per call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+using gdn::Dt;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool dtype_ok(gdn_dtype d) { return d == GDN_DTYPE_F32 || d == GDN_DTYPE_BF16; }
+
+size_t dsize(gdn_dtype d) { return d == GDN_DTYPE_F32 ? 4 : 2; }
+
+bool dk_supported(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk == 128 || dk == 256; }
+
+// Checks shared by decode, verify and commit: sizes, dtypes, geometry.
+gdn_status check_dims(const gdn_dims* d, bool need_tokens) {
+  if (!d) return GDN_ERR_NULL;
+  if (d->batch < 0 || d->num_k_heads < 1 || d->num_v_heads < 1 || d->d_k < 1 || d->d_v < 1 ||
+      d->pool_slots < 0)
+    return GDN_ERR_SHAPE;
+  if (need_tokens && d->T < 1) return GDN_ERR_SHAPE;
+  if (d->num_v_heads % d->num_k_heads != 0) return GDN_ERR_SHAPE;
+  if (!dtype_ok(d->state_dtype) || !dtype_ok(d->io_dtype)) return GDN_ERR_DTYPE;
+  if (!dk_supported(d->d_k) || d->d_v % 16 != 0 || d->d_v > 256) return GDN_ERR_UNSUPPORTED;
+  if (need_tokens && d->T > GDN_MAX_T) return GDN_ERR_UNSUPPORTED;
+  // grid size and 32-bit row offsets inside the kernels
+  if (int64_t(d->batch) * d->num_v_heads * 16 > int64_t(INT32_MAX)) return GDN_ERR_UNSUPPORTED;
+  if (need_tokens && int64_t(d->batch) * d->T * d->num_v_heads > int64_t(INT32_MAX) / 256)
+    return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+// Rows of the value dimension per lane in the recurrent kernel: more rows per
+// workgroup for large grids (fewer, fatter workgroups), fewer for small ones.
+int pick_rows_per_lane(const gdn_dims* d) {
+  if (d->d_k != 128) return 1;
+  return 2;
+}
+
+gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const int32_t* idx,
+                         void* cache, int32_t cache_T, int32_t write_final,
+                         const int32_t* prev_accept, void* stream) {
+  if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
+      !pool || !idx)
+    return GDN_ERR_NULL;
+  if (prev_accept && !cache) return GDN_ERR_NULL;
+  if (cache && cache_T < d->T) return GDN_ERR_SHAPE;
+  const uintptr_t isz = dsize(d->io_dtype);
+  if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->o, 16) ||
+      !aligned(pool, 16) || (cache && !aligned(cache, 16)) || !aligned(io->a, isz) || !aligned(io->b, isz) ||
+      !aligned(io->A_log, 4) || !aligned(io->dt_bias, 4) || !aligned(idx, 4) ||
+      (prev_accept && !aligned(prev_accept, 4)))
+    return GDN_ERR_ALIGN;
+  if (d->batch == 0) return GDN_OK;
+
+  gdn::RecurrentArgs p;
+  p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
+  p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
+  p.pool = pool; p.idx = idx; p.cache = cache; p.prev_accept = prev_accept;
+  p.B = d->batch; p.T = d->T; p.Hk = d->num_k_heads; p.Hv = d->num_v_heads;
+  p.DK = d->d_k; p.DV = d->d_v; p.P = d->pool_slots; p.cache_T = cache ? cache_T : 0;
+  p.write_final = write_final ? 1 : 0;
+  p.scale = d->scale; p.eps = d->l2norm_eps;
+  const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(d->state_dtype), static_cast<Dt>(d->io_dtype),
+                                             pick_rows_per_lane(d), p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                      const int32_t* state_indices, void* stream) {
+  const gdn_status s = check_dims(dims, true);
+  if (s != GDN_OK) return s;
+  if (dims->T != 1) return GDN_ERR_SHAPE;
+  return run_recurrent(dims, io, state_pool, state_indices, nullptr, 0, 1, nullptr, stream);
+}
+
+gdn_status gdn_verify(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                      const int32_t* state_indices, void* inter_cache, int32_t cache_T,
+                      int32_t write_final, const int32_t* prev_accept_len, void* stream) {
+  const gdn_status s = check_dims(dims, true);
+  if (s != GDN_OK) return s;
+  return run_recurrent(dims, io, state_pool, state_indices, inter_cache, cache_T, write_final,
+                       prev_accept_len, stream);
+}
+
+gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cache_T,
+                      const int32_t* state_indices, const int32_t* accept_len, void* state_pool,
+                      void* stream) {
+  const gdn_status s = check_dims(dims, false);
+  if (s != GDN_OK) return s;
+  if (!inter_cache || !state_indices || !accept_len || !state_pool) return GDN_ERR_NULL;
+  if (cache_T < 1) return GDN_ERR_SHAPE;
+  if (!aligned(inter_cache, 16) || !aligned(state_pool, 16) || !aligned(state_indices, 4) ||
+      !aligned(accept_len, 4))
+    return GDN_ERR_ALIGN;
+  if (dims->batch == 0) return GDN_OK;
+  gdn::CommitArgs p;
+  p.cache = inter_cache; p.pool = state_pool; p.idx = state_indices; p.accept = accept_len;
+  p.B = dims->batch; p.Hv = dims->num_v_heads; p.P = dims->pool_slots; p.cache_T = cache_T;
+  p.tile_bytes = int64_t(dims->d_k) * dims->d_v * int64_t(dsize(dims->state_dtype));
+  const int64_t per_block = int64_t(gdn::kThreads) * gdn::kCommitChunksPerThread * 16;
+  p.blocks_per_tile = int32_t((p.tile_bytes + per_block - 1) / per_block);
+  const hipError_t e = gdn::launch_commit(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+const char* gdn_status_string(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK: success";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: inconsistent or negative sizes";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown dtype";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not aligned as required";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: geometry outside the supported set";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: kernel launch failed";
+  }
+  return "GDN: unknown status";
+}
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

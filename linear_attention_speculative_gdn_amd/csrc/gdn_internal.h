@@ -1,0 +1,54 @@
+// gdn_internal.h -- launch descriptors shared by the host entry points (gdn_api.cpp)
+// and the gfx950 kernels (gdn_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+// One launch of the recurrent kernel (decode, verify, verify with fused commit).
+struct RecurrentArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  void* o;
+  void* pool;
+  const int32_t* idx;
+  void* cache;                 // nullptr: no intermediate states
+  const int32_t* prev_accept;  // nullptr: no fused commit
+  int32_t B, T, Hk, Hv, DK, DV, P, cache_T;
+  int32_t write_final;
+  float scale, eps;
+};
+
+// One launch of the accepted-prefix commit copy.
+struct CommitArgs {
+  const void* cache;
+  void* pool;
+  const int32_t* idx;
+  const int32_t* accept;
+  int32_t B, Hv, P, cache_T;
+  int32_t blocks_per_tile;
+  int64_t tile_bytes;
+};
+
+// Rows of the value dimension one recurrent workgroup covers, for a key dimension,
+// a state dtype and a rows-per-lane factor (see the kernel's lane map).
+int rows_per_workgroup(int dk, int rows_per_lane);
+
+hipError_t launch_recurrent(Dt state, Dt io, int rows_per_lane, const RecurrentArgs& p,
+                            hipStream_t stream);
+hipError_t launch_commit(const CommitArgs& p, hipStream_t stream);
+
+constexpr int kCommitChunksPerThread = 4;
+constexpr int kThreads = 256;
+
+}  // namespace gdn

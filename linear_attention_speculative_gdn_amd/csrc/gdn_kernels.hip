@@ -1,0 +1,453 @@
+// gdn_kernels.hip -- gfx950 (CDNA4) kernels of the Gated DeltaNet state update for
+// pooled decode, multi-token (MTP / speculative) verify and accepted-prefix commit.
+//
+// The operation: the pages "[NVIDIA] [GDN] Enable FlashInfer MTP verify on SM100+
+// (Blackwell)" (Summary, Requirements) and TensorRT-LLM PR 20937 (Per-File QA
+// Perspective; Moved out of this PR) -- a per-request recurrent state gathered from a
+// pool by slot index, padding slots skipped, T draft tokens through the gated delta
+// rule, one cached state per token, fp32 or bf16 pools, commit of the accepted prefix.
+// Per token, with q^ and k^ the L2-normalised q and k:
+//     g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+//     S <- g S;  S <- S + beta k^ (v - S^T k^)^T;  o = scale S^T q^
+// evaluated here in the equivalent single-pass order
+//     rk = S^T k^, rq = S^T q^            (one pass over the old state)
+//     w  = beta (v - g rk)
+//     S  <- g S + k^ w^T                  (second pass, fused with the store)
+//     o  = scale (g rq + (k^.q^) w)
+// which needs no second reduction over the updated state.
+//
+// The work is rank-1 updates and matrix-vector products: about 3 flop per byte of
+// state traffic, far below the MI355X ridge, so the kernels are HBM-bound and use no
+// MFMA. Design for gfx950:
+// - the state of a (row, v-head) tile is stored value-column-major ([d_v][d_k], key
+//   index contiguous), so each value index j owns a contiguous row and the two
+//   reductions run along contiguous memory;
+// - a workgroup (4 wave64) covers one (row, v-head, block of value rows); each value
+//   row is spread over L = d_k/16 lanes holding 16 elements each, as 16-byte chunks
+//   l, l+L, l+2L, ... so one wave64 load/store instruction moves whole 128-byte lines;
+// - every global load (per-token inputs, then the state) is issued before the first
+//   store, so the in-order vector memory counter never makes a load wait on stores;
+// - the state stays in VGPRs across all T tokens; rk and rq are summed over the L
+//   lanes of a row with DPP (quad_perm, row_half_mirror, row_mirror), no LDS trip;
+// - the intermediate states are written with nontemporal 16-byte stores;
+// - bf16 states are rounded to nearest even with v_cvt_pk_bf16_f32 after every token
+//   and the rounded value is carried, so verify(T) equals T decodes bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// 16 bytes as a native vector (global_load/store_dwordx4, nontemporal builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct bf16s {
+  uint16_t bits;
+};
+
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------- io elements
+__device__ __forceinline__ float ld_io(const float* p) { return *p; }
+__device__ __forceinline__ float ld_io(const bf16s* p) { return __uint_as_float(uint32_t(p->bits) << 16); }
+__device__ __forceinline__ void st_io(float* p, float x) { *p = x; }
+__device__ __forceinline__ void st_io(bf16s* p, float x) { p->bits = uint16_t(pack_bf16x2(x, 0.f)); }
+
+// 16 bytes of io elements -> floats
+__device__ __forceinline__ void unpack_io(const u32x4& u, float* f, const float*) {
+  f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+  f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ void unpack_io(const u32x4& u, float* f, const bf16s*) {
+  f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+  f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+}
+
+// ---------------------------------------------------------------- state chunks
+// A chunk is 16 bytes of a state row: 4 fp32 or 8 bf16 elements.
+template <typename ST>
+struct Chunk;
+
+template <>
+struct Chunk<float> {
+  static constexpr int CE = 4;
+  __device__ __forceinline__ static void unpack(const u32x4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+  // fp32 state: storing is exact, nothing to round.
+  __device__ __forceinline__ static u32x4 pack_round(float* f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+};
+
+template <>
+struct Chunk<bf16s> {
+  static constexpr int CE = 8;
+  __device__ __forceinline__ static void unpack(const u32x4& u, float* f) {
+    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+  }
+  // bf16 state: round to nearest even and carry the rounded value in f.
+  __device__ __forceinline__ static u32x4 pack_round(float* f) {
+    u32x4 u;
+    u.x = pack_bf16x2(f[0], f[1]); u.y = pack_bf16x2(f[2], f[3]);
+    u.z = pack_bf16x2(f[4], f[5]); u.w = pack_bf16x2(f[6], f[7]);
+    unpack(u, f);
+    return u;
+  }
+};
+
+// ---------------------------------------------------------------- cross-lane sums
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over aligned groups of L lanes (L in {1,2,4,8,16}); every lane of a group gets
+// the same, bit-identical total (each step adds the same two partial sums).
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (L >= 2) x += dpp<kQuadXor1>(x);
+  if constexpr (L >= 4) x += dpp<kQuadXor2>(x);
+  if constexpr (L >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (L >= 16) x += dpp<kRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  const int i = __float_as_int(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(i, 0)) + __int_as_float(__builtin_amdgcn_readlane(i, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(i, 32)) + __int_as_float(__builtin_amdgcn_readlane(i, 48)));
+}
+
+__device__ __forceinline__ void st_nt(void* p, const u32x4& u) {
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+}
+
+// ---------------------------------------------------------------- recurrent kernel
+// Lane map: L = DK/16 lanes per value row, RW = 64/L rows per wave and slot, R slots
+// per lane; a workgroup of NW waves covers RPW = NW*R*RW value rows of one
+// (request row, v-head). Lane (grp = lane/L, l = lane%L) of wave w holds, for slot r,
+// value row jl = (w*R + r)*RW + grp and the chunks l + c*L (c < 16/CE) of that row.
+template <typename ST, typename IT, int DK, int R>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs p) {
+  constexpr int NW = kThreads / 64;
+  constexpr int L = DK / 16;
+  constexpr int RW = 64 / L;
+  constexpr int RPW = NW * R * RW;
+  constexpr int CE = Chunk<ST>::CE;
+  constexpr int NCH = 16 / CE;          // chunks per lane and row
+  constexpr int VE = 16 / sizeof(IT);   // io elements per 16-byte vector
+  constexpr int QV_MAX = (GDN_MAX_T * DK / VE + kThreads - 1) / kThreads;
+  constexpr int V_MAX = (GDN_MAX_T * RPW + kThreads - 1) / kThreads;
+
+  extern __shared__ float smem[];
+  const int T = p.T;
+  float* s_q = smem;                // [T][DK]  q, then q^
+  float* s_k = s_q + T * DK;        // [T][DK]  k, then k^
+  float* s_v = s_k + T * DK;        // [T][RPW] v of this block's rows
+  float* s_g = s_v + T * RPW;       // [T] decay
+  float* s_beta = s_g + T;          // [T] write strength
+  float* s_kq = s_beta + T;         // [T] k^.q^
+
+  const int nvb = (p.DV + RPW - 1) / RPW;
+  int bid = blockIdx.x;
+  const int vb = bid % nvb;
+  bid /= nvb;
+  const int h = bid % p.Hv;
+  const int row = bid / p.Hv;
+  const int kh = h / (p.Hv / p.Hk);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane / L, l = lane % L;
+  const int DV = p.DV;
+  const size_t tile = size_t(DK) * DV;
+
+  const IT* qp = static_cast<const IT*>(p.q);
+  const IT* kp = static_cast<const IT*>(p.k);
+  const IT* vp = static_cast<const IT*>(p.v);
+  const IT* ap = static_cast<const IT*>(p.a);
+  const IT* bp = static_cast<const IT*>(p.b);
+  IT* op = static_cast<IT*>(p.o);
+
+  const int32_t slot = p.idx[row];
+  if (slot < 0 || slot >= p.P) {  // padding row: o = 0, no state traffic
+    for (int e = tid; e < T * RPW; e += kThreads) {
+      const int t = e / RPW, j = vb * RPW + (e - t * RPW);
+      if (j < DV) st_io(op + (size_t(row * T + t) * p.Hv + h) * DV + j, 0.f);
+    }
+    return;
+  }
+
+  // ---- 1. per-token inputs, issued first (16-byte vectors for q and k)
+  const int nqv = T * (DK / VE);
+  u32x4 qraw[QV_MAX], kraw[QV_MAX];
+#pragma unroll
+  for (int it = 0; it < QV_MAX; ++it) {
+    const int e = tid + it * kThreads;
+    if (e < nqv) {
+      const int t = e / (DK / VE), c = e - t * (DK / VE);
+      const size_t off = (size_t(row * T + t) * p.Hk + kh) * DK + c * VE;
+      qraw[it] = *reinterpret_cast<const u32x4*>(qp + off);
+      kraw[it] = *reinterpret_cast<const u32x4*>(kp + off);
+    }
+  }
+  float vraw[V_MAX];
+#pragma unroll
+  for (int it = 0; it < V_MAX; ++it) {
+    const int e = tid + it * kThreads;
+    vraw[it] = 0.f;
+    if (e < T * RPW) {
+      const int t = e / RPW, j = vb * RPW + (e - t * RPW);
+      if (j < DV) vraw[it] = ld_io(vp + (size_t(row * T + t) * p.Hv + h) * DV + j);
+    }
+  }
+  float a_in = 0.f, b_in = 0.f;
+  if (tid < T) {
+    a_in = ld_io(ap + size_t(row * T + tid) * p.Hv + h);
+    b_in = ld_io(bp + size_t(row * T + tid) * p.Hv + h);
+  }
+
+  // ---- 2. the initial state: pool slot, or the previous step's accepted
+  //         intermediate for a fused commit
+  const ST* src = static_cast<const ST*>(p.pool) + (size_t(slot) * p.Hv + h) * tile;
+  bool commit_prev = false;
+  if (p.prev_accept) {
+    const int32_t n = p.prev_accept[row];
+    if (n >= 1 && n <= p.cache_T) {
+      src = static_cast<const ST*>(p.cache) + ((size_t(row) * p.cache_T + (n - 1)) * p.Hv + h) * tile;
+      commit_prev = true;
+    }
+  }
+  int jrow[R];
+  bool rv[R];
+  u32x4 raw[R][NCH];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    jrow[r] = vb * RPW + (wave * R + r) * RW + grp;
+    rv[r] = jrow[r] < DV;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      raw[r][c] = u32x4{0u, 0u, 0u, 0u};
+      if (rv[r]) raw[r][c] = *reinterpret_cast<const u32x4*>(src + size_t(jrow[r]) * DK + (l + c * L) * CE);
+    }
+  }
+
+  // ---- 3. per-token inputs -> LDS; gates
+#pragma unroll
+  for (int it = 0; it < QV_MAX; ++it) {
+    const int e = tid + it * kThreads;
+    if (e < nqv) {
+      float f[VE];
+      unpack_io(qraw[it], f, qp);
+#pragma unroll
+      for (int m = 0; m < VE; ++m) s_q[e * VE + m] = f[m];
+      unpack_io(kraw[it], f, kp);
+#pragma unroll
+      for (int m = 0; m < VE; ++m) s_k[e * VE + m] = f[m];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < V_MAX; ++it) {
+    const int e = tid + it * kThreads;
+    if (e < T * RPW) s_v[e] = vraw[it];
+  }
+  if (tid < T) {
+    const float x = a_in + p.dt_bias[h];
+    const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    s_g[tid] = expf(-expf(p.A_log[h]) * sp);
+    s_beta[tid] = 1.f / (1.f + expf(-b_in));
+  }
+  __syncthreads();
+
+  // ---- 4. L2 normalisation of q and k, and k^.q^, one wave per token
+  for (int t = wave; t < T; t += NW) {
+    float sq = 0.f, sk = 0.f, skq = 0.f;
+    for (int i = lane; i < DK; i += 64) {
+      const float qv = s_q[t * DK + i], kv = s_k[t * DK + i];
+      sq = fmaf(qv, qv, sq);
+      sk = fmaf(kv, kv, sk);
+      skq = fmaf(qv, kv, skq);
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    skq = wave_sum(skq);
+    const float rq = 1.f / sqrtf(sq + p.eps), rk = 1.f / sqrtf(sk + p.eps);
+    for (int i = lane; i < DK; i += 64) {
+      s_q[t * DK + i] *= rq;
+      s_k[t * DK + i] *= rk;
+    }
+    if (lane == 0) s_kq[t] = skq * rq * rk;
+  }
+  __syncthreads();
+
+  // ---- 5. state to registers; fused commit of the gathered state
+  float S[R][16];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) Chunk<ST>::unpack(raw[r][c], &S[r][c * CE]);
+
+  ST* const pool_tile = static_cast<ST*>(p.pool) + (size_t(slot) * p.Hv + h) * tile;
+  if (commit_prev) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (rv[r])
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          *reinterpret_cast<u32x4*>(pool_tile + size_t(jrow[r]) * DK + (l + c * L) * CE) = raw[r][c];
+  }
+
+  // ---- 6. the T tokens
+  ST* const cache_row = p.cache ? static_cast<ST*>(p.cache) + size_t(row) * p.cache_T * p.Hv * tile : nullptr;
+  const size_t cache_t_stride = size_t(p.Hv) * tile;
+  const float scale = p.scale;
+  for (int t = 0; t < T; ++t) {
+    float kh_[16], qh_[16];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int m = 0; m < CE; ++m) {
+        kh_[c * CE + m] = s_k[t * DK + (l + c * L) * CE + m];
+        qh_[c * CE + m] = s_q[t * DK + (l + c * L) * CE + m];
+      }
+    const float gt = s_g[t], bt = s_beta[t], kqt = s_kq[t];
+    float rk[R], rq[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float pk0 = 0.f, pk1 = 0.f, pq0 = 0.f, pq1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        pk0 = fmaf(S[r][e], kh_[e], pk0);
+        pk1 = fmaf(S[r][e + 1], kh_[e + 1], pk1);
+        pq0 = fmaf(S[r][e], qh_[e], pq0);
+        pq1 = fmaf(S[r][e + 1], qh_[e + 1], pq1);
+      }
+      rk[r] = group_sum<L>(pk0 + pk1);
+      rq[r] = group_sum<L>(pq0 + pq1);
+    }
+    ST* const cache_t = cache_row ? cache_row + t * cache_t_stride + h * tile : nullptr;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int jl = (wave * R + r) * RW + grp;
+      const float w = bt * (s_v[t * RPW + jl] - gt * rk[r]);
+      const float ov = (gt * rq[r] + kqt * w) * scale;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[r][e] = fmaf(gt, S[r][e], kh_[e] * w);
+      u32x4 packed[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) packed[c] = Chunk<ST>::pack_round(&S[r][c * CE]);
+      if (rv[r]) {
+        if (cache_t) {
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+            st_nt(cache_t + size_t(jrow[r]) * DK + (l + c * L) * CE, packed[c]);
+        }
+        if (l == 0) st_io(op + (size_t(row * T + t) * p.Hv + h) * DV + jrow[r], ov);
+      }
+    }
+  }
+
+  // ---- 7. final state back to the slot
+  if (p.write_final) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (rv[r])
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          *reinterpret_cast<u32x4*>(pool_tile + size_t(jrow[r]) * DK + (l + c * L) * CE) =
+              Chunk<ST>::pack_round(&S[r][c * CE]);
+  }
+}
+
+// ---------------------------------------------------------------- commit kernel
+// pool[idx[r], h] <- cache[r, n-1, h] for 1 <= n <= cache_T and a valid slot.
+// blocks_per_tile workgroups per (row, v-head), each copying kThreads*CPT chunks.
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
+  int bid = blockIdx.x;
+  const int blk = bid % p.blocks_per_tile;
+  bid /= p.blocks_per_tile;
+  const int h = bid % p.Hv;
+  const int row = bid / p.Hv;
+  const int32_t slot = p.idx[row], n = p.accept[row];
+  if (slot < 0 || slot >= p.P || n < 1 || n > p.cache_T) return;
+  const char* src = static_cast<const char*>(p.cache) + ((size_t(row) * p.cache_T + (n - 1)) * p.Hv + h) * p.tile_bytes;
+  char* dst = static_cast<char*>(p.pool) + (size_t(slot) * p.Hv + h) * p.tile_bytes;
+  const int64_t nchunks = p.tile_bytes / 16;
+  u32x4 buf[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t e = (int64_t(blk) * CPT + c) * kThreads + threadIdx.x;
+    if (e < nchunks) buf[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + e);
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t e = (int64_t(blk) * CPT + c) * kThreads + threadIdx.x;
+    if (e < nchunks) reinterpret_cast<u32x4*>(dst)[e] = buf[c];
+  }
+}
+
+template <typename ST, typename IT, int DK, int R>
+hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
+  constexpr int RPW = (kThreads / 64) * R * (64 / (DK / 16));
+  const int nvb = (p.DV + RPW - 1) / RPW;
+  const dim3 grid(unsigned(size_t(p.B) * p.Hv * nvb));
+  const size_t lds = sizeof(float) * (size_t(2) * p.T * DK + size_t(p.T) * RPW + 3 * size_t(p.T));
+  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R>), grid, dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <typename ST, typename IT>
+hipError_t launch_dk(int rows_per_lane, const RecurrentArgs& p, hipStream_t stream) {
+  switch (p.DK) {
+    case 16: return launch_rec<ST, IT, 16, 1>(p, stream);
+    case 32: return launch_rec<ST, IT, 32, 1>(p, stream);
+    case 64: return launch_rec<ST, IT, 64, 1>(p, stream);
+    case 128:
+      if (rows_per_lane == 1) return launch_rec<ST, IT, 128, 1>(p, stream);
+      if (rows_per_lane == 4) return launch_rec<ST, IT, 128, 4>(p, stream);
+      return launch_rec<ST, IT, 128, 2>(p, stream);
+    case 256: return launch_rec<ST, IT, 256, 1>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int rows_per_workgroup(int dk, int rows_per_lane) {
+  return (kThreads / 64) * rows_per_lane * (64 / (dk / 16));
+}
+
+hipError_t launch_recurrent(Dt state, Dt io, int rows_per_lane, const RecurrentArgs& p,
+                            hipStream_t stream) {
+  if (state == Dt::F32 && io == Dt::F32) return launch_dk<float, float>(rows_per_lane, p, stream);
+  if (state == Dt::F32 && io == Dt::BF16) return launch_dk<float, bf16s>(rows_per_lane, p, stream);
+  if (state == Dt::BF16 && io == Dt::F32) return launch_dk<bf16s, float>(rows_per_lane, p, stream);
+  return launch_dk<bf16s, bf16s>(rows_per_lane, p, stream);
+}
+
+hipError_t launch_commit(const CommitArgs& p, hipStream_t stream) {
+  const dim3 grid(unsigned(size_t(p.B) * p.Hv * p.blocks_per_tile));
+  hipLaunchKernelGGL((commit_kernel<kCommitChunksPerThread>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and the
+host-side validation returns the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_speculative_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return gdn.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_only_abi_symbols_exported(L):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert {s for s in syms if not s.startswith("_")} == set(gdn.EXPORTED)
+
+
+def test_abi_version_and_limits(L):
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define GDN_ABI_VERSION (\d+)", text).group(1))
+    assert L.gdn_abi_version() == ver
+    assert int(re.search(r"#define GDN_MAX_T (\d+)", text).group(1)) == gdn.GDN_MAX_T
+
+
+def test_status_strings(L):
+    for code, name in gdn.STATUS.items():
+        assert gdn.status_string(code).startswith(name)
+    assert "unknown" in gdn.status_string(99)
+
+
+# Fake device addresses: validation never dereferences them and returns before launch.
+A16 = 0x10000
+
+
+def dims(**kw):
+    base = dict(batch=4, T=4, num_k_heads=2, num_v_heads=4, d_k=128, d_v=128, pool_slots=8,
+                state_dtype=gdn.GDN_DTYPE_BF16, io_dtype=gdn.GDN_DTYPE_BF16, scale=128 ** -0.5, l2norm_eps=1e-6)
+    base.update(kw)
+    return gdn.GdnDims(**base)
+
+
+def io(**kw):
+    base = dict(q=A16, k=A16 * 2, v=A16 * 3, a=A16 * 4, b=A16 * 5, A_log=A16 * 6, dt_bias=A16 * 7, o=A16 * 8)
+    base.update(kw)
+    return gdn.GdnIo(**base)
+
+
+def verify(L, d, i, pool=A16 * 9, idx=A16 * 10, cache=A16 * 11, cache_T=4, wf=0, prev=None):
+    return L.gdn_verify(ctypes.byref(d) if d is not None else None, ctypes.byref(i) if i is not None else None,
+                        pool, idx, cache, cache_T, wf, prev, None)
+
+
+def test_verify_validation(L):
+    assert verify(L, dims(batch=0), io()) == 0                       # empty batch: no-op
+    assert verify(L, None, io()) == 1
+    assert verify(L, dims(batch=0), None) == 1
+    assert verify(L, dims(batch=0), io(q=None)) == 1
+    assert verify(L, dims(batch=0), io(), pool=None) == 1
+    assert verify(L, dims(batch=0), io(), idx=None) == 1
+    assert verify(L, dims(batch=0), io(), cache=None, prev=A16 * 12) == 1   # fused commit needs a cache
+    assert verify(L, dims(batch=-1), io()) == 2
+    assert verify(L, dims(T=0), io()) == 2
+    assert verify(L, dims(num_v_heads=3), io()) == 2                 # Hv % Hk != 0
+    assert verify(L, dims(batch=0), io(), cache_T=3) == 2            # cache shallower than T
+    assert verify(L, dims(state_dtype=7), io()) == 3
+    assert verify(L, dims(io_dtype=-1), io()) == 3
+    assert verify(L, dims(d_k=96), io()) == 5
+    assert verify(L, dims(d_v=120), io()) == 5
+    assert verify(L, dims(d_v=512), io()) == 5
+    assert verify(L, dims(T=gdn.GDN_MAX_T + 1), io(), cache_T=64) == 5
+    assert verify(L, dims(batch=0), io(q=A16 + 8)) == 4
+    assert verify(L, dims(batch=0), io(), pool=A16 * 9 + 4) == 4
+    assert verify(L, dims(batch=0), io(), cache=A16 * 11 + 2) == 4
+    assert verify(L, dims(batch=0), io(a=A16 * 4 + 1)) == 4
+    assert verify(L, dims(batch=0, io_dtype=gdn.GDN_DTYPE_F32), io(a=A16 * 4 + 2)) == 4
+    assert verify(L, dims(batch=0), io(A_log=A16 * 6 + 2)) == 4
+
+
+def test_decode_validation(L):
+    def dec(d, i, pool=A16 * 9, idx=A16 * 10):
+        return L.gdn_decode(ctypes.byref(d), ctypes.byref(i), pool, idx, None)
+    assert dec(dims(batch=0, T=1), io()) == 0
+    assert dec(dims(batch=0, T=2), io()) == 2                        # decode is one token
+    assert dec(dims(batch=0, T=1), io(), idx=None) == 1
+    assert dec(dims(batch=0, T=1, d_k=48), io()) == 5
+
+
+def test_commit_validation(L):
+    def com(d, cache=A16, cache_T=4, idx=A16 * 2, acc=A16 * 3, pool=A16 * 4):
+        return L.gdn_commit(ctypes.byref(d), cache, cache_T, idx, acc, pool, None)
+    assert com(dims(batch=0)) == 0
+    assert com(dims(batch=0), cache=None) == 1
+    assert com(dims(batch=0), acc=None) == 1
+    assert com(dims(batch=0), cache_T=0) == 2
+    assert com(dims(batch=0), pool=A16 * 4 + 8) == 4
+    assert com(dims(batch=0), acc=A16 * 3 + 2) == 4
+    assert com(dims(batch=0, d_v=8)) == 5
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 1, 16)
+    with pytest.raises(ValueError):
+        gdn.gdn_verify(x, x, x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1), torch.zeros(1), torch.zeros(1), x,
+                       torch.zeros(1, 1, 16, 16), torch.zeros(1, dtype=torch.int32))
