@@ -29,7 +29,8 @@ gdn_status check_dims(const gdn_dims* d, bool need_tokens) {
   if (!dtype_ok(d->state_dtype) || !dtype_ok(d->io_dtype)) return GDN_ERR_DTYPE;
   if (!dk_supported(d->d_k) || d->d_v % 16 != 0 || d->d_v > 256) return GDN_ERR_UNSUPPORTED;
   if (need_tokens && d->T > GDN_MAX_T) return GDN_ERR_UNSUPPORTED;
-  // grid size and 32-bit row offsets inside the kernels
+  // grid (v-blocks, Hv, B) limits and 32-bit row offsets inside the kernels
+  if (d->batch > 65535 || d->num_v_heads > 65535) return GDN_ERR_UNSUPPORTED;
   if (int64_t(d->batch) * d->num_v_heads * 16 > int64_t(INT32_MAX)) return GDN_ERR_UNSUPPORTED;
   if (need_tokens && int64_t(d->batch) * d->T * d->num_v_heads > int64_t(INT32_MAX) / 256)
     return GDN_ERR_UNSUPPORTED;
@@ -65,6 +66,7 @@ gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const 
   p.pool = pool; p.idx = idx; p.cache = cache; p.prev_accept = prev_accept;
   p.B = d->batch; p.T = d->T; p.Hk = d->num_k_heads; p.Hv = d->num_v_heads;
   p.DK = d->d_k; p.DV = d->d_v; p.P = d->pool_slots; p.cache_T = cache ? cache_T : 0;
+  p.G = d->num_v_heads / d->num_k_heads;
   p.write_final = write_final ? 1 : 0;
   p.scale = d->scale; p.eps = d->l2norm_eps;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(d->state_dtype), static_cast<Dt>(d->io_dtype),

@@ -25,6 +25,7 @@ struct RecurrentArgs {
   void* cache;                 // nullptr: no intermediate states
   const int32_t* prev_accept;  // nullptr: no fused commit
   int32_t B, T, Hk, Hv, DK, DV, P, cache_T;
+  int32_t G;                   // v-heads per k-head (Hv / Hk)
   int32_t write_final;
   float scale, eps;
 };

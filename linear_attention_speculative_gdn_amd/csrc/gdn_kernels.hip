@@ -44,6 +44,7 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 // 16 bytes as a native vector (global_load/store_dwordx4, nontemporal builtins).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct bf16s {
@@ -147,19 +148,25 @@ __device__ __forceinline__ void st_nt(void* p, const u32x4& u) {
 // per lane; a workgroup of NW waves covers RPW = NW*R*RW value rows of one
 // (request row, v-head). Lane (grp = lane/L, l = lane%L) of wave w holds, for slot r,
 // value row jl = (w*R + r)*RW + grp and the chunks l + c*L (c < 16/CE) of that row.
-template <typename ST, typename IT, int DK, int R>
-__global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs p) {
-  constexpr int NW = kThreads / 64;
+//
+// Every global load is unconditional, from an address clamped into its buffer, and
+// out-of-range lanes discard the value afterwards: a load inside a branch would be
+// waited on at the end of the branch, which serialises the memory round trips.
+template <typename ST, typename IT, int DK, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs p) {
+  constexpr int NT = NW * 64;
   constexpr int L = DK / 16;
   constexpr int RW = 64 / L;
   constexpr int RPW = NW * R * RW;
   constexpr int CE = Chunk<ST>::CE;
-  constexpr int NCH = 16 / CE;          // chunks per lane and row
-  constexpr int VE = 16 / sizeof(IT);   // io elements per 16-byte vector
-  constexpr int QV_MAX = (GDN_MAX_T * DK / VE + kThreads - 1) / kThreads;
-  constexpr int V_MAX = (GDN_MAX_T * RPW + kThreads - 1) / kThreads;
+  constexpr int NCH = 16 / CE;           // chunks per lane and row
+  constexpr int VE = 16 / sizeof(IT);    // io elements per 16-byte vector
+  constexpr int QVEC = DK / VE;          // vectors of one token's q (or k)
+  constexpr int VVEC = RPW / VE;         // vectors of one token's v rows of this block
+  constexpr int NQ = (GDN_MAX_T * QVEC + NT - 1) / NT;
+  constexpr int NV = (GDN_MAX_T * VVEC + NT - 1) / NT;
 
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   const int T = p.T;
   float* s_q = smem;                // [T][DK]  q, then q^
   float* s_k = s_q + T * DK;        // [T][DK]  k, then k^
@@ -168,13 +175,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
   float* s_beta = s_g + T;          // [T] write strength
   float* s_kq = s_beta + T;         // [T] k^.q^
 
-  const int nvb = (p.DV + RPW - 1) / RPW;
-  int bid = blockIdx.x;
-  const int vb = bid % nvb;
-  bid /= nvb;
-  const int h = bid % p.Hv;
-  const int row = bid / p.Hv;
-  const int kh = h / (p.Hv / p.Hk);
+  // grid (v-block, v-head, row): no integer division on the way to the first loads
+  const int vb = blockIdx.x;
+  const int h = blockIdx.y;
+  const int row = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane / L, l = lane % L;
   const int DV = p.DV;
@@ -188,54 +192,48 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
   IT* op = static_cast<IT*>(p.o);
 
   const int32_t slot = p.idx[row];
+  const int32_t n_prev = p.prev_accept ? p.prev_accept[row] : 0;
+  const int kh = h / p.G;
+
+  // ---- 1. per-token inputs (do not depend on the slot): q, k, v as 16-byte vectors
+  const int nq = T * QVEC, nv = T * VVEC;
+  u32x4 qraw[NQ], kraw[NQ], vraw[NV];
+#pragma unroll
+  for (int it = 0; it < NQ; ++it) {
+    const int e = min(tid + it * NT, nq - 1);
+    const int t = e / QVEC, c = e - t * QVEC;
+    const size_t off = (size_t(row * T + t) * p.Hk + kh) * DK + c * VE;
+    qraw[it] = *reinterpret_cast<const u32x4*>(qp + off);
+    kraw[it] = *reinterpret_cast<const u32x4*>(kp + off);
+  }
+#pragma unroll
+  for (int it = 0; it < NV; ++it) {
+    const int e = min(tid + it * NT, nv - 1);
+    const int t = e / VVEC, c = e - t * VVEC;
+    const int j = min(vb * RPW + c * VE, DV - VE);
+    vraw[it] = *reinterpret_cast<const u32x4*>(vp + (size_t(row * T + t) * p.Hv + h) * DV + j);
+  }
+  const int tg = min(tid, T - 1);
+  const float a_in = ld_io(ap + size_t(row * T + tg) * p.Hv + h);
+  const float b_in = ld_io(bp + size_t(row * T + tg) * p.Hv + h);
+  // keep the loads above issued before the wait on the slot index (they must not
+  // be sunk into the non-padding branch)
+  asm volatile("" ::: "memory");
+
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0, no state traffic
-    for (int e = tid; e < T * RPW; e += kThreads) {
+    for (int e = tid; e < T * RPW; e += NT) {
       const int t = e / RPW, j = vb * RPW + (e - t * RPW);
       if (j < DV) st_io(op + (size_t(row * T + t) * p.Hv + h) * DV + j, 0.f);
     }
     return;
   }
 
-  // ---- 1. per-token inputs, issued first (16-byte vectors for q and k)
-  const int nqv = T * (DK / VE);
-  u32x4 qraw[QV_MAX], kraw[QV_MAX];
-#pragma unroll
-  for (int it = 0; it < QV_MAX; ++it) {
-    const int e = tid + it * kThreads;
-    if (e < nqv) {
-      const int t = e / (DK / VE), c = e - t * (DK / VE);
-      const size_t off = (size_t(row * T + t) * p.Hk + kh) * DK + c * VE;
-      qraw[it] = *reinterpret_cast<const u32x4*>(qp + off);
-      kraw[it] = *reinterpret_cast<const u32x4*>(kp + off);
-    }
-  }
-  float vraw[V_MAX];
-#pragma unroll
-  for (int it = 0; it < V_MAX; ++it) {
-    const int e = tid + it * kThreads;
-    vraw[it] = 0.f;
-    if (e < T * RPW) {
-      const int t = e / RPW, j = vb * RPW + (e - t * RPW);
-      if (j < DV) vraw[it] = ld_io(vp + (size_t(row * T + t) * p.Hv + h) * DV + j);
-    }
-  }
-  float a_in = 0.f, b_in = 0.f;
-  if (tid < T) {
-    a_in = ld_io(ap + size_t(row * T + tid) * p.Hv + h);
-    b_in = ld_io(bp + size_t(row * T + tid) * p.Hv + h);
-  }
-
-  // ---- 2. the initial state: pool slot, or the previous step's accepted
+  // ---- 2. the initial state: the pool slot, or the previous step's accepted
   //         intermediate for a fused commit
-  const ST* src = static_cast<const ST*>(p.pool) + (size_t(slot) * p.Hv + h) * tile;
-  bool commit_prev = false;
-  if (p.prev_accept) {
-    const int32_t n = p.prev_accept[row];
-    if (n >= 1 && n <= p.cache_T) {
-      src = static_cast<const ST*>(p.cache) + ((size_t(row) * p.cache_T + (n - 1)) * p.Hv + h) * tile;
-      commit_prev = true;
-    }
-  }
+  const bool commit_prev = n_prev >= 1 && n_prev <= p.cache_T;
+  const ST* src = commit_prev
+                      ? static_cast<const ST*>(p.cache) + ((size_t(row) * p.cache_T + (n_prev - 1)) * p.Hv + h) * tile
+                      : static_cast<const ST*>(p.pool) + (size_t(slot) * p.Hv + h) * tile;
   int jrow[R];
   bool rv[R];
   u32x4 raw[R][NCH];
@@ -243,18 +241,17 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
   for (int r = 0; r < R; ++r) {
     jrow[r] = vb * RPW + (wave * R + r) * RW + grp;
     rv[r] = jrow[r] < DV;
+    const int jr = min(jrow[r], DV - 1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      raw[r][c] = u32x4{0u, 0u, 0u, 0u};
-      if (rv[r]) raw[r][c] = *reinterpret_cast<const u32x4*>(src + size_t(jrow[r]) * DK + (l + c * L) * CE);
-    }
+    for (int c = 0; c < NCH; ++c)
+      raw[r][c] = *reinterpret_cast<const u32x4*>(src + size_t(jr) * DK + (l + c * L) * CE);
   }
 
   // ---- 3. per-token inputs -> LDS; gates
 #pragma unroll
-  for (int it = 0; it < QV_MAX; ++it) {
-    const int e = tid + it * kThreads;
-    if (e < nqv) {
+  for (int it = 0; it < NQ; ++it) {
+    const int e = tid + it * NT;
+    if (e < nq) {
       float f[VE];
       unpack_io(qraw[it], f, qp);
 #pragma unroll
@@ -265,9 +262,16 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
     }
   }
 #pragma unroll
-  for (int it = 0; it < V_MAX; ++it) {
-    const int e = tid + it * kThreads;
-    if (e < T * RPW) s_v[e] = vraw[it];
+  for (int it = 0; it < NV; ++it) {
+    const int e = tid + it * NT;
+    if (e < nv) {
+      float f[VE];
+      unpack_io(vraw[it], f, vp);
+      const int t = e / VVEC, c = e - t * VVEC;
+      const bool ok = vb * RPW + c * VE < DV;
+#pragma unroll
+      for (int m = 0; m < VE; ++m) s_v[t * RPW + c * VE + m] = ok ? f[m] : 0.f;
+    }
   }
   if (tid < T) {
     const float x = a_in + p.dt_bias[h];
@@ -278,21 +282,30 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
   __syncthreads();
 
   // ---- 4. L2 normalisation of q and k, and k^.q^, one wave per token
+  constexpr int PL = (DK + 63) / 64;  // elements per lane
   for (int t = wave; t < T; t += NW) {
+    float qv[PL], kv[PL];
     float sq = 0.f, sk = 0.f, skq = 0.f;
-    for (int i = lane; i < DK; i += 64) {
-      const float qv = s_q[t * DK + i], kv = s_k[t * DK + i];
-      sq = fmaf(qv, qv, sq);
-      sk = fmaf(kv, kv, sk);
-      skq = fmaf(qv, kv, skq);
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      const int i = lane + u * 64;
+      qv[u] = (DK >= 64 || i < DK) ? s_q[t * DK + i] : 0.f;
+      kv[u] = (DK >= 64 || i < DK) ? s_k[t * DK + i] : 0.f;
+      sq = fmaf(qv[u], qv[u], sq);
+      sk = fmaf(kv[u], kv[u], sk);
+      skq = fmaf(qv[u], kv[u], skq);
     }
     sq = wave_sum(sq);
     sk = wave_sum(sk);
     skq = wave_sum(skq);
     const float rq = 1.f / sqrtf(sq + p.eps), rk = 1.f / sqrtf(sk + p.eps);
-    for (int i = lane; i < DK; i += 64) {
-      s_q[t * DK + i] *= rq;
-      s_k[t * DK + i] *= rk;
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      const int i = lane + u * 64;
+      if (DK >= 64 || i < DK) {
+        s_q[t * DK + i] = qv[u] * rq;
+        s_k[t * DK + i] = kv[u] * rk;
+      }
     }
     if (lane == 0) s_kq[t] = skq * rq * rk;
   }
@@ -319,14 +332,20 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
   ST* const cache_row = p.cache ? static_cast<ST*>(p.cache) + size_t(row) * p.cache_T * p.Hv * tile : nullptr;
   const size_t cache_t_stride = size_t(p.Hv) * tile;
   const float scale = p.scale;
+  const f32x4* s_k4 = reinterpret_cast<const f32x4*>(s_k);
+  const f32x4* s_q4 = reinterpret_cast<const f32x4*>(s_q);
   for (int t = 0; t < T; ++t) {
     float kh_[16], qh_[16];
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int m = 0; m < CE; ++m) {
-        kh_[c * CE + m] = s_k[t * DK + (l + c * L) * CE + m];
-        qh_[c * CE + m] = s_q[t * DK + (l + c * L) * CE + m];
+      for (int m4 = 0; m4 < CE / 4; ++m4) {
+        const int i4 = (t * DK + (l + c * L) * CE) / 4 + m4;
+        const f32x4 kk = s_k4[i4], qq = s_q4[i4];
+        kh_[c * CE + m4 * 4 + 0] = kk.x; kh_[c * CE + m4 * 4 + 1] = kk.y;
+        kh_[c * CE + m4 * 4 + 2] = kk.z; kh_[c * CE + m4 * 4 + 3] = kk.w;
+        qh_[c * CE + m4 * 4 + 0] = qq.x; qh_[c * CE + m4 * 4 + 1] = qq.y;
+        qh_[c * CE + m4 * 4 + 2] = qq.z; qh_[c * CE + m4 * 4 + 3] = qq.w;
       }
     const float gt = s_g[t], bt = s_beta[t], kqt = s_kq[t];
     float rk[R], rq[R];
@@ -379,14 +398,11 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(const RecurrentArgs
 
 // ---------------------------------------------------------------- commit kernel
 // pool[idx[r], h] <- cache[r, n-1, h] for 1 <= n <= cache_T and a valid slot.
-// blocks_per_tile workgroups per (row, v-head), each copying kThreads*CPT chunks.
+// blocks_per_tile workgroups per (row, v-head), each copying kThreads*CPT chunks;
+// a tile is read once (nontemporal: nothing reads the cache entry again) and written once.
 template <int CPT>
 __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
-  int bid = blockIdx.x;
-  const int blk = bid % p.blocks_per_tile;
-  bid /= p.blocks_per_tile;
-  const int h = bid % p.Hv;
-  const int row = bid / p.Hv;
+  const int blk = blockIdx.x, h = blockIdx.y, row = blockIdx.z;  // grid (blocks, Hv, B)
   const int32_t slot = p.idx[row], n = p.accept[row];
   if (slot < 0 || slot >= p.P || n < 1 || n > p.cache_T) return;
   const char* src = static_cast<const char*>(p.cache) + ((size_t(row) * p.cache_T + (n - 1)) * p.Hv + h) * p.tile_bytes;
@@ -405,13 +421,13 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
   }
 }
 
-template <typename ST, typename IT, int DK, int R>
+template <typename ST, typename IT, int DK, int R, int NW = 4>
 hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
-  constexpr int RPW = (kThreads / 64) * R * (64 / (DK / 16));
+  constexpr int RPW = NW * R * (64 / (DK / 16));
   const int nvb = (p.DV + RPW - 1) / RPW;
-  const dim3 grid(unsigned(size_t(p.B) * p.Hv * nvb));
+  const dim3 grid(unsigned(nvb), unsigned(p.Hv), unsigned(p.B));
   const size_t lds = sizeof(float) * (size_t(2) * p.T * DK + size_t(p.T) * RPW + 3 * size_t(p.T));
-  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R>), grid, dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW>), grid, dim3(NW * 64), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -424,6 +440,8 @@ hipError_t launch_dk(int rows_per_lane, const RecurrentArgs& p, hipStream_t stre
     case 128:
       if (rows_per_lane == 1) return launch_rec<ST, IT, 128, 1>(p, stream);
       if (rows_per_lane == 4) return launch_rec<ST, IT, 128, 4>(p, stream);
+      if (rows_per_lane == 12) return launch_rec<ST, IT, 128, 1, 8>(p, stream);
+      if (rows_per_lane == 22) return launch_rec<ST, IT, 128, 2, 8>(p, stream);
       return launch_rec<ST, IT, 128, 2>(p, stream);
     case 256: return launch_rec<ST, IT, 256, 1>(p, stream);
     default: return hipErrorInvalidValue;
@@ -445,7 +463,7 @@ hipError_t launch_recurrent(Dt state, Dt io, int rows_per_lane, const RecurrentA
 }
 
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream) {
-  const dim3 grid(unsigned(size_t(p.B) * p.Hv * p.blocks_per_tile));
+  const dim3 grid(unsigned(p.blocks_per_tile), unsigned(p.Hv), unsigned(p.B));
   hipLaunchKernelGGL((commit_kernel<kCommitChunksPerThread>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

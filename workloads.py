@@ -167,6 +167,13 @@ def from_device_state(s: torch.Tensor) -> torch.Tensor:
     return s.transpose(-1, -2)
 
 
+def state_read_bytes(w: Workload, idx: np.ndarray) -> int:
+    """Bytes of state one call reads (one tile per valid row and v-head)."""
+    ssz = 4 if w.state_dtype == "f32" else 2
+    valid = int(np.sum((idx >= 0) & (idx < w.pool)))
+    return valid * w.Hv * w.dk * w.dv * ssz
+
+
 def algorithmic_bytes(w: Workload, idx: np.ndarray, kind: str) -> int:
     """Bytes the method must move for one call: each valid (row, v-head) state tile
     read once and written once per stored state, plus the per-token io.
