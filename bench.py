@@ -83,12 +83,14 @@ def cpu_baseline(w, x, budget_s: float) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4000)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=8000)
+    ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--workload", type=int, default=None, help="workload index (default: the MTP verify T=4 one)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device copy (known bytes) for counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the GDN state "
@@ -111,13 +113,15 @@ def main():
     v_bytes = workloads.algorithmic_bytes(w, idx, "verify")
     c_bytes = workloads.algorithmic_bytes(w, idx, "commit") if w.commit else 0
 
-    # rotating buffer sets: each launch touches memory the previous ones evicted
+    # Rotating buffer sets, so that every launch reads its state from HBM: the pool
+    # reads of all sets together exceed the 256 MB Infinity Cache four times over
+    # (nontemporal cache writes do not displace them, so only the reads are counted).
+    # Slot indices and accept lengths are shared by all sets, as every GDN layer of a
+    # serving step uses the same ones; everything else is per set.
     touched = v_bytes + c_bytes
-    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / touched))
-    base = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx")}
-    for n in ("accept", "prev_accept"):
-        if n in x:
-            base[n] = x[n].to(dev)
+    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / workloads.state_read_bytes(w, idx)))
+    shared = {n: x[n].to(dev) for n in ("idx", "accept", "prev_accept") if n in x}
+    base = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
     pool0 = workloads.to_device_state(x["pool"]).to(dev)
     cache0 = None
     if w.cache_T:
@@ -126,6 +130,7 @@ def main():
     sets = []
     for _ in range(R):
         s = {n: t.clone() for n, t in base.items()}
+        s.update(shared)
         s["pool"] = pool0.clone()
         s["cache"] = None if cache0 is None else cache0.clone()
         s["o"] = torch.empty((w.batch, w.T, w.Hv, w.dv), dtype=x["v"].dtype, device=dev)
@@ -212,6 +217,17 @@ def main():
     achieved = v_bytes / (us_ver * 1e-6) / 1e9
     log(f"[bench] verify alone: {us_ver:.2f} us/launch, {achieved:.1f} GB/s algorithmic "
         f"({v_bytes / 1e6:.2f} MB), {achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s")
+
+    if args.calibrate_copy:
+        # 256 MiB read + 256 MiB written, launched alone: the reference for scaling
+        # FETCH_SIZE / WRITE_SIZE counters to bytes
+        a_ = torch.ones(1 << 27, dtype=torch.bfloat16, device=dev)
+        b_ = torch.empty_like(a_)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b_.copy_(a_)
+            torch.cuda.synchronize()
+        del a_, b_
 
     # practical ceiling: a plain device copy of 1 GiB, same event protocol
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1)

@@ -38,7 +38,8 @@
  * Conventions shared by every entry point:
  * - A slot index outside [0, P) (the padding index -1 included) marks a padding row:
  *   no state is read or written for it and its o rows are zeroed.
- * - batch == 0 is a no-op that returns GDN_OK.
+ * - batch == 0 is a no-op that returns GDN_OK once the sizes and dtypes are valid;
+ *   the pointers are not examined then (empty tensors may have NULL data).
  * - Host-checkable faults return an error before anything is launched; nothing is
  *   written. A failed launch returns GDN_ERR_LAUNCH.
  * - The library allocates nothing, never synchronises, keeps no global state and

@@ -47,6 +47,7 @@ int pick_rows_per_lane(const gdn_dims* d) {
 gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const int32_t* idx,
                          void* cache, int32_t cache_T, int32_t write_final,
                          const int32_t* prev_accept, void* stream) {
+  if (d->batch == 0) return GDN_OK;
   if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
       !pool || !idx)
     return GDN_ERR_NULL;
@@ -58,7 +59,6 @@ gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const 
       !aligned(io->A_log, 4) || !aligned(io->dt_bias, 4) || !aligned(idx, 4) ||
       (prev_accept && !aligned(prev_accept, 4)))
     return GDN_ERR_ALIGN;
-  if (d->batch == 0) return GDN_OK;
 
   gdn::RecurrentArgs p;
   p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
@@ -100,12 +100,12 @@ gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cac
                       void* stream) {
   const gdn_status s = check_dims(dims, false);
   if (s != GDN_OK) return s;
-  if (!inter_cache || !state_indices || !accept_len || !state_pool) return GDN_ERR_NULL;
   if (cache_T < 1) return GDN_ERR_SHAPE;
+  if (dims->batch == 0) return GDN_OK;
+  if (!inter_cache || !state_indices || !accept_len || !state_pool) return GDN_ERR_NULL;
   if (!aligned(inter_cache, 16) || !aligned(state_pool, 16) || !aligned(state_indices, 4) ||
       !aligned(accept_len, 4))
     return GDN_ERR_ALIGN;
-  if (dims->batch == 0) return GDN_OK;
   gdn::CommitArgs p;
   p.cache = inter_cache; p.pool = state_pool; p.idx = state_indices; p.accept = accept_len;
   p.B = dims->batch; p.Hv = dims->num_v_heads; p.P = dims->pool_slots; p.cache_T = cache_T;

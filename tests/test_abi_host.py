@@ -74,29 +74,37 @@ def verify(L, d, i, pool=A16 * 9, idx=A16 * 10, cache=A16 * 11, cache_T=4, wf=0,
 
 
 def test_verify_validation(L):
-    assert verify(L, dims(batch=0), io()) == 0                       # empty batch: no-op
+    # sizes and dtypes first; a valid empty batch is a no-op whatever the pointers
+    assert verify(L, dims(batch=0), io()) == 0
+    assert verify(L, dims(batch=0), io(q=None), pool=None, idx=None) == 0
     assert verify(L, None, io()) == 1
-    assert verify(L, dims(batch=0), None) == 1
-    assert verify(L, dims(batch=0), io(q=None)) == 1
-    assert verify(L, dims(batch=0), io(), pool=None) == 1
-    assert verify(L, dims(batch=0), io(), idx=None) == 1
-    assert verify(L, dims(batch=0), io(), cache=None, prev=A16 * 12) == 1   # fused commit needs a cache
     assert verify(L, dims(batch=-1), io()) == 2
     assert verify(L, dims(T=0), io()) == 2
     assert verify(L, dims(num_v_heads=3), io()) == 2                 # Hv % Hk != 0
-    assert verify(L, dims(batch=0), io(), cache_T=3) == 2            # cache shallower than T
     assert verify(L, dims(state_dtype=7), io()) == 3
     assert verify(L, dims(io_dtype=-1), io()) == 3
     assert verify(L, dims(d_k=96), io()) == 5
     assert verify(L, dims(d_v=120), io()) == 5
     assert verify(L, dims(d_v=512), io()) == 5
     assert verify(L, dims(T=gdn.GDN_MAX_T + 1), io(), cache_T=64) == 5
-    assert verify(L, dims(batch=0), io(q=A16 + 8)) == 4
-    assert verify(L, dims(batch=0), io(), pool=A16 * 9 + 4) == 4
-    assert verify(L, dims(batch=0), io(), cache=A16 * 11 + 2) == 4
-    assert verify(L, dims(batch=0), io(a=A16 * 4 + 1)) == 4
-    assert verify(L, dims(batch=0, io_dtype=gdn.GDN_DTYPE_F32), io(a=A16 * 4 + 2)) == 4
-    assert verify(L, dims(batch=0), io(A_log=A16 * 6 + 2)) == 4
+    assert verify(L, dims(batch=70000), io()) == 5
+    # with rows to process (these all return before any launch)
+    assert verify(L, dims(), None) == 1
+    assert verify(L, dims(), io(q=None)) == 1
+    assert verify(L, dims(), io(dt_bias=None)) == 1
+    assert verify(L, dims(), io(), pool=None) == 1
+    assert verify(L, dims(), io(), idx=None) == 1
+    assert verify(L, dims(), io(), cache=None, prev=A16 * 12) == 1   # fused commit needs a cache
+    assert verify(L, dims(), io(), cache_T=3) == 2                   # cache shallower than T
+    assert verify(L, dims(), io(q=A16 + 8)) == 4
+    assert verify(L, dims(), io(o=A16 * 8 + 4)) == 4
+    assert verify(L, dims(), io(), pool=A16 * 9 + 4) == 4
+    assert verify(L, dims(), io(), cache=A16 * 11 + 2) == 4
+    assert verify(L, dims(), io(a=A16 * 4 + 1)) == 4
+    assert verify(L, dims(io_dtype=gdn.GDN_DTYPE_F32), io(a=A16 * 4 + 2)) == 4
+    assert verify(L, dims(), io(A_log=A16 * 6 + 2)) == 4
+    assert verify(L, dims(), io(), idx=A16 * 10 + 2) == 4
+    assert verify(L, dims(), io(), prev=A16 * 12 + 1) == 4
 
 
 def test_decode_validation(L):
@@ -104,7 +112,8 @@ def test_decode_validation(L):
         return L.gdn_decode(ctypes.byref(d), ctypes.byref(i), pool, idx, None)
     assert dec(dims(batch=0, T=1), io()) == 0
     assert dec(dims(batch=0, T=2), io()) == 2                        # decode is one token
-    assert dec(dims(batch=0, T=1), io(), idx=None) == 1
+    assert dec(dims(T=1), io(), idx=None) == 1
+    assert dec(dims(T=1), io(v=A16 * 3 + 8)) == 4
     assert dec(dims(batch=0, T=1, d_k=48), io()) == 5
 
 
@@ -112,11 +121,13 @@ def test_commit_validation(L):
     def com(d, cache=A16, cache_T=4, idx=A16 * 2, acc=A16 * 3, pool=A16 * 4):
         return L.gdn_commit(ctypes.byref(d), cache, cache_T, idx, acc, pool, None)
     assert com(dims(batch=0)) == 0
-    assert com(dims(batch=0), cache=None) == 1
-    assert com(dims(batch=0), acc=None) == 1
+    assert com(dims(batch=0), cache=None) == 0
     assert com(dims(batch=0), cache_T=0) == 2
-    assert com(dims(batch=0), pool=A16 * 4 + 8) == 4
-    assert com(dims(batch=0), acc=A16 * 3 + 2) == 4
+    assert com(dims(), cache=None) == 1
+    assert com(dims(), acc=None) == 1
+    assert com(dims(), cache_T=0) == 2
+    assert com(dims(), pool=A16 * 4 + 8) == 4
+    assert com(dims(), acc=A16 * 3 + 2) == 4
     assert com(dims(batch=0, d_v=8)) == 5
 
 
