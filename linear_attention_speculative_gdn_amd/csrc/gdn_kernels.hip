@@ -62,8 +62,6 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // ---------------------------------------------------------------- io elements
 __device__ __forceinline__ float ld_io(const float* p) { return *p; }
 __device__ __forceinline__ float ld_io(const bf16s* p) { return __uint_as_float(uint32_t(p->bits) << 16); }
-__device__ __forceinline__ void st_io(float* p, float x) { *p = x; }
-__device__ __forceinline__ void st_io(bf16s* p, float x) { p->bits = uint16_t(pack_bf16x2(x, 0.f)); }
 
 // 16 bytes of io elements -> floats
 __device__ __forceinline__ void unpack_io(const u32x4& u, float* f, const float*) {
@@ -73,6 +71,17 @@ __device__ __forceinline__ void unpack_io(const u32x4& u, float* f, const float*
 __device__ __forceinline__ void unpack_io(const u32x4& u, float* f, const bf16s*) {
   f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
   f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+}
+
+__device__ __forceinline__ void st_io(float* p, float x) { *p = x; }
+__device__ __forceinline__ void st_io(bf16s* p, float x) { p->bits = uint16_t(pack_bf16x2(x, 0.f)); }
+
+// floats -> 16 bytes of io elements (bf16: round to nearest even)
+__device__ __forceinline__ u32x4 pack_io(const float* f, const float*) {
+  return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+}
+__device__ __forceinline__ u32x4 pack_io(const float* f, const bf16s*) {
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
 // ---------------------------------------------------------------- state chunks
@@ -174,6 +183,7 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   float* s_g = s_v + T * RPW;       // [T] decay
   float* s_beta = s_g + T;          // [T] write strength
   float* s_kq = s_beta + T;         // [T] k^.q^
+  float* s_o = s_kq + T;            // [NW][R*RW] outputs of one token, per wave
 
   // grid (v-block, v-head, row): no integer division on the way to the first loads
   const int vb = blockIdx.x;
@@ -221,9 +231,9 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   asm volatile("" ::: "memory");
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0, no state traffic
-    for (int e = tid; e < T * RPW; e += NT) {
-      const int t = e / RPW, j = vb * RPW + (e - t * RPW);
-      if (j < DV) st_io(op + (size_t(row * T + t) * p.Hv + h) * DV + j, 0.f);
+    for (int e = tid; e < nv; e += NT) {
+      const int t = e / VVEC, j = vb * RPW + (e - t * VVEC) * VE;
+      if (j < DV) *reinterpret_cast<u32x4*>(op + (size_t(row * T + t) * p.Hv + h) * DV + j) = u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
@@ -379,8 +389,22 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
           for (int c = 0; c < NCH; ++c)
             st_nt(cache_t + size_t(jrow[r]) * DK + (l + c * L) * CE, packed[c]);
         }
-        if (l == 0) st_io(op + (size_t(row * T + t) * p.Hv + h) * DV + jrow[r], ov);
+        if (l == 0) s_o[wave * (R * RW) + r * RW + grp] = ov;
       }
+    }
+    // o of this wave's R*RW consecutive value rows, as whole 16-byte vectors. The
+    // strip in LDS is private to the wave, and a wave's LDS accesses complete in
+    // order, so no barrier is needed.
+    IT* const o_t = op + (size_t(row * T + t) * p.Hv + h) * DV + vb * RPW + wave * (R * RW);
+    if constexpr ((R * RW) % VE == 0) {
+      if (lane < (R * RW) / VE && vb * RPW + wave * (R * RW) + lane * VE < DV) {
+        float f[VE];
+#pragma unroll
+        for (int m = 0; m < VE; ++m) f[m] = s_o[wave * (R * RW) + lane * VE + m];
+        *reinterpret_cast<u32x4*>(o_t + lane * VE) = pack_io(f, op);
+      }
+    } else {  // fewer rows per wave than one vector holds (d_k = 256)
+      if (lane < R * RW && vb * RPW + wave * (R * RW) + lane < DV) st_io(o_t + lane, s_o[wave * (R * RW) + lane]);
     }
   }
 
@@ -426,7 +450,7 @@ hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
   constexpr int RPW = NW * R * (64 / (DK / 16));
   const int nvb = (p.DV + RPW - 1) / RPW;
   const dim3 grid(unsigned(nvb), unsigned(p.Hv), unsigned(p.B));
-  const size_t lds = sizeof(float) * (size_t(2) * p.T * DK + size_t(p.T) * RPW + 3 * size_t(p.T));
+  const size_t lds = sizeof(float) * (size_t(2) * p.T * DK + size_t(p.T) * RPW + 3 * size_t(p.T) + RPW);
   hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW>), grid, dim3(NW * 64), lds, stream, p);
   return hipGetLastError();
 }
@@ -438,11 +462,10 @@ hipError_t launch_dk(int rows_per_lane, const RecurrentArgs& p, hipStream_t stre
     case 32: return launch_rec<ST, IT, 32, 1>(p, stream);
     case 64: return launch_rec<ST, IT, 64, 1>(p, stream);
     case 128:
-      if (rows_per_lane == 1) return launch_rec<ST, IT, 128, 1>(p, stream);
-      if (rows_per_lane == 4) return launch_rec<ST, IT, 128, 4>(p, stream);
-      if (rows_per_lane == 12) return launch_rec<ST, IT, 128, 1, 8>(p, stream);
-      if (rows_per_lane == 22) return launch_rec<ST, IT, 128, 2, 8>(p, stream);
-      return launch_rec<ST, IT, 128, 2>(p, stream);
+      if (rows_per_lane == 2) return launch_rec<ST, IT, 128, 2>(p, stream);
+      if (rows_per_lane == 12) return launch_rec<ST, IT, 128, 1, 2>(p, stream);
+      if (rows_per_lane == 14) return launch_rec<ST, IT, 128, 1, 8>(p, stream);
+      return launch_rec<ST, IT, 128, 1>(p, stream);
     case 256: return launch_rec<ST, IT, 256, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
