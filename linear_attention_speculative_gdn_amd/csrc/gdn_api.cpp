@@ -29,7 +29,7 @@ gdn_status check_dims(const gdn_dims* d, bool need_tokens) {
   if (!dtype_ok(d->state_dtype) || !dtype_ok(d->io_dtype)) return GDN_ERR_DTYPE;
   if (!dk_supported(d->d_k) || d->d_v % 16 != 0 || d->d_v > 256) return GDN_ERR_UNSUPPORTED;
   if (need_tokens && d->T > GDN_MAX_T) return GDN_ERR_UNSUPPORTED;
-  // grid (v-blocks, Hv, B) limits and 32-bit row offsets inside the kernels
+  // grid limits (heads in y, rows in z) and 32-bit row offsets inside the kernels
   if (d->batch > 65535 || d->num_v_heads > 65535) return GDN_ERR_UNSUPPORTED;
   if (int64_t(d->batch) * d->num_v_heads * 16 > int64_t(INT32_MAX)) return GDN_ERR_UNSUPPORTED;
   if (need_tokens && int64_t(d->batch) * d->T * d->num_v_heads > int64_t(INT32_MAX) / 256)
@@ -37,10 +37,16 @@ gdn_status check_dims(const gdn_dims* d, bool need_tokens) {
   return GDN_OK;
 }
 
-// Value rows per lane in the recurrent kernel. One row per lane (32 value rows per
-// workgroup at d_k = 128) measured fastest on every workload: more, smaller
-// workgroups reach their state sooner and start storing earlier.
-int pick_rows_per_lane(const gdn_dims*) { return 1; }
+// Launch shape of the recurrent kernel at d_k = 128 (other d_k use one shape).
+// One value row per lane and 4 waves (32 value rows per workgroup) measured fastest
+// on the decode and bf16 workloads: more, smaller workgroups reach their state
+// sooner and start storing earlier. Large fp32-state grids (a 64 KiB tile, many
+// rounds of workgroups) measured faster with 2-wave workgroups (16 value rows).
+int pick_shape(const gdn_dims* d) {
+  const int64_t tiles = int64_t(d->batch) * d->num_v_heads;
+  if (d->state_dtype == GDN_DTYPE_F32 && tiles >= 4096) return 12;
+  return 1;
+}
 
 gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const int32_t* idx,
                          void* cache, int32_t cache_T, int32_t write_final,
@@ -68,7 +74,7 @@ gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const 
   p.write_final = write_final ? 1 : 0;
   p.scale = d->scale; p.eps = d->l2norm_eps;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(d->state_dtype), static_cast<Dt>(d->io_dtype),
-                                             pick_rows_per_lane(d), p, static_cast<hipStream_t>(stream));
+                                             pick_shape(d), p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -41,11 +41,9 @@ struct CommitArgs {
   int64_t tile_bytes;
 };
 
-// Rows of the value dimension one recurrent workgroup covers, for a key dimension,
-// a state dtype and a rows-per-lane factor (see the kernel's lane map).
-int rows_per_workgroup(int dk, int rows_per_lane);
-
-hipError_t launch_recurrent(Dt state, Dt io, int rows_per_lane, const RecurrentArgs& p,
+// shape: 1 = one value row per lane, 4 waves; 2 = two rows per lane, 4 waves;
+// 12 = one row per lane, 2 waves; 14 = one row per lane, 8 waves (d_k = 128 only).
+hipError_t launch_recurrent(Dt state, Dt io, int shape, const RecurrentArgs& p,
                             hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream);
 
