@@ -66,6 +66,12 @@ def lib():
         L.oracle_decode.restype = ctypes.c_int32
         L.oracle_commit.argtypes = [ctypes.POINTER(Dims), _D, ctypes.c_int32, _I, _I, _D, ctypes.c_int32]
         L.oracle_commit.restype = ctypes.c_int32
+        L.oracle_verify_replay.argtypes = ([ctypes.POINTER(Dims)] + [_D] * 7 + [_D, _I] + [_D] * 4 +
+                                           [ctypes.c_int32, _I, ctypes.c_int32, _D, ctypes.c_int32])
+        L.oracle_verify_replay.restype = ctypes.c_int32
+        L.oracle_commit_replay.argtypes = ([ctypes.POINTER(Dims), _D, _D, _D, _I] + [_D] * 4 +
+                                           [ctypes.c_int32, _I, ctypes.c_int32])
+        L.oracle_commit_replay.restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -162,4 +168,37 @@ def commit(dims: Dims, cache, cache_T: int, idx, accept, pool, *, nthreads: int 
                              _p(_i32(accept), _I), _p(pool), _nthreads(nthreads))
     if rc:
         raise ValueError("oracle_commit: invalid dimensions")
+    return pool
+
+
+def verify_replay(dims: Dims, q, k, v, a, b, A_log, dt_bias, pool, idx, rk, rv, ra, rb, rlen, *,
+                  commit: bool = True, nthreads: int | None = None) -> dict:
+    """Replay rlen[r] cached tokens (rk, rv, ra, rb: [B, rT, ...]) from each row's slot,
+    commit the result to the slot if asked, then run this call's T tokens.
+    Returns dict(o, pool)."""
+    B, T, Hv, dv = dims.batch, dims.T, dims.num_v_heads, dims.d_v
+    q, k, v, a, b, rk, rv, ra, rb = map(_f64, (q, k, v, a, b, rk, rv, ra, rb))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    pool = _f64(pool).copy()
+    o = np.zeros((B, T, Hv, dv), dtype=np.float64)
+    rT = rk.shape[1]
+    rc = lib().oracle_verify_replay(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log),
+                                    _p(dt_bias), _p(pool), _p(_i32(idx), _I), _p(rk), _p(rv), _p(ra), _p(rb),
+                                    int(rT), _p(_i32(rlen), _I), int(bool(commit)), _p(o), _nthreads(nthreads))
+    if rc:
+        raise ValueError("oracle_verify_replay: invalid dimensions")
+    return dict(o=o, pool=pool)
+
+
+def commit_replay(dims: Dims, A_log, dt_bias, pool, idx, rk, rv, ra, rb, rlen, *,
+                  nthreads: int | None = None) -> np.ndarray:
+    """Separate replay commit. Returns the new pool."""
+    rk, rv, ra, rb = map(_f64, (rk, rv, ra, rb))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    pool = _f64(pool).copy()
+    rc = lib().oracle_commit_replay(ctypes.byref(dims), _p(A_log), _p(dt_bias), _p(pool), _p(_i32(idx), _I),
+                                    _p(rk), _p(rv), _p(ra), _p(rb), int(rk.shape[1]), _p(_i32(rlen), _I),
+                                    _nthreads(nthreads))
+    if rc:
+        raise ValueError("oracle_commit_replay: invalid dimensions")
     return pool

@@ -29,6 +29,12 @@
  *     bf16 state: S <- RNE_bf16(S) elementwise, carried forward rounded.
  * Readings where the pages are silent are listed beside each function.
  *
+ * Cached replay (TensorRT-LLM PR 20937, What changes: a copy-free cached replay of the
+ * GDN verify; Moved out of this PR: replay commits in-kernel or by a separate all-layer
+ * commit; the cache manager tracks the previous step's accept count and which token
+ * buffer holds it): instead of one state per token, the per-token inputs of a verify are
+ * kept, and the accepted prefix is replayed from the slot's checkpoint state later.
+ *
  * Pins (tests, CPU): closed forms of the gates; one step from a zero state; decay
  * only; the delta property S'^T k^ = v at beta = 1; associative recall with
  * orthonormal keys; the scalar case worked by hand; brute force against the
@@ -266,6 +272,103 @@ int32_t oracle_decode(const oracle_dims* d,
                 d->scale, d->eps, d->state_bf16, orow, qh, kh, u);
     }
     free(qh); free(kh); free(u);
+  }
+  return 0;
+}
+
+/* Replay rlen[r] cached tokens of row r from its slot's state; optionally commit the
+ * result to the slot; then run this call's T tokens (outputs only, no state stored).
+ * Reading: the replayed tokens produce no output; a replay length outside [0, rT]
+ * replays nothing; the commit writes only when at least one token was replayed. */
+int32_t oracle_verify_replay(const oracle_dims* d,
+                             const double* q, const double* k, const double* v,
+                             const double* a, const double* b,
+                             const double* A_log, const double* dt_bias,
+                             double* pool, const int32_t* idx,
+                             const double* rk, const double* rv, const double* ra, const double* rb,
+                             int32_t rT, const int32_t* rlen, int32_t commit, double* o,
+                             int32_t nthreads) {
+  if (!dims_ok(d) || rT < 0) return -1;
+  const int B = d->batch, T = d->T, Hk = d->num_k_heads, Hv = d->num_v_heads;
+  const int dk = d->d_k, dv = d->d_v, G = Hv / Hk;
+  const size_t tile = (size_t)dk * dv;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double* S = (double*)malloc(tile * sizeof(double));
+    double* qh = (double*)malloc((size_t)dk * sizeof(double));
+    double* kh = (double*)malloc((size_t)dk * sizeof(double));
+    double* u = (double*)malloc((size_t)dv * sizeof(double));
+    double* qz = (double*)calloc((size_t)dk, sizeof(double));
+    double* oz = (double*)malloc((size_t)dv * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic)
+#endif
+    for (int64_t th = 0; th < (int64_t)B * Hv; ++th) {
+      const int r = (int)(th / Hv), h = (int)(th % Hv), kh_i = h / G;
+      const int32_t s = idx[r];
+      if (!slot_valid(s, d->pool_slots)) {
+        for (int t = 0; t < T; ++t)
+          memset(o + (((size_t)r * T + t) * Hv + h) * dv, 0, (size_t)dv * sizeof(double));
+        continue;
+      }
+      memcpy(S, pool + ((size_t)s * Hv + h) * tile, tile * sizeof(double));
+      const int32_t n = (rlen && rlen[r] >= 0 && rlen[r] <= rT) ? rlen[r] : 0;
+      for (int t = 0; t < n; ++t) {
+        const size_t rt = (size_t)r * rT + t;
+        gdn_token(dk, dv, S, qz, rk + (rt * Hk + kh_i) * dk, rv + (rt * Hv + h) * dv, ra[rt * Hv + h],
+                  rb[rt * Hv + h], A_log[h], dt_bias[h], d->scale, d->eps, d->state_bf16, oz, qh, kh, u);
+      }
+      if (commit && n > 0) memcpy(pool + ((size_t)s * Hv + h) * tile, S, tile * sizeof(double));
+      for (int t = 0; t < T; ++t) {
+        const size_t rt = (size_t)r * T + t;
+        gdn_token(dk, dv, S, q + (rt * Hk + kh_i) * dk, k + (rt * Hk + kh_i) * dk, v + (rt * Hv + h) * dv,
+                  a[rt * Hv + h], b[rt * Hv + h], A_log[h], dt_bias[h], d->scale, d->eps, d->state_bf16,
+                  o + (rt * Hv + h) * dv, qh, kh, u);
+      }
+    }
+    free(S); free(qh); free(kh); free(u); free(qz); free(oz);
+  }
+  return 0;
+}
+
+/* Separate replay commit: every row with a valid slot and 1 <= rlen[r] <= rT gets the
+ * state after replaying its rlen[r] cached tokens from the slot written back to it. */
+int32_t oracle_commit_replay(const oracle_dims* d, const double* A_log, const double* dt_bias,
+                             double* pool, const int32_t* idx,
+                             const double* rk, const double* rv, const double* ra, const double* rb,
+                             int32_t rT, const int32_t* rlen, int32_t nthreads) {
+  if (!dims_ok(d) || rT < 0) return -1;
+  const int B = d->batch, Hk = d->num_k_heads, Hv = d->num_v_heads;
+  const int dk = d->d_k, dv = d->d_v, G = Hv / Hk;
+  const size_t tile = (size_t)dk * dv;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double* qh = (double*)malloc((size_t)dk * sizeof(double));
+    double* kh = (double*)malloc((size_t)dk * sizeof(double));
+    double* u = (double*)malloc((size_t)dv * sizeof(double));
+    double* qz = (double*)calloc((size_t)dk, sizeof(double));
+    double* oz = (double*)malloc((size_t)dv * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic)
+#endif
+    for (int64_t th = 0; th < (int64_t)B * Hv; ++th) {
+      const int r = (int)(th / Hv), h = (int)(th % Hv), kh_i = h / G;
+      const int32_t s = idx[r], n = rlen[r];
+      if (!slot_valid(s, d->pool_slots) || n < 1 || n > rT) continue;
+      double* S = pool + ((size_t)s * Hv + h) * tile;
+      for (int t = 0; t < n; ++t) {
+        const size_t rt = (size_t)r * rT + t;
+        gdn_token(dk, dv, S, qz, rk + (rt * Hk + kh_i) * dk, rv + (rt * Hv + h) * dv, ra[rt * Hv + h],
+                  rb[rt * Hv + h], A_log[h], dt_bias[h], d->scale, d->eps, d->state_bf16, oz, qh, kh, u);
+      }
+    }
+    free(qh); free(kh); free(u); free(qz); free(oz);
   }
   return 0;
 }

@@ -53,6 +53,23 @@ int32_t oracle_commit(const oracle_dims* d, const double* cache, int32_t cache_T
                       const int32_t* idx, const int32_t* accept, double* pool,
                       int32_t nthreads);
 
+/* Cached replay. rk, rv, ra, rb hold the per-token inputs of an earlier verify
+ * ([B][rT][Hk][dk], [B][rT][Hv][dv], [B][rT][Hv], [B][rT][Hv]); rlen[r] tokens of row r
+ * are replayed from its pool slot (rlen outside [0, rT] replays nothing). */
+int32_t oracle_verify_replay(const oracle_dims* d,
+                             const double* q, const double* k, const double* v,
+                             const double* a, const double* b,
+                             const double* A_log, const double* dt_bias,
+                             double* pool, const int32_t* idx,
+                             const double* rk, const double* rv, const double* ra, const double* rb,
+                             int32_t rT, const int32_t* rlen, int32_t commit, double* o,
+                             int32_t nthreads);
+
+int32_t oracle_commit_replay(const oracle_dims* d, const double* A_log, const double* dt_bias,
+                             double* pool, const int32_t* idx,
+                             const double* rk, const double* rv, const double* ra, const double* rb,
+                             int32_t rT, const int32_t* rlen, int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif
