@@ -136,6 +136,41 @@ GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int
                       const int32_t* state_indices, const int32_t* accept_len,
                       void* state_pool, void* stream);
 
+/* Per-token inputs of an earlier verify, kept by the caller for cached replay: the k,
+ * v, a, b arrays that verify consumed (typically the previous step's io buffers, used
+ * alternately with the current ones). io dtype, 16-byte aligned k and v. */
+typedef struct {
+  const void* k;    /* [B][T_src][Hk][d_k] */
+  const void* v;    /* [B][T_src][Hv][d_v] */
+  const void* a;    /* [B][T_src][Hv] */
+  const void* b;    /* [B][T_src][Hv] */
+  int32_t T_src;    /* tokens per row in these arrays, >= 1 */
+} gdn_tokens;
+
+/* Cached-replay verify [P3, What changes: a copy-free cached replay of the GDN verify;
+ * Moved out of this PR: commit in-kernel or by the separate all-layer commit; the cache
+ * manager tracks the previous step's accept count and which token buffer holds it].
+ * Instead of one stored state per token, the accepted prefix of the previous verify is
+ * replayed: for each valid row, with n = replay_len[r] (n outside [0, T_src] replays
+ * nothing), the state of the slot advances through tokens 0..n-1 of `replay`; with
+ * commit = 1 and n >= 1 that state is written back to the slot; then this call's T
+ * tokens run from it and write o. No per-token state is stored. Replayed and new tokens
+ * use the same arithmetic as gdn_verify, so the replayed state equals, bit for bit, the
+ * intermediate state gdn_verify would have cached after n tokens. Needs
+ * T + T_src <= GDN_MAX_T. `replay` must not alias io's k, v, a, b. */
+GDN_API gdn_status gdn_verify_replay(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                                     const int32_t* state_indices, const gdn_tokens* replay,
+                                     const int32_t* replay_len, int32_t commit, void* stream);
+
+/* Replay commit (the separate all-layer commit of the same contract): for each valid row
+ * with 1 <= n = replay_len[r] <= T_src, the slot's state advanced through tokens 0..n-1
+ * of `replay` is written back to the slot; other rows are untouched. Reads dims->batch,
+ * num_k_heads, num_v_heads, d_k, d_v, pool_slots, state_dtype, io_dtype, l2norm_eps;
+ * needs T_src <= GDN_MAX_T. */
+GDN_API gdn_status gdn_commit_replay(const gdn_dims* dims, const float* A_log, const float* dt_bias,
+                                     void* state_pool, const int32_t* state_indices,
+                                     const gdn_tokens* replay, const int32_t* replay_len, void* stream);
+
 /* Static text for a status code (never NULL). */
 GDN_API const char* gdn_status_string(gdn_status status);
 

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
-EXPORTED = ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_status_string", "gdn_abi_version")
+EXPORTED = ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+            "gdn_status_string", "gdn_abi_version")
 GDN_MAX_T = 16
 
 
@@ -46,6 +47,11 @@ class GdnIo(ctypes.Structure):
                 ("dt_bias", ctypes.c_void_p), ("o", ctypes.c_void_p)]
 
 
+class GdnTokens(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("T_src", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -62,7 +68,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode.argtypes = [D, I, vp, vp, vp]
         L.gdn_verify.argtypes = [D, I, vp, vp, vp, i32, i32, vp, vp]
         L.gdn_commit.argtypes = [D, vp, i32, vp, vp, vp, vp]
-        for f in ("gdn_decode", "gdn_verify", "gdn_commit"):
+        TK = ctypes.POINTER(GdnTokens)
+        L.gdn_verify_replay.argtypes = [D, I, vp, vp, TK, vp, i32, vp]
+        L.gdn_commit_replay.argtypes = [D, vp, vp, vp, vp, TK, vp, vp]
+        for f in ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
@@ -189,3 +198,58 @@ def gdn_commit(inter_cache, state_indices, accept_len, state_pool, *, stream=Non
     st = lib().gdn_commit(ctypes.byref(dims), _ptr(inter_cache), cache_T, _ptr(state_indices), _ptr(accept_len),
                           _ptr(state_pool), _stream(dev, stream))
     _raise(st, "gdn_commit")
+
+
+def _tokens(rk, rv, ra, rb, B, Hk, Hv, dk, dv, io_dtype, device) -> GdnTokens:
+    _need(rk, "replay_k", 4, device); _need(rv, "replay_v", 4, device)
+    _need(ra, "replay_a", 3, device); _need(rb, "replay_b", 3, device)
+    Ts = rk.shape[1]
+    if rk.shape != (B, Ts, Hk, dk) or rv.shape != (B, Ts, Hv, dv) or ra.shape != (B, Ts, Hv) or rb.shape != (B, Ts, Hv):
+        raise ValueError("replay arrays must be k [B,T_src,Hk,dk], v [B,T_src,Hv,dv], a and b [B,T_src,Hv]")
+    for name, t in (("replay_k", rk), ("replay_v", rv), ("replay_a", ra), ("replay_b", rb)):
+        if t.dtype != io_dtype:
+            raise TypeError(f"{name} must have the io dtype {io_dtype}")
+    return GdnTokens(rk.data_ptr(), rv.data_ptr(), ra.data_ptr(), rb.data_ptr(), Ts)
+
+
+def _need_len(t, B, device, name="replay_len"):
+    _need(t, name, 1, device)
+    if t.shape != (B,) or t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32 [B]")
+
+
+def gdn_verify_replay(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, replay_k, replay_v,
+                      replay_a, replay_b, replay_len, commit=True, *, scale=None, l2norm_eps=1e-6,
+                      stream=None) -> None:
+    """Replay replay_len[r] tokens of an earlier verify (replay_* arrays) from each row's
+    slot, commit the result to the slot if asked, then run this call's T tokens."""
+    dims, io = _dims_io(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, scale, l2norm_eps)
+    rep = _tokens(replay_k, replay_v, replay_a, replay_b, dims.batch, dims.num_k_heads, dims.num_v_heads,
+                  dims.d_k, dims.d_v, q.dtype, q.device)
+    _need_len(replay_len, dims.batch, q.device)
+    st = lib().gdn_verify_replay(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
+                                 ctypes.byref(rep), _ptr(replay_len), int(bool(commit)), _stream(q.device, stream))
+    _raise(st, "gdn_verify_replay")
+
+
+def gdn_commit_replay(A_log, dt_bias, state_pool, state_indices, replay_k, replay_v, replay_a, replay_b,
+                      replay_len, *, l2norm_eps=1e-6, stream=None) -> None:
+    """Separate replay commit: each valid row's slot advances through its replay_len[r]
+    replayed tokens and is written back."""
+    dev = state_pool.device
+    _need(state_pool, "state_pool", 4, dev); _need(state_indices, "state_indices", 1, dev)
+    _need(A_log, "A_log", 1, dev); _need(dt_bias, "dt_bias", 1, dev)
+    B, Ts, Hk, dk = replay_k.shape
+    P, Hv, dv, dk2 = state_pool.shape
+    if dk2 != dk:
+        raise ValueError("state_pool must be [P, Hv, dv, dk] with the replay arrays' dk")
+    if A_log.shape != (Hv,) or dt_bias.shape != (Hv,) or A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise ValueError("A_log and dt_bias must be float32 [Hv]")
+    if state_indices.shape != (B,) or state_indices.dtype != torch.int32:
+        raise ValueError("state_indices must be int32 [B]")
+    rep = _tokens(replay_k, replay_v, replay_a, replay_b, B, Hk, Hv, dk, dv, replay_k.dtype, dev)
+    _need_len(replay_len, B, dev)
+    dims = GdnDims(B, 1, Hk, Hv, dk, dv, P, _dt(state_pool), _dt(replay_k), 1.0, float(l2norm_eps))
+    st = lib().gdn_commit_replay(ctypes.byref(dims), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool),
+                                 _ptr(state_indices), ctypes.byref(rep), _ptr(replay_len), _stream(dev, stream))
+    _raise(st, "gdn_commit_replay")

@@ -73,9 +73,30 @@ gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const 
   p.G = d->num_v_heads / d->num_k_heads;
   p.write_final = write_final ? 1 : 0;
   p.scale = d->scale; p.eps = d->l2norm_eps;
+  p.rk = p.rv = p.ra = p.rb = nullptr;
+  p.rlen = nullptr;
+  p.rT = 0;
+  p.rcommit = 0;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(d->state_dtype), static_cast<Dt>(d->io_dtype),
-                                             pick_shape(d), p, static_cast<hipStream_t>(stream));
+                                             pick_shape(d), 0, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+// Checks of the replay token arrays (pointers, alignment, depth).
+gdn_status check_replay(const gdn_dims* d, const gdn_tokens* rep, const int32_t* rlen) {
+  if (!rep || !rep->k || !rep->v || !rep->a || !rep->b || !rlen) return GDN_ERR_NULL;
+  const uintptr_t isz = dsize(d->io_dtype);
+  if (!aligned(rep->k, 16) || !aligned(rep->v, 16) || !aligned(rep->a, isz) || !aligned(rep->b, isz) ||
+      !aligned(rlen, 4))
+    return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+void set_replay(gdn::RecurrentArgs& p, const gdn_tokens* rep, const int32_t* rlen, int32_t commit) {
+  p.rk = rep->k; p.rv = rep->v; p.ra = rep->a; p.rb = rep->b;
+  p.rlen = rlen;
+  p.rT = rep->T_src;
+  p.rcommit = commit ? 1 : 0;
 }
 
 }  // namespace
@@ -117,6 +138,65 @@ gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cac
   const int64_t per_block = int64_t(gdn::kThreads) * gdn::kCommitChunksPerThread * 16;
   p.blocks_per_tile = int32_t((p.tile_bytes + per_block - 1) / per_block);
   const hipError_t e = gdn::launch_commit(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status gdn_verify_replay(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                             const int32_t* state_indices, const gdn_tokens* replay,
+                             const int32_t* replay_len, int32_t commit, void* stream) {
+  gdn_status s = check_dims(dims, true);
+  if (s != GDN_OK) return s;
+  if (replay && replay->T_src < 1) return GDN_ERR_SHAPE;
+  if (replay && dims->T + replay->T_src > GDN_MAX_T) return GDN_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return GDN_OK;
+  if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
+      !state_pool || !state_indices)
+    return GDN_ERR_NULL;
+  if ((s = check_replay(dims, replay, replay_len)) != GDN_OK) return s;
+  const uintptr_t isz = dsize(dims->io_dtype);
+  if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->o, 16) ||
+      !aligned(state_pool, 16) || !aligned(io->a, isz) || !aligned(io->b, isz) || !aligned(io->A_log, 4) ||
+      !aligned(io->dt_bias, 4) || !aligned(state_indices, 4))
+    return GDN_ERR_ALIGN;
+  gdn::RecurrentArgs p;
+  p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
+  p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
+  p.pool = state_pool; p.idx = state_indices; p.cache = nullptr; p.prev_accept = nullptr;
+  p.B = dims->batch; p.T = dims->T; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads;
+  p.DK = dims->d_k; p.DV = dims->d_v; p.P = dims->pool_slots; p.cache_T = 0;
+  p.G = dims->num_v_heads / dims->num_k_heads;
+  p.write_final = 0;
+  p.scale = dims->scale; p.eps = dims->l2norm_eps;
+  set_replay(p, replay, replay_len, commit);
+  const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
+                                             1, 1, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status gdn_commit_replay(const gdn_dims* dims, const float* A_log, const float* dt_bias,
+                             void* state_pool, const int32_t* state_indices,
+                             const gdn_tokens* replay, const int32_t* replay_len, void* stream) {
+  gdn_status s = check_dims(dims, false);
+  if (s != GDN_OK) return s;
+  if (replay && replay->T_src < 1) return GDN_ERR_SHAPE;
+  if (replay && replay->T_src > GDN_MAX_T) return GDN_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return GDN_OK;
+  if (!A_log || !dt_bias || !state_pool || !state_indices) return GDN_ERR_NULL;
+  if ((s = check_replay(dims, replay, replay_len)) != GDN_OK) return s;
+  if (!aligned(state_pool, 16) || !aligned(A_log, 4) || !aligned(dt_bias, 4) || !aligned(state_indices, 4))
+    return GDN_ERR_ALIGN;
+  gdn::RecurrentArgs p;
+  p.q = p.k = p.v = p.a = p.b = nullptr;
+  p.A_log = A_log; p.dt_bias = dt_bias; p.o = nullptr;
+  p.pool = state_pool; p.idx = state_indices; p.cache = nullptr; p.prev_accept = nullptr;
+  p.B = dims->batch; p.T = 0; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads;
+  p.DK = dims->d_k; p.DV = dims->d_v; p.P = dims->pool_slots; p.cache_T = 0;
+  p.G = dims->num_v_heads / dims->num_k_heads;
+  p.write_final = 0;
+  p.scale = dims->scale; p.eps = dims->l2norm_eps;
+  set_replay(p, replay, replay_len, 1);
+  const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
+                                             1, 2, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -28,6 +28,14 @@ struct RecurrentArgs {
   int32_t G;                   // v-heads per k-head (Hv / Hk)
   int32_t write_final;
   float scale, eps;
+  // cached replay (modes 1 and 2)
+  const void* rk;              // [B][rT][Hk][DK] io dtype
+  const void* rv;              // [B][rT][Hv][DV]
+  const void* ra;              // [B][rT][Hv]
+  const void* rb;              // [B][rT][Hv]
+  const int32_t* rlen;         // [B] tokens to replay per row
+  int32_t rT;                  // tokens per row in the replay arrays (>= 1)
+  int32_t rcommit;             // 1: write the replayed state to the slot
 };
 
 // One launch of the accepted-prefix commit copy.
@@ -43,7 +51,8 @@ struct CommitArgs {
 
 // shape: 1 = one value row per lane, 4 waves; 2 = two rows per lane, 4 waves;
 // 12 = one row per lane, 2 waves; 14 = one row per lane, 8 waves (d_k = 128 only).
-hipError_t launch_recurrent(Dt state, Dt io, int shape, const RecurrentArgs& p,
+// mode: 0 decode / verify, 1 cached-replay verify, 2 replay commit (shape 1 only).
+hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, const RecurrentArgs& p,
                             hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream);
 

@@ -160,11 +160,25 @@ __device__ __forceinline__ void st_nt(void* p, const u32x4& u) {
 // (request row, v-head). Lane (grp = lane/L, l = lane%L) of wave w holds, for slot r,
 // value row jl = (w*R + r)*RW + grp and the chunks l + c*L (c < 16/CE) of that row.
 //
+// MODE 0: decode / verify. T tokens from the slot's state (or, with a fused commit,
+//         from the previous step's accepted intermediate), optional intermediate
+//         cache and write-back.
+// MODE 1: cached-replay verify. n = rlen[row] tokens of an earlier verify (their k, v,
+//         a, b kept by the caller) are replayed from the slot's state, the result is
+//         optionally committed to the slot, then the T new tokens run; no state is
+//         stored per token.
+// MODE 2: replay commit. The n replayed tokens' state is written back to the slot; no
+//         new tokens, no outputs.
+// Replayed and new tokens go through the same per-token code, in one sequence (the
+// replayed ones first), so a replay reproduces the states a verify computed bit for bit.
+//
 // Every global load is unconditional, from an address clamped into its buffer, and
 // out-of-range lanes discard the value afterwards: a load inside a branch would be
 // waited on at the end of the branch, which serialises the memory round trips.
-template <typename ST, typename IT, int DK, int R, int NW>
+template <typename ST, typename IT, int DK, int R, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs p) {
+  constexpr bool NEW = MODE != 2;        // this call has its own tokens (and outputs)
+  constexpr bool REPLAY = MODE != 0;
   constexpr int NT = NW * 64;
   constexpr int L = DK / 16;
   constexpr int RW = 64 / L;
@@ -178,14 +192,15 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   constexpr int NV = (GDN_MAX_T * VVEC + NT - 1) / NT;
 
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int T = p.T;
-  float* s_q = smem;                // [T][DK]  q, then q^
-  float* s_k = s_q + T * DK;        // [T][DK]  k, then k^
-  float* s_v = s_k + T * DK;        // [T][RPW] v of this block's rows
-  float* s_g = s_v + T * RPW;       // [T] decay
-  float* s_beta = s_g + T;          // [T] write strength
-  float* s_kq = s_beta + T;         // [T] k^.q^
-  float* s_o = s_kq + T;            // [NW][R*RW] outputs of one token, per wave
+  const int T = NEW ? p.T : 0;
+  const int TMAX = T + (REPLAY ? p.rT : 0);  // token capacity of the LDS buffers
+  float* s_q = smem;                // [TMAX][DK]  q, then q^ (zero for replayed tokens)
+  float* s_k = s_q + TMAX * DK;     // [TMAX][DK]  k, then k^
+  float* s_v = s_k + TMAX * DK;     // [TMAX][RPW] v of this block's rows
+  float* s_g = s_v + TMAX * RPW;    // [TMAX] decay
+  float* s_beta = s_g + TMAX;       // [TMAX] write strength
+  float* s_kq = s_beta + TMAX;      // [TMAX] k^.q^
+  float* s_o = s_kq + TMAX;         // [NW][R*RW] outputs of one token, per wave
 
   // grid (v-block, v-head, row): no integer division on the way to the first loads.
   // Workgroups are dealt to the 8 XCDs round-robin by linear id, so the v-blocks of
@@ -209,43 +224,80 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   IT* op = static_cast<IT*>(p.o);
 
   const int32_t slot = p.idx[row];
-  const int32_t n_prev = p.prev_accept ? p.prev_accept[row] : 0;
+  const int32_t n_prev = (MODE == 0 && p.prev_accept) ? p.prev_accept[row] : 0;
+  int32_t n_rep = 0;
+  if constexpr (REPLAY) {
+    const int32_t x = p.rlen[row];
+    n_rep = (x >= 0 && x <= p.rT) ? x : 0;
+  }
   const int kh = h / p.G;
 
-  // ---- 1. per-token inputs (do not depend on the slot): q, k, v as 16-byte vectors
+  // ---- 1. this call's per-token inputs (do not depend on the slot): q, k, v as
+  //         16-byte vectors, a and b of token tid
   const int nq = T * QVEC, nv = T * VVEC;
   u32x4 qraw[NQ], kraw[NQ], vraw[NV];
+  float a_in = 0.f, b_in = 0.f;
+  if constexpr (NEW) {
 #pragma unroll
-  for (int it = 0; it < NQ; ++it) {
-    const int e = min(tid + it * NT, nq - 1);
-    const int t = e / QVEC, c = e - t * QVEC;
-    const size_t off = (size_t(row * T + t) * p.Hk + kh) * DK + c * VE;
-    qraw[it] = *reinterpret_cast<const u32x4*>(qp + off);
-    kraw[it] = *reinterpret_cast<const u32x4*>(kp + off);
-  }
+    for (int it = 0; it < NQ; ++it) {
+      const int e = min(tid + it * NT, nq - 1);
+      const int t = e / QVEC, c = e - t * QVEC;
+      const size_t off = (size_t(row * T + t) * p.Hk + kh) * DK + c * VE;
+      qraw[it] = *reinterpret_cast<const u32x4*>(qp + off);
+      kraw[it] = *reinterpret_cast<const u32x4*>(kp + off);
+    }
 #pragma unroll
-  for (int it = 0; it < NV; ++it) {
-    const int e = min(tid + it * NT, nv - 1);
-    const int t = e / VVEC, c = e - t * VVEC;
-    const int j = min(vb * RPW + c * VE, DV - VE);
-    vraw[it] = *reinterpret_cast<const u32x4*>(vp + (size_t(row * T + t) * p.Hv + h) * DV + j);
+    for (int it = 0; it < NV; ++it) {
+      const int e = min(tid + it * NT, nv - 1);
+      const int t = e / VVEC, c = e - t * VVEC;
+      const int j = min(vb * RPW + c * VE, DV - VE);
+      vraw[it] = *reinterpret_cast<const u32x4*>(vp + (size_t(row * T + t) * p.Hv + h) * DV + j);
+    }
+    const int tg = min(tid, T - 1);
+    a_in = ld_io(ap + size_t(row * T + tg) * p.Hv + h);
+    b_in = ld_io(bp + size_t(row * T + tg) * p.Hv + h);
   }
-  const int tg = min(tid, T - 1);
-  const float a_in = ld_io(ap + size_t(row * T + tg) * p.Hv + h);
-  const float b_in = ld_io(bp + size_t(row * T + tg) * p.Hv + h);
   // keep the loads above issued before the wait on the slot index (they must not
   // be sunk into the non-padding branch)
   asm volatile("" ::: "memory");
 
-  if (slot < 0 || slot >= p.P) {  // padding row: o = 0, no state traffic
-    for (int e = tid; e < nv; e += NT) {
-      const int t = e / VVEC, j = vb * RPW + (e - t * VVEC) * VE;
-      if (j < DV) *reinterpret_cast<u32x4*>(op + (size_t(row * T + t) * p.Hv + h) * DV + j) = u32x4{0u, 0u, 0u, 0u};
+  if (slot < 0 || slot >= p.P || (MODE == 2 && n_rep == 0)) {  // nothing to do but o = 0
+    if constexpr (NEW) {
+      for (int e = tid; e < nv; e += NT) {
+        const int t = e / VVEC, j = vb * RPW + (e - t * VVEC) * VE;
+        if (j < DV) *reinterpret_cast<u32x4*>(op + (size_t(row * T + t) * p.Hv + h) * DV + j) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     return;
   }
 
-  // ---- 2. the initial state: the pool slot, or the previous step's accepted
+  // ---- 2. the replayed tokens' k, v, a, b (the caller guarantees at least one token
+  //         per row in the replay arrays, so the clamped addresses stay inside them)
+  const int nrq = n_rep * QVEC, nrv = n_rep * VVEC;
+  u32x4 rkraw[NQ], rvraw[NV];
+  float ra_in = 0.f, rb_in = 0.f;
+  if constexpr (REPLAY) {
+    const IT* rkp = static_cast<const IT*>(p.rk);
+    const IT* rvp = static_cast<const IT*>(p.rv);
+#pragma unroll
+    for (int it = 0; it < NQ; ++it) {
+      const int e = min(tid + it * NT, max(nrq, 1) - 1);
+      const int t = e / QVEC, c = e - t * QVEC;
+      rkraw[it] = *reinterpret_cast<const u32x4*>(rkp + (size_t(row * p.rT + t) * p.Hk + kh) * DK + c * VE);
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = min(tid + it * NT, max(nrv, 1) - 1);
+      const int t = e / VVEC, c = e - t * VVEC;
+      const int j = min(vb * RPW + c * VE, DV - VE);
+      rvraw[it] = *reinterpret_cast<const u32x4*>(rvp + (size_t(row * p.rT + t) * p.Hv + h) * DV + j);
+    }
+    const int tg = min(tid, max(n_rep, 1) - 1);
+    ra_in = ld_io(static_cast<const IT*>(p.ra) + size_t(row * p.rT + tg) * p.Hv + h);
+    rb_in = ld_io(static_cast<const IT*>(p.rb) + size_t(row * p.rT + tg) * p.Hv + h);
+  }
+
+  // ---- 3. the initial state: the pool slot, or the previous step's accepted
   //         intermediate for a fused commit
   const bool commit_prev = n_prev >= 1 && n_prev <= p.cache_T;
   const ST* src = commit_prev
@@ -264,43 +316,81 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
       raw[r][c] = *reinterpret_cast<const u32x4*>(src + size_t(jr) * DK + (l + c * L) * CE);
   }
 
-  // ---- 3. per-token inputs -> LDS; gates
+  // ---- 4. token inputs -> LDS (replayed tokens first, then this call's); gates
+  const float A = expf(p.A_log[h]), dtb = p.dt_bias[h];
+  if constexpr (REPLAY) {
 #pragma unroll
-  for (int it = 0; it < NQ; ++it) {
-    const int e = tid + it * NT;
-    if (e < nq) {
-      float f[VE];
-      unpack_io(qraw[it], f, qp);
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + it * NT;
+      if (e < nrq) {
+        float f[VE];
+        unpack_io(rkraw[it], f, kp);
 #pragma unroll
-      for (int m = 0; m < VE; ++m) s_q[e * VE + m] = f[m];
-      unpack_io(kraw[it], f, kp);
+        for (int m = 0; m < VE; ++m) {
+          s_k[e * VE + m] = f[m];
+          s_q[e * VE + m] = 0.f;
+        }
+      }
+    }
 #pragma unroll
-      for (int m = 0; m < VE; ++m) s_k[e * VE + m] = f[m];
+    for (int it = 0; it < NV; ++it) {
+      const int e = tid + it * NT;
+      if (e < nrv) {
+        float f[VE];
+        unpack_io(rvraw[it], f, vp);
+        const int t = e / VVEC, c = e - t * VVEC;
+        const bool ok = vb * RPW + c * VE < DV;
+#pragma unroll
+        for (int m = 0; m < VE; ++m) s_v[t * RPW + c * VE + m] = ok ? f[m] : 0.f;
+      }
+    }
+    if (tid < n_rep) {
+      const float x = ra_in + dtb;
+      s_g[tid] = expf(-A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))));
+      s_beta[tid] = 1.f / (1.f + expf(-rb_in));
     }
   }
+  if constexpr (NEW) {
+    float* const sq_new = s_q + n_rep * DK;
+    float* const sk_new = s_k + n_rep * DK;
+    float* const sv_new = s_v + n_rep * RPW;
 #pragma unroll
-  for (int it = 0; it < NV; ++it) {
-    const int e = tid + it * NT;
-    if (e < nv) {
-      float f[VE];
-      unpack_io(vraw[it], f, vp);
-      const int t = e / VVEC, c = e - t * VVEC;
-      const bool ok = vb * RPW + c * VE < DV;
+    for (int it = 0; it < NQ; ++it) {
+      const int e = tid + it * NT;
+      if (e < nq) {
+        float f[VE];
+        unpack_io(qraw[it], f, qp);
 #pragma unroll
-      for (int m = 0; m < VE; ++m) s_v[t * RPW + c * VE + m] = ok ? f[m] : 0.f;
+        for (int m = 0; m < VE; ++m) sq_new[e * VE + m] = f[m];
+        unpack_io(kraw[it], f, kp);
+#pragma unroll
+        for (int m = 0; m < VE; ++m) sk_new[e * VE + m] = f[m];
+      }
     }
-  }
-  if (tid < T) {
-    const float x = a_in + p.dt_bias[h];
-    const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-    s_g[tid] = expf(-expf(p.A_log[h]) * sp);
-    s_beta[tid] = 1.f / (1.f + expf(-b_in));
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = tid + it * NT;
+      if (e < nv) {
+        float f[VE];
+        unpack_io(vraw[it], f, vp);
+        const int t = e / VVEC, c = e - t * VVEC;
+        const bool ok = vb * RPW + c * VE < DV;
+#pragma unroll
+        for (int m = 0; m < VE; ++m) sv_new[t * RPW + c * VE + m] = ok ? f[m] : 0.f;
+      }
+    }
+    if (tid < T) {
+      const float x = a_in + dtb;
+      s_g[n_rep + tid] = expf(-A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))));
+      s_beta[n_rep + tid] = 1.f / (1.f + expf(-b_in));
+    }
   }
   __syncthreads();
 
-  // ---- 4. L2 normalisation of q and k, and k^.q^, one wave per token
+  // ---- 5. L2 normalisation of q and k, and k^.q^, one wave per token
+  const int NTOK = n_rep + T;
   constexpr int PL = (DK + 63) / 64;  // elements per lane
-  for (int t = wave; t < T; t += NW) {
+  for (int t = wave; t < NTOK; t += NW) {
     float qv[PL], kv[PL];
     float sq = 0.f, sk = 0.f, skq = 0.f;
 #pragma unroll
@@ -328,7 +418,7 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   }
   __syncthreads();
 
-  // ---- 5. state to registers; fused commit of the gathered state
+  // ---- 6. state to registers; fused commit of the gathered state
   float S[R][16];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -345,26 +435,26 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
           st_nt(pool_tile + size_t(jrow[r]) * DK + (l + c * L) * CE, raw[r][c]);
   }
 
-  // ---- 6. the T tokens
+  // ---- 7. the tokens: n_rep replayed ones, then this call's T
   ST* const cache_row = p.cache ? static_cast<ST*>(p.cache) + size_t(row) * p.cache_T * p.Hv * tile : nullptr;
   const size_t cache_t_stride = size_t(p.Hv) * tile;
   const float scale = p.scale;
   const f32x4* s_k4 = reinterpret_cast<const f32x4*>(s_k);
   const f32x4* s_q4 = reinterpret_cast<const f32x4*>(s_q);
-  for (int t = 0; t < T; ++t) {
+  for (int tau = 0; tau < NTOK; ++tau) {
     float kh_[16], qh_[16];
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int m4 = 0; m4 < CE / 4; ++m4) {
-        const int i4 = (t * DK + (l + c * L) * CE) / 4 + m4;
+        const int i4 = (tau * DK + (l + c * L) * CE) / 4 + m4;
         const f32x4 kk = s_k4[i4], qq = s_q4[i4];
         kh_[c * CE + m4 * 4 + 0] = kk.x; kh_[c * CE + m4 * 4 + 1] = kk.y;
         kh_[c * CE + m4 * 4 + 2] = kk.z; kh_[c * CE + m4 * 4 + 3] = kk.w;
         qh_[c * CE + m4 * 4 + 0] = qq.x; qh_[c * CE + m4 * 4 + 1] = qq.y;
         qh_[c * CE + m4 * 4 + 2] = qq.z; qh_[c * CE + m4 * 4 + 3] = qq.w;
       }
-    const float gt = s_g[t], bt = s_beta[t], kqt = s_kq[t];
+    const float gt = s_g[tau], bt = s_beta[tau], kqt = s_kq[tau];
     float rk[R], rq[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -379,11 +469,13 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
       rk[r] = group_sum<L>(pk0 + pk1);
       rq[r] = group_sum<L>(pq0 + pq1);
     }
-    ST* const cache_t = cache_row ? cache_row + t * cache_t_stride + h * tile : nullptr;
+    const int t = tau - n_rep;  // index among this call's tokens (negative: replayed)
+    ST* const cache_t = (cache_row && t >= 0) ? cache_row + t * cache_t_stride + h * tile : nullptr;
+    const bool commit_now = REPLAY && p.rcommit && tau == n_rep - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int jl = (wave * R + r) * RW + grp;
-      const float w = bt * (s_v[t * RPW + jl] - gt * rk[r]);
+      const float w = bt * (s_v[tau * RPW + jl] - gt * rk[r]);
       const float ov = (gt * rq[r] + kqt * w) * scale;
 #pragma unroll
       for (int e = 0; e < 16; ++e) S[r][e] = fmaf(gt, S[r][e], kh_[e] * w);
@@ -396,27 +488,37 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
           for (int c = 0; c < NCH; ++c)
             st_nt(cache_t + size_t(jrow[r]) * DK + (l + c * L) * CE, packed[c]);
         }
-        if (l == 0) s_o[wave * (R * RW) + r * RW + grp] = ov;
+        if (commit_now) {
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+            st_nt(pool_tile + size_t(jrow[r]) * DK + (l + c * L) * CE, packed[c]);
+        }
+        if (NEW && l == 0) s_o[wave * (R * RW) + r * RW + grp] = ov;
       }
     }
-    // o of this wave's R*RW consecutive value rows, as whole 16-byte vectors. The
-    // strip in LDS is private to the wave, and a wave's LDS accesses complete in
-    // order, so no barrier is needed.
-    IT* const o_t = op + (size_t(row * T + t) * p.Hv + h) * DV + vb * RPW + wave * (R * RW);
-    if constexpr ((R * RW) % VE == 0) {
-      if (lane < (R * RW) / VE && vb * RPW + wave * (R * RW) + lane * VE < DV) {
-        float f[VE];
+    if constexpr (NEW) {
+      if (t >= 0) {
+        // o of this wave's R*RW consecutive value rows, as whole 16-byte vectors. The
+        // strip in LDS is private to the wave, and a wave's LDS accesses complete in
+        // order, so no barrier is needed.
+        IT* const o_t = op + (size_t(row * T + t) * p.Hv + h) * DV + vb * RPW + wave * (R * RW);
+        if constexpr ((R * RW) % VE == 0) {
+          if (lane < (R * RW) / VE && vb * RPW + wave * (R * RW) + lane * VE < DV) {
+            float f[VE];
 #pragma unroll
-        for (int m = 0; m < VE; ++m) f[m] = s_o[wave * (R * RW) + lane * VE + m];
-        *reinterpret_cast<u32x4*>(o_t + lane * VE) = pack_io(f, op);
+            for (int m = 0; m < VE; ++m) f[m] = s_o[wave * (R * RW) + lane * VE + m];
+            *reinterpret_cast<u32x4*>(o_t + lane * VE) = pack_io(f, op);
+          }
+        } else {  // fewer rows per wave than one vector holds (d_k = 256)
+          if (lane < R * RW && vb * RPW + wave * (R * RW) + lane < DV)
+            st_io(o_t + lane, s_o[wave * (R * RW) + lane]);
+        }
       }
-    } else {  // fewer rows per wave than one vector holds (d_k = 256)
-      if (lane < R * RW && vb * RPW + wave * (R * RW) + lane < DV) st_io(o_t + lane, s_o[wave * (R * RW) + lane]);
     }
   }
 
-  // ---- 7. final state back to the slot
-  if (p.write_final) {
+  // ---- 8. final state back to the slot
+  if (MODE == 0 && p.write_final) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (rv[r])
@@ -451,18 +553,40 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
   }
 }
 
-template <typename ST, typename IT, int DK, int R, int NW = 4>
+template <typename ST, typename IT, int DK, int R, int NW = 4, int MODE = 0>
 hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
   constexpr int RPW = NW * R * (64 / (DK / 16));
   const int nvb = (p.DV + RPW - 1) / RPW;
   const dim3 grid(unsigned(nvb), unsigned(p.Hv), unsigned(p.B));
-  const size_t lds = sizeof(float) * (size_t(2) * p.T * DK + size_t(p.T) * RPW + 3 * size_t(p.T) + RPW);
-  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW>), grid, dim3(NW * 64), lds, stream, p);
+  const size_t tmax = size_t(MODE == 2 ? 0 : p.T) + size_t(MODE == 0 ? 0 : p.rT);
+  const size_t lds = sizeof(float) * (2 * tmax * DK + tmax * RPW + 3 * tmax + RPW);
+  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW, MODE>), grid, dim3(NW * 64), lds, stream, p);
   return hipGetLastError();
 }
 
+// Plain calls choose among the measured launch shapes; replay calls use the default.
 template <typename ST, typename IT>
-hipError_t launch_dk(int shape, const RecurrentArgs& p, hipStream_t stream) {
+hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t stream) {
+  if (mode == 1) {
+    switch (p.DK) {
+      case 16: return launch_rec<ST, IT, 16, 1, 4, 1>(p, stream);
+      case 32: return launch_rec<ST, IT, 32, 1, 4, 1>(p, stream);
+      case 64: return launch_rec<ST, IT, 64, 1, 4, 1>(p, stream);
+      case 128: return launch_rec<ST, IT, 128, 1, 4, 1>(p, stream);
+      case 256: return launch_rec<ST, IT, 256, 1, 4, 1>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (mode == 2) {
+    switch (p.DK) {
+      case 16: return launch_rec<ST, IT, 16, 1, 4, 2>(p, stream);
+      case 32: return launch_rec<ST, IT, 32, 1, 4, 2>(p, stream);
+      case 64: return launch_rec<ST, IT, 64, 1, 4, 2>(p, stream);
+      case 128: return launch_rec<ST, IT, 128, 1, 4, 2>(p, stream);
+      case 256: return launch_rec<ST, IT, 256, 1, 4, 2>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.DK) {
     case 16: return launch_rec<ST, IT, 16, 1>(p, stream);
     case 32: return launch_rec<ST, IT, 32, 1>(p, stream);
@@ -479,12 +603,12 @@ hipError_t launch_dk(int shape, const RecurrentArgs& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_recurrent(Dt state, Dt io, int shape, const RecurrentArgs& p,
+hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, const RecurrentArgs& p,
                             hipStream_t stream) {
-  if (state == Dt::F32 && io == Dt::F32) return launch_dk<float, float>(shape, p, stream);
-  if (state == Dt::F32 && io == Dt::BF16) return launch_dk<float, bf16s>(shape, p, stream);
-  if (state == Dt::BF16 && io == Dt::F32) return launch_dk<bf16s, float>(shape, p, stream);
-  return launch_dk<bf16s, bf16s>(shape, p, stream);
+  if (state == Dt::F32 && io == Dt::F32) return launch_dk<float, float>(shape, mode, p, stream);
+  if (state == Dt::F32 && io == Dt::BF16) return launch_dk<float, bf16s>(shape, mode, p, stream);
+  if (state == Dt::BF16 && io == Dt::F32) return launch_dk<bf16s, float>(shape, mode, p, stream);
+  return launch_dk<bf16s, bf16s>(shape, mode, p, stream);
 }
 
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream) {

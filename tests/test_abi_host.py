@@ -131,6 +131,46 @@ def test_commit_validation(L):
     assert com(dims(batch=0, d_v=8)) == 5
 
 
+def tokens(**kw):
+    base = dict(k=A16 * 13, v=A16 * 14, a=A16 * 15, b=A16 * 16, T_src=4)
+    base.update(kw)
+    return gdn.GdnTokens(**base)
+
+
+def test_verify_replay_validation(L):
+    def vr(d, i=None, rep=None, rlen=A16 * 17, pool=A16 * 9, idx=A16 * 10, commit=1):
+        i = io() if i is None else i
+        rep = tokens() if rep is None else rep
+        return L.gdn_verify_replay(ctypes.byref(d), ctypes.byref(i), pool, idx,
+                                   ctypes.byref(rep) if rep != "null" else None, rlen, commit, None)
+    assert vr(dims(batch=0)) == 0
+    assert vr(dims(batch=0), rep=tokens(T_src=0)) == 2
+    assert vr(dims(batch=0, T=12), rep=tokens(T_src=5)) == 5          # T + T_src > GDN_MAX_T
+    assert vr(dims(), rep="null") == 1
+    assert vr(dims(), rep=tokens(v=None)) == 1
+    assert vr(dims(), rlen=None) == 1
+    assert vr(dims(), i=io(o=None)) == 1
+    assert vr(dims(), rep=tokens(k=A16 * 13 + 8)) == 4
+    assert vr(dims(), rep=tokens(a=A16 * 15 + 1)) == 4
+    assert vr(dims(), rlen=A16 * 17 + 2) == 4
+    assert vr(dims(), pool=A16 * 9 + 4) == 4
+
+
+def test_commit_replay_validation(L):
+    def cr(d, rep=None, rlen=A16 * 17, pool=A16 * 9, idx=A16 * 10, A=A16 * 6, dt=A16 * 7):
+        rep = tokens() if rep is None else rep
+        return L.gdn_commit_replay(ctypes.byref(d), A, dt, pool, idx, ctypes.byref(rep), rlen, None)
+    assert cr(dims(batch=0)) == 0
+    assert cr(dims(batch=0), rep=tokens(T_src=0)) == 2
+    assert cr(dims(batch=0), rep=tokens(T_src=gdn.GDN_MAX_T + 1)) == 5
+    assert cr(dims(), A=None) == 1
+    assert cr(dims(), rlen=None) == 1
+    assert cr(dims(), rep=tokens(b=None)) == 1
+    assert cr(dims(), rep=tokens(v=A16 * 14 + 4)) == 4
+    assert cr(dims(), dt=A16 * 7 + 2) == 4
+    assert cr(dims(d_k=48)) == 5
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1, 16)
