@@ -93,6 +93,10 @@ def main():
     ap.add_argument("--steps", type=int, default=8000)
     ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--workload", type=int, default=None, help="workload index (default: the MTP verify T=4 one)")
+    ap.add_argument("--mode", choices=("intermediate", "replay"), default="intermediate",
+                    help="intermediate: verify storing every intermediate state, then commit (the "
+                         "workload as defined); replay: cached-replay verify with in-kernel commit of the "
+                         "previous step's accepted prefix (one launch per step, no per-token states)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -117,8 +121,18 @@ def main():
     log(f"[bench] workload {wi}: {w.description}")
     x = workloads.make_inputs(w, seed=0)
     idx = x["idx"].numpy()
-    v_bytes = workloads.algorithmic_bytes(w, idx, "verify")
-    c_bytes = workloads.algorithmic_bytes(w, idx, "commit") if w.commit else 0
+    replay = args.mode == "replay"
+    if replay:
+        if w.mode == "decode":
+            sys.exit("bench.py: replay mode needs a verify workload")
+        # the previous step's tokens (its k, v, a, b) and accept lengths
+        xp = workloads.make_inputs(w, seed=1)
+        rlen = np.random.default_rng(2).integers(1, w.T + 1, w.batch).astype(np.int32)
+        v_bytes = workloads.replay_bytes(w, idx, rlen)
+        c_bytes = 0
+    else:
+        v_bytes = workloads.algorithmic_bytes(w, idx, "verify")
+        c_bytes = workloads.algorithmic_bytes(w, idx, "commit") if w.commit else 0
 
     # Rotating buffer sets, so that every launch reads its state from HBM: the pool
     # reads of all sets together exceed the 256 MB Infinity Cache four times over
@@ -132,6 +146,9 @@ def main():
     R = min(R, 1024, max(2, int(16e9 // set_bytes)))   # tiny workloads: latency-bound anyway
     shared = {n: x[n].to(dev) for n in ("idx", "accept", "prev_accept") if n in x}
     base = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    if replay:
+        shared["rlen"] = torch.from_numpy(rlen).to(dev)
+        base.update({"r" + n: xp[n].to(dev) for n in ("k", "v", "a", "b")})
     pool0 = workloads.to_device_state(x["pool"]).to(dev)
     cache0 = None
     if w.cache_T:
@@ -142,7 +159,7 @@ def main():
         s = {n: t.clone() for n, t in base.items()}
         s.update(shared)
         s["pool"] = pool0.clone()
-        s["cache"] = None if cache0 is None else cache0.clone()
+        s["cache"] = None if (cache0 is None or replay) else cache0.clone()
         s["o"] = torch.empty((w.batch, w.T, w.Hv, w.dv), dtype=x["v"].dtype, device=dev)
         sets.append(s)
     del pool0, cache0
@@ -150,7 +167,11 @@ def main():
     log(f"[bench] {R} rotating buffer sets, {touched / 1e6:.2f} MB touched per step")
 
     def verify(s):
-        if w.mode == "decode":
+        if replay:
+            gdn.gdn_verify_replay(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"],
+                                  s["pool"], s["idx"], s["rk"], s["rv"], s["ra"], s["rb"], s["rlen"], True,
+                                  scale=w.scale)
+        elif w.mode == "decode":
             gdn.gdn_decode(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"], s["pool"],
                            s["idx"], scale=w.scale)
         else:
@@ -158,7 +179,7 @@ def main():
                            s["idx"], s["cache"], w.write_final, s.get("prev_accept"), scale=w.scale)
 
     def commit(s):
-        if w.commit:
+        if w.commit and not replay:
             gdn.gdn_commit(s["cache"], s["idx"], s["accept"], s["pool"])
 
     def step(s):
@@ -279,17 +300,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "T": w.T, "num_k_heads": w.Hk, "num_v_heads": w.Hv,
                    "d_k": w.dk, "d_v": w.dv, "pool_slots": w.pool, "state_dtype": w.state_dtype,
-                   "io_dtype": w.io_dtype, "step": ("verify" if w.mode != "decode" else "decode") +
-                   (" + commit" if w.commit else ""), "rotating_buffer_sets": R,
+                   "io_dtype": w.io_dtype,
+                   "step": ("cached-replay verify with in-kernel commit (accept lengths U{1..T})" if replay else
+                            ("verify" if w.mode != "decode" else "decode") + (" + commit" if w.commit else "")),
+                   "rotating_buffer_sets": R,
                    "launch": "eager" if args.eager else "hip_graph", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_profiles(w.name),
-                     "kernel": "gdn_verify (recurrent_kernel)", "algorithmic_bytes_per_launch": v_bytes,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None if replay else traffic_from_profiles(w.name),
+                     "kernel": ("gdn_verify_replay" if replay else "gdn_verify") + " (recurrent_kernel)",
+                     "algorithmic_bytes_per_launch": v_bytes,
                      "avg_launch_us": us_ver},
         "verify_tokens_per_s": tokens / (us_ver * 1e-6),
         "copy_ceiling_GBps": copy_gbps,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not replay:
         log("[bench] CPU oracle baseline ...")
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
         log(f"[bench] CPU oracle: {res['cpu_baseline']['value']:.1f} tokens/s on {res['cpu_baseline']['cores']} threads")

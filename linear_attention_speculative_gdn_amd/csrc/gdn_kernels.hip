@@ -456,18 +456,32 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
       }
     const float gt = s_g[tau], bt = s_beta[tau], kqt = s_kq[tau];
     float rk[R], rq[R];
+    if (!REPLAY || tau >= n_rep) {  // a token with an output: S^T k and S^T q
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float pk0 = 0.f, pk1 = 0.f, pq0 = 0.f, pq1 = 0.f;
+      for (int r = 0; r < R; ++r) {
+        float pk0 = 0.f, pk1 = 0.f, pq0 = 0.f, pq1 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        pk0 = fmaf(S[r][e], kh_[e], pk0);
-        pk1 = fmaf(S[r][e + 1], kh_[e + 1], pk1);
-        pq0 = fmaf(S[r][e], qh_[e], pq0);
-        pq1 = fmaf(S[r][e + 1], qh_[e + 1], pq1);
+        for (int e = 0; e < 16; e += 2) {
+          pk0 = fmaf(S[r][e], kh_[e], pk0);
+          pk1 = fmaf(S[r][e + 1], kh_[e + 1], pk1);
+          pq0 = fmaf(S[r][e], qh_[e], pq0);
+          pq1 = fmaf(S[r][e + 1], qh_[e + 1], pq1);
+        }
+        rk[r] = group_sum<L>(pk0 + pk1);
+        rq[r] = group_sum<L>(pq0 + pq1);
       }
-      rk[r] = group_sum<L>(pk0 + pk1);
-      rq[r] = group_sum<L>(pq0 + pq1);
+    } else {  // a replayed token has no output: S^T k only
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float pk0 = 0.f, pk1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          pk0 = fmaf(S[r][e], kh_[e], pk0);
+          pk1 = fmaf(S[r][e + 1], kh_[e + 1], pk1);
+        }
+        rk[r] = group_sum<L>(pk0 + pk1);
+        rq[r] = 0.f;
+      }
     }
     const int t = tau - n_rep;  // index among this call's tokens (negative: replayed)
     ST* const cache_t = (cache_row && t >= 0) ? cache_row + t * cache_t_stride + h * tile : nullptr;
@@ -564,7 +578,10 @@ hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Plain calls choose among the measured launch shapes; replay calls use the default.
+// Plain calls choose among the measured launch shapes. Replay calls are bound by
+// vector ALU and LDS reads rather than HBM (up to twice the tokens per state pass, no
+// per-token stores): at d_k = 128 two rows per lane halve the k^/q^ reads from LDS
+// per state element, and 8 waves per workgroup keep more of them in flight.
 template <typename ST, typename IT>
 hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t stream) {
   if (mode == 1) {
@@ -572,7 +589,7 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
       case 16: return launch_rec<ST, IT, 16, 1, 4, 1>(p, stream);
       case 32: return launch_rec<ST, IT, 32, 1, 4, 1>(p, stream);
       case 64: return launch_rec<ST, IT, 64, 1, 4, 1>(p, stream);
-      case 128: return launch_rec<ST, IT, 128, 1, 4, 1>(p, stream);
+      case 128: return launch_rec<ST, IT, 128, 2, 8, 1>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 1, 4, 1>(p, stream);
       default: return hipErrorInvalidValue;
     }
@@ -582,7 +599,7 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
       case 16: return launch_rec<ST, IT, 16, 1, 4, 2>(p, stream);
       case 32: return launch_rec<ST, IT, 32, 1, 4, 2>(p, stream);
       case 64: return launch_rec<ST, IT, 64, 1, 4, 2>(p, stream);
-      case 128: return launch_rec<ST, IT, 128, 1, 4, 2>(p, stream);
+      case 128: return launch_rec<ST, IT, 128, 2, 8, 2>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 1, 4, 2>(p, stream);
       default: return hipErrorInvalidValue;
     }

@@ -174,6 +174,22 @@ def state_read_bytes(w: Workload, idx: np.ndarray) -> int:
     return valid * w.Hv * w.dk * w.dv * ssz
 
 
+def replay_bytes(w: Workload, idx: np.ndarray, rlen: np.ndarray, commit: bool = True) -> int:
+    """Bytes one cached-replay verify must move: each valid tile read once, written once
+    more if its row commits a replayed prefix, the new tokens' io and o, and the
+    replayed tokens' k, v, a, b."""
+    ssz = 4 if w.state_dtype == "f32" else 2
+    isz = 4 if w.io_dtype == "f32" else 2
+    valid = (idx >= 0) & (idx < w.pool)
+    n = np.where(valid & (rlen >= 0) & (rlen <= w.T), rlen, 0)
+    tile = w.dk * w.dv * ssz
+    state = int(valid.sum()) * w.Hv * tile + (int(np.sum(valid & (n >= 1))) * w.Hv * tile if commit else 0)
+    per_tok = (2 * w.Hk * w.dk + w.Hv * w.dv + 2 * w.Hv) * isz
+    io = int(valid.sum()) * w.T * per_tok + w.batch * w.T * w.Hv * w.dv * isz
+    io += int(n.sum()) * (w.Hk * w.dk + w.Hv * w.dv + 2 * w.Hv) * isz
+    return state + io + w.batch * 8 + 2 * w.Hv * 4
+
+
 def algorithmic_bytes(w: Workload, idx: np.ndarray, kind: str) -> int:
     """Bytes the method must move for one call: each valid (row, v-head) state tile
     read once and written once per stored state, plus the per-token io.
