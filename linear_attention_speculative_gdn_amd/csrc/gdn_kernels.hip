@@ -223,13 +223,20 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   const IT* bp = static_cast<const IT*>(p.b);
   IT* op = static_cast<IT*>(p.o);
 
+  // The per-row scalars first, as scalar loads issued together (the compiler reads
+  // memory with scalar loads only before anything that might write it, hence the
+  // barrier after them), so that one wait on the slot index covers them all.
   const int32_t slot = p.idx[row];
   const int32_t n_prev = (MODE == 0 && p.prev_accept) ? p.prev_accept[row] : 0;
   int32_t n_rep = 0;
+  float a_log = 0.f, dtb = 0.f;  // replay modes: the gate parameters, read up front
   if constexpr (REPLAY) {
     const int32_t x = p.rlen[row];
     n_rep = (x >= 0 && x <= p.rT) ? x : 0;
+    a_log = p.A_log[h];
+    dtb = p.dt_bias[h];
   }
+  asm volatile("" ::: "memory");
   const int kh = h / p.G;
 
   // ---- 1. this call's per-token inputs (do not depend on the slot): q, k, v as
@@ -316,8 +323,13 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
       raw[r][c] = *reinterpret_cast<const u32x4*>(src + size_t(jr) * DK + (l + c * L) * CE);
   }
 
-  // ---- 4. token inputs -> LDS (replayed tokens first, then this call's); gates
-  const float A = expf(p.A_log[h]), dtb = p.dt_bias[h];
+  // ---- 4. token inputs -> LDS (replayed tokens first, then this call's); gates.
+  //         In mode 0, A_log and dt_bias are read only by the lanes that compute a
+  //         gate, after the state loads: reading them earlier, in every wave or in
+  //         wave 0 only, as scalar or as vector loads, measured 15-20 % slower on the
+  //         small MTP verify batch (B = 64, one wave of workgroups), though decode
+  //         gained 5 %. The replay modes, bound by arithmetic, gain 2-7 % from the
+  //         early read.
   if constexpr (REPLAY) {
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
@@ -346,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
     }
     if (tid < n_rep) {
       const float x = ra_in + dtb;
-      s_g[tid] = expf(-A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))));
+      s_g[tid] = expf(-expf(a_log) * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))));
       s_beta[tid] = 1.f / (1.f + expf(-rb_in));
     }
   }
@@ -380,8 +392,8 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
       }
     }
     if (tid < T) {
-      const float x = a_in + dtb;
-      s_g[n_rep + tid] = expf(-A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))));
+      const float x = a_in + (REPLAY ? dtb : p.dt_bias[h]);
+      s_g[n_rep + tid] = expf(-expf(REPLAY ? a_log : p.A_log[h]) * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))));
       s_beta[n_rep + tid] = 1.f / (1.f + expf(-b_in));
     }
   }
