@@ -17,7 +17,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_SRCS = [os.path.join(_HERE, "gdn_oracle.c"), os.path.join(_HERE, "conv_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
 _lib = None
 
@@ -27,7 +27,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -39,6 +39,11 @@ class Dims(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("pool_slots", ctypes.c_int32), ("state_bf16", ctypes.c_int32),
                 ("scale", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+class ConvDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("T", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("pool_slots", ctypes.c_int32), ("activation", ctypes.c_int32)]
 
 
 _D = ctypes.POINTER(ctypes.c_double)
@@ -72,6 +77,11 @@ def lib():
         L.oracle_commit_replay.argtypes = ([ctypes.POINTER(Dims), _D, _D, _D, _I] + [_D] * 4 +
                                            [ctypes.c_int32, _I, ctypes.c_int32])
         L.oracle_commit_replay.restype = ctypes.c_int32
+        CD = ctypes.POINTER(ConvDims)
+        L.oracle_conv_update.argtypes = [CD, _D, _D, _D, _D, _I, _D, ctypes.c_int32, _I, _D, ctypes.c_int32]
+        L.oracle_conv_update.restype = ctypes.c_int32
+        L.oracle_conv_commit.argtypes = [CD, _D, _D, _I, _I]
+        L.oracle_conv_commit.restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -201,4 +211,38 @@ def commit_replay(dims: Dims, A_log, dt_bias, pool, idx, rk, rv, ra, rb, rlen, *
                                     _nthreads(nthreads))
     if rc:
         raise ValueError("oracle_commit_replay: invalid dimensions")
+    return pool
+
+
+def make_conv_dims(batch, T, channels, width, pool, activation="silu") -> ConvDims:
+    return ConvDims(batch, T, channels, width, pool, {"none": 0, "silu": 1}[activation])
+
+
+def conv_update(dims: ConvDims, x, w, bias, pool, idx, *, prev_x=None, prev_len=None,
+                write_back: bool = False) -> dict:
+    """Short causal convolution of this call's tokens (x [B, T, D]) from each valid row's
+    slot state (pool [P, K-1, D]); optional fused commit of prev_x's first prev_len[r]
+    tokens before, optional write-back of the advanced state after. Returns dict(y, pool)."""
+    B, T, D = dims.batch, dims.T, dims.channels
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    pool = _f64(pool).copy()
+    y = np.zeros((B, T, D), dtype=np.float64)
+    px = None if prev_x is None else _f64(prev_x)
+    T_prev = 0 if px is None else px.shape[1]
+    pl = None if px is None else _i32(prev_len)
+    rc = lib().oracle_conv_update(ctypes.byref(dims), _p(x), _p(w), _p(b), _p(pool), _p(_i32(idx), _I), _p(px),
+                                  int(T_prev), _p(pl, _I), _p(y), int(bool(write_back)))
+    if rc:
+        raise ValueError("oracle_conv_update: invalid dimensions")
+    return dict(y=y, pool=pool)
+
+
+def conv_commit(dims: ConvDims, x, pool, idx, accept) -> np.ndarray:
+    """Accepted-prefix commit of the convolution state. Returns the new pool."""
+    pool = _f64(pool).copy()
+    rc = lib().oracle_conv_commit(ctypes.byref(dims), _p(_f64(x)), _p(pool), _p(_i32(idx), _I),
+                                  _p(_i32(accept), _I))
+    if rc:
+        raise ValueError("oracle_conv_commit: invalid dimensions")
     return pool

@@ -218,3 +218,94 @@ def algorithmic_bytes(w: Workload, idx: np.ndarray, kind: str) -> int:
     if w.mode == "verify_fused":
         io += B * 4
     return state + io
+
+
+# ---------------------------------------------------------------- short convolution
+# The short causal convolution over the mixed q/k/v channels whose state sits in a pool
+# next to the GDN state (TensorRT-LLM PR 20937, What changes: the in_proj GEMV's fused
+# conv1d epilogue for verify and decode rows; Per-File QA Perspective: convolution state
+# staged and committed per accepted prefix). Its channels are D = 2*Hk*dk + Hv*dv of
+# the GDN layer it feeds; width K = 4.
+#
+# Recipe (one ``numpy.random.default_rng(seed)``, in this order): slot indices as for
+# the GDN workloads; x ~ N(0,1) [B,T,D]; taps w ~ N(0, 1/K) [K,D] and bias ~ N(0, 0.1)
+# [D] (fp32); the state pool ~ N(0,1) [P,K-1,D] (earlier inputs); accept lengths
+# ~ U{1..T}; the previous step's inputs ~ N(0,1) [B,T,D] and accept lengths ~ U{1..T}.
+# x, the pool and the previous inputs are stored in the workload's dtype.
+
+
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    batch: int
+    T: int
+    channels: int
+    width: int
+    pool: int
+    dtype: str                # "f32" | "bf16"
+    mode: str                 # "verify" (read-only) | "fused" (commit of the previous step, then verify) | "decode"
+    activation: str = "silu"
+    n_pad: int = 0
+    description: str = ""
+
+    def replace(self, **kw) -> "ConvWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+def conv_channels(Hk: int, Hv: int, dk: int, dv: int) -> int:
+    return 2 * Hk * dk + Hv * dv
+
+
+CONV_WORKLOADS: list[ConvWorkload] = [
+    ConvWorkload("conv-tiny-f32", batch=3, T=2, channels=16, width=4, pool=5, dtype="f32", mode="fused", n_pad=1,
+                 description="tiny: B=3 (1 padding), T=2, D=16, K=4, fp32, fused commit"),
+    ConvWorkload("conv-mtp-t4-bf16", batch=64, T=4, channels=conv_channels(4, 8, 128, 128), width=4, pool=256,
+                 dtype="bf16", mode="fused",
+                 description="MTP verify T=4 of the headline GDN layer: B=64, D=2048, K=4, bf16, fused commit"),
+    ConvWorkload("conv-decode-f32", batch=64, T=1, channels=conv_channels(4, 8, 128, 128), width=4, pool=256,
+                 dtype="f32", mode="decode", n_pad=8,
+                 description="decode: B=64 (8 padding), D=2048, K=4, fp32, state written back"),
+    ConvWorkload("conv-t8-bf16", batch=128, T=8, channels=conv_channels(16, 32, 128, 128), width=4, pool=1024,
+                 dtype="bf16", mode="fused", n_pad=13,
+                 description="verify T=8: B=128 (13 padding), D=8192, K=4, bf16, fused commit"),
+]
+CONV_HEADLINE = 1
+
+
+def make_conv_inputs(w: ConvWorkload, seed: int = 0) -> dict:
+    """Draw one batch of short-convolution inputs. Returns CPU torch tensors."""
+    rng = np.random.default_rng(seed)
+    B, T, D, K, P = w.batch, w.T, w.channels, w.width, w.pool
+    assert B <= P, "more rows than pool slots"
+    idx = rng.permutation(P)[:B].astype(np.int32)
+    if w.n_pad:
+        idx[rng.choice(B, size=w.n_pad, replace=False)] = -1
+    x = rng.standard_normal((B, T, D))
+    taps = rng.normal(0.0, 1.0 / math.sqrt(K), (K, D))
+    bias = rng.normal(0.0, 0.1, D)
+    pool = rng.standard_normal((P, K - 1, D), dtype=np.float32)
+    accept = rng.integers(1, T + 1, B).astype(np.int32)
+    prev_x = rng.standard_normal((B, T, D))
+    prev_len = rng.integers(1, T + 1, B).astype(np.int32)
+    return dict(idx=torch.from_numpy(idx), x=_store(x, w.dtype),
+                w=torch.from_numpy(taps.astype(np.float32)), bias=torch.from_numpy(bias.astype(np.float32)),
+                pool=_store(pool, w.dtype), accept=torch.from_numpy(accept),
+                prev_x=_store(prev_x, w.dtype), prev_len=torch.from_numpy(prev_len))
+
+
+def conv_bytes(w: ConvWorkload, idx: np.ndarray, prev_len: np.ndarray | None = None) -> int:
+    """Bytes one convolution update must move: x of valid rows, y of all rows, taps and
+    bias, the K-1 state rows of each valid row read once, written once when the row
+    commits (fused commit with 1 <= prev_len <= T, or write-back), plus the previous
+    step's inputs that the commit selects (at most K-1 per row)."""
+    esz = 4 if w.dtype == "f32" else 2
+    B, T, D, H = w.batch, w.T, w.channels, w.width - 1
+    valid = (idx >= 0) & (idx < w.pool)
+    nv = int(valid.sum())
+    total = nv * T * D * esz + B * T * D * esz + (H + 2) * D * 4 + B * 4 + nv * H * D * esz
+    if w.mode == "decode":
+        total += nv * H * D * esz
+    elif w.mode == "fused" and prev_len is not None:
+        n = np.where(valid & (prev_len >= 1) & (prev_len <= T), prev_len, 0)
+        total += int(np.sum(n >= 1)) * H * D * esz + int(np.minimum(n, H).sum()) * D * esz + B * 4
+    return total
