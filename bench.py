@@ -87,16 +87,159 @@ def cpu_baseline(w, x, budget_s: float) -> dict:
                       f"in {el:.1f} s, float64, OpenMP over (row, v-head) tiles"}
 
 
+class Runner:
+    """n calls of ``fn`` over rotating buffer sets, replayed from HIP graphs captured
+    beforehand (``prepare(n)`` captures whatever ``run(n)`` replays), or launched eagerly."""
+
+    def __init__(self, fn, sets, stream, eager: bool, per_replay: int):
+        self.fn, self.sets, self.stream, self.eager, self.per_replay = fn, sets, stream, eager, per_replay
+        self.graphs, self.pos = {}, 0
+
+    def _capture(self, n):
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for i in range(n):
+                self.fn(self.sets[i % len(self.sets)])
+        return g
+
+    def prepare(self, n):
+        if self.eager:
+            return
+        full, rest = divmod(n, self.per_replay)
+        for k in ([self.per_replay] if full else []) + ([rest] if rest else []):
+            if k not in self.graphs:
+                self.graphs[k] = self._capture(k)
+
+    def run(self, n):
+        if self.eager:
+            for i in range(n):
+                self.fn(self.sets[(self.pos + i) % len(self.sets)])
+            self.pos += n
+            return
+        full, rest = divmod(n, self.per_replay)
+        for _ in range(full):
+            self.graphs[self.per_replay].replay()
+        if rest:
+            self.graphs[rest].replay()
+
+    def warm(self, n):
+        import torch
+        self.prepare(n)
+        with torch.cuda.stream(self.stream):
+            self.run(n)
+        torch.cuda.synchronize()
+
+    def timed(self, n) -> float:
+        """Seconds for n calls, HIP events on the launch stream."""
+        import torch
+        self.prepare(n)
+        cs = self.stream if not self.eager else torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cs):
+            e0.record(cs)
+            self.run(n)
+            e1.record(cs)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+
+def copy_ceiling_gbps(dev) -> float:
+    """A plain 1 GiB device copy, same event protocol: the practical streaming ceiling."""
+    import torch
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 10 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
+
+
+def conv_main(args):
+    """The short causal convolution kept next to the GDN state: one gdn_conv_update per
+    step (fused commit of the previous step's accepted prefix, then this step's tokens;
+    write-back for the decode workload), same cold protocol as the GDN path."""
+    import numpy as np
+    import torch
+
+    import linear_attention_speculative_gdn_amd as gdn
+    import workloads
+
+    wi = workloads.CONV_HEADLINE if args.workload is None else args.workload
+    w = workloads.CONV_WORKLOADS[wi]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] conv workload {wi}: {w.description}")
+    x = workloads.make_conv_inputs(w, seed=0)
+    idx, plen = x["idx"].numpy(), x["prev_len"].numpy()
+    fused, wb = w.mode == "fused", w.mode == "decode"
+    nbytes = workloads.conv_bytes(w, idx, plen if fused else None)
+    esz = x["x"].element_size()
+    state_read = int(((idx >= 0) & (idx < w.pool)).sum()) * (w.width - 1) * w.channels * esz
+    set_bytes = sum(x[n].numel() * x[n].element_size() for n in ("x", "prev_x", "pool")) + x["x"].numel() * esz
+    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / max(1, state_read)))
+    R = min(R, 1024, max(2, int(16e9 // set_bytes)))
+    shared = {n: x[n].to(dev) for n in ("idx", "prev_len", "w", "bias")}
+    sets = []
+    for _ in range(R):
+        s = {n: x[n].to(dev) for n in ("x", "prev_x", "pool")}
+        s.update(shared)
+        s["y"] = torch.empty_like(s["x"])
+        sets.append(s)
+    torch.cuda.synchronize()
+    log(f"[bench] {R} rotating buffer sets, {nbytes / 1e6:.2f} MB algorithmic per call")
+
+    def call(s):
+        gdn.gdn_conv_update(s["x"], s["w"], s["bias"], s["pool"], s["idx"], s["y"],
+                            prev_x=s["prev_x"] if fused else None, prev_len=s["prev_len"] if fused else None,
+                            write_back=wb, activation=w.activation)
+
+    call(sets[0])
+    torch.cuda.synchronize()
+    run = Runner(call, sets, torch.cuda.Stream(), args.eager, R * max(1, 200 // R))
+    run.warm(args.warmup)
+    t = run.timed(args.steps)
+    us = t / args.steps * 1e6
+    achieved = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] conv: {us:.2f} us/launch, {achieved:.1f} GB/s algorithmic, {achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s")
+    res = {
+        "metric": "GDN short-conv update tokens/s (batch x T) + achieved HBM GB/s vs peak",
+        "value": w.batch * w.T / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "T": w.T, "channels": w.channels, "width": w.width,
+                   "pool_slots": w.pool, "dtype": w.dtype, "activation": w.activation,
+                   "step": "conv update" + (" with fused commit" if fused else "") + (" + write-back" if wb else ""),
+                   "rotating_buffer_sets": R, "launch": "eager" if args.eager else "hip_graph",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "gdn_conv_update (conv_kernel)",
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": us},
+    }
+    del np
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8000)
     ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--workload", type=int, default=None, help="workload index (default: the MTP verify T=4 one)")
-    ap.add_argument("--mode", choices=("intermediate", "replay"), default="intermediate",
+    ap.add_argument("--mode", choices=("intermediate", "replay", "conv"), default="intermediate",
                     help="intermediate: verify storing every intermediate state, then commit (the "
                          "workload as defined); replay: cached-replay verify with in-kernel commit of the "
-                         "previous step's accepted prefix (one launch per step, no per-token states)")
+                         "previous step's accepted prefix (one launch per step, no per-token states); conv: "
+                         "the short causal convolution next to the GDN state (--workload indexes the "
+                         "convolution workloads)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -104,9 +247,12 @@ def main():
                     help="also run a 256 MiB device copy (known bytes) for counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the GDN state "
-              "update shards by head or request with no collective, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the GDN state update "
+              "shards by v-head or by request row with no collective, so N GPUs each run this one-GPU step "
+              "on their share", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "conv":
+        return conv_main(args)
 
     import numpy as np
     import torch
@@ -187,71 +333,19 @@ def main():
         commit(s)
 
     stream = torch.cuda.Stream()
-
-    def make_runner(fn, n_per_replay):
-        """run(n): n calls of fn over the rotating sets, from HIP graphs captured
-        beforehand (prepare(n) captures whatever run(n) will replay)."""
-        if args.eager:
-            pos = [0]
-
-            def run(n):
-                for i in range(n):
-                    fn(sets[(pos[0] + i) % R])
-                pos[0] += n
-            return (lambda n: None), run
-        graphs = {}
-
-        def capture(n):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(n):
-                    fn(sets[i % R])
-            return g
-
-        def prepare(n):
-            full, rest = divmod(n, n_per_replay)
-            for k in ([n_per_replay] if full else []) + ([rest] if rest else []):
-                if k not in graphs:
-                    graphs[k] = capture(k)
-
-        def run(n):
-            full, rest = divmod(n, n_per_replay)
-            for _ in range(full):
-                graphs[n_per_replay].replay()
-            if rest:
-                graphs[rest].replay()
-        return prepare, run
-
     step(sets[0])  # first launches load the code objects, outside any capture
     torch.cuda.synchronize()
     per_replay = R * max(1, 200 // R)
-    prep_step, run_step = make_runner(step, per_replay)
-    prep_verify, run_verify = make_runner(verify, per_replay)
+    run_step = Runner(step, sets, stream, args.eager, per_replay)
+    run_verify = Runner(verify, sets, stream, args.eager, per_replay)
 
-    def timed(prepare, run, n):
-        prepare(n)
-        cs = stream if not args.eager else torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(cs):
-            e0.record(cs)
-            run(n)
-            e1.record(cs)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3
-
-    prep_step(args.warmup)
-    with torch.cuda.stream(stream):
-        run_step(args.warmup)
-    torch.cuda.synchronize()
-    t_step = timed(prep_step, run_step, args.steps)
+    run_step.warm(args.warmup)
+    t_step = run_step.timed(args.steps)
     log(f"[bench] {args.steps} steps in {t_step * 1e3:.3f} ms -> {t_step / args.steps * 1e6:.2f} us/step")
 
     # the dominant kernel on its own, same protocol
-    prep_verify(args.warmup)
-    with torch.cuda.stream(stream):
-        run_verify(args.warmup)
-    t_ver = timed(prep_verify, run_verify, args.steps)
+    run_verify.warm(args.warmup)
+    t_ver = run_verify.timed(args.steps)
     us_ver = t_ver / args.steps * 1e6
     achieved = v_bytes / (us_ver * 1e-6) / 1e9
     log(f"[bench] verify alone: {us_ver:.2f} us/launch, {achieved:.1f} GB/s algorithmic "
@@ -268,19 +362,7 @@ def main():
             torch.cuda.synchronize()
         del a_, b_
 
-    # practical ceiling: a plain device copy of 1 GiB, same event protocol
-    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 10 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    copy_gbps = copy_ceiling_gbps(dev)
     log(f"[bench] device copy ceiling: {copy_gbps:.1f} GB/s")
 
     tokens = w.batch * w.T

@@ -15,6 +15,9 @@
  *      Perspective and Moved out of this PR -- bf16 or fp32 recurrent pools, commit of
  *      the accepted prefix in-kernel (below 16 requests) or by a separate all-layer
  *      commit, duplicate rows, graph capture and replay.
+ * [P4] "Proposal: native BF16 MTP speculative decoding for dense Qwen3.8-27B
+ *      (qwen38_dense), with results on SM120": What -- recovery records and the
+ *      convolution state committed with them.
  *
  * The update (the pages name the gated delta rule without printing it; this is its
  * standard form). For request row r, v-head h, k-head kh = h / (Hv/Hk), token t:
@@ -170,6 +173,59 @@ GDN_API gdn_status gdn_verify_replay(const gdn_dims* dims, const gdn_io* io, voi
 GDN_API gdn_status gdn_commit_replay(const gdn_dims* dims, const float* A_log, const float* dt_bias,
                                      void* state_pool, const int32_t* state_indices,
                                      const gdn_tokens* replay, const int32_t* replay_len, void* stream);
+
+/* ---- Short causal convolution state, pooled next to the GDN state ------------------
+ * [P3] What changes: the GDN in_proj GEMV carries a fused conv1d epilogue for verify and
+ * decode rows; Per-File QA Perspective: the speculative staging and commit kernels keep
+ * accepted-prefix boundaries of the convolution state along with the other per-request
+ * state. [P4] "Proposal: native BF16 MTP speculative decoding for dense Qwen3.8-27B",
+ * What: the verify keeps recovery records and commits the convolution state with them.
+ * The pages do not print the convolution; this is the standard depthwise causal form of
+ * width K, per request row r and channel c:
+ *     in(tau) = x[r][tau][c] (tau >= 0),   state[slot][K-1+tau][c] (-(K-1) <= tau < 0)
+ *     y[r][t][c] = act(bias[c] + sum_{i<K} w[i][c] * in(t-(K-1)+i)),   act = id | SiLU
+ * The state of a slot is its last K-1 inputs, oldest first. Advancing it over n tokens
+ * keeps the last K-1 entries of (state ++ those tokens): an exact selection, so a commit
+ * or a rejected draft never rounds it.
+ * Layouts: x, y [B][T][D] and prev_x [B][T_prev][D] and conv_pool [P][K-1][D] in the
+ * dims' dtype; weight [K][D] fp32 (tap i multiplies the input K-1-i tokens back); bias
+ * [D] fp32 or NULL; state_indices, prev_len, accept_len [B] int32.
+ * Geometry: D a multiple of 8 (bf16) or 4 (fp32); 2 <= K <= GDN_CONV_MAX_WIDTH;
+ * 1 <= T <= GDN_MAX_T; B <= 65535. x, y, prev_x, conv_pool, weight and bias are
+ * 16-byte aligned. Padding rows get y = 0 and no state access. The conventions above
+ * (batch 0, errors before launch, one launch, no allocation, distinct indices in
+ * writing calls) apply. */
+#define GDN_CONV_MAX_WIDTH 8
+typedef enum { GDN_CONV_ACT_NONE = 0, GDN_CONV_ACT_SILU = 1 } gdn_conv_act;
+
+typedef struct {
+  int32_t batch;
+  int32_t T;           /* tokens per row of x */
+  int32_t channels;    /* D */
+  int32_t width;       /* K */
+  int32_t pool_slots;  /* P */
+  int32_t dtype;       /* gdn_dtype of x, y, prev_x and conv_pool */
+  int32_t activation;  /* gdn_conv_act */
+} gdn_conv_dims;
+
+/* Verify or decode of the convolution. For each valid row: (1) when prev_x is given and
+ * 1 <= prev_len[r] <= T_prev, the slot's state advances over the first prev_len[r]
+ * tokens of prev_x and is written back (the fused commit of the previous step's
+ * accepted prefix); (2) y of this call's T tokens from that state; (3) when write_back,
+ * the state advanced over all T tokens is written back (decode). Without prev_x and
+ * write_back the pool is read-only. prev_x needs prev_len and 1 <= T_prev <= GDN_MAX_T,
+ * and must not alias x. */
+GDN_API gdn_status gdn_conv_update(const gdn_conv_dims* dims, const void* x, const float* weight,
+                                   const float* bias, void* conv_pool, const int32_t* state_indices,
+                                   const void* prev_x, int32_t T_prev, const int32_t* prev_len,
+                                   void* y, int32_t write_back, void* stream);
+
+/* Accepted-prefix commit of the convolution state: for each valid row with
+ * 1 <= accept_len[r] <= T, the slot's state advances over the first accept_len[r]
+ * tokens of x; other rows are untouched. Reads dims->batch, T, channels, width,
+ * pool_slots and dtype. */
+GDN_API gdn_status gdn_conv_commit(const gdn_conv_dims* dims, const void* x, void* conv_pool,
+                                   const int32_t* state_indices, const int32_t* accept_len, void* stream);
 
 /* Static text for a status code (never NULL). */
 GDN_API const char* gdn_status_string(gdn_status status);

@@ -24,7 +24,8 @@ GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
 EXPORTED = ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
-            "gdn_status_string", "gdn_abi_version")
+            "gdn_conv_update", "gdn_conv_commit", "gdn_status_string", "gdn_abi_version")
+GDN_CONV_MAX_WIDTH = 8
 GDN_MAX_T = 16
 
 
@@ -52,6 +53,12 @@ class GdnTokens(ctypes.Structure):
                 ("T_src", ctypes.c_int32)]
 
 
+class GdnConvDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("T", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("pool_slots", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("activation", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -71,7 +78,11 @@ def lib() -> ctypes.CDLL:
         TK = ctypes.POINTER(GdnTokens)
         L.gdn_verify_replay.argtypes = [D, I, vp, vp, TK, vp, i32, vp]
         L.gdn_commit_replay.argtypes = [D, vp, vp, vp, vp, TK, vp, vp]
-        for f in ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay"):
+        CD = ctypes.POINTER(GdnConvDims)
+        L.gdn_conv_update.argtypes = [CD, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp]
+        L.gdn_conv_commit.argtypes = [CD, vp, vp, vp, vp, vp]
+        for f in ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+                  "gdn_conv_update", "gdn_conv_commit"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
@@ -253,3 +264,67 @@ def gdn_commit_replay(A_log, dt_bias, state_pool, state_indices, replay_k, repla
     st = lib().gdn_commit_replay(ctypes.byref(dims), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool),
                                  _ptr(state_indices), ctypes.byref(rep), _ptr(replay_len), _stream(dev, stream))
     _raise(st, "gdn_commit_replay")
+
+
+# ---------------------------------------------------------------- short convolution
+# Layouts: x, y [B,T,D]; prev_x [B,T_prev,D]; conv_pool [P,K-1,D] (x's dtype); weight
+# [K,D] fp32; bias [D] fp32 or None; state_indices, prev_len, accept_len [B] int32.
+
+_ACT = {"none": 0, "silu": 1}
+
+
+def _conv_dims(x, conv_pool, state_indices, activation="silu") -> GdnConvDims:
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    _need(x, "x", 3, dev); _need(conv_pool, "conv_pool", 3, dev); _need(state_indices, "state_indices", 1, dev)
+    B, T, D = x.shape
+    P, H = conv_pool.shape[0], conv_pool.shape[1]
+    if conv_pool.shape[2] != D or conv_pool.dtype != x.dtype:
+        raise ValueError(f"conv_pool must be [P, K-1, {D}] of x's dtype")
+    if state_indices.shape != (B,) or state_indices.dtype != torch.int32:
+        raise ValueError("state_indices must be int32 [B]")
+    return GdnConvDims(B, T, D, H + 1, P, _dt(x), _ACT[activation])
+
+
+def gdn_conv_update(x, weight, bias, conv_pool, state_indices, y, *, prev_x=None, prev_len=None,
+                    write_back=False, activation="silu", stream=None) -> None:
+    """Short causal convolution of this call's tokens from each valid row's slot state:
+    optional fused commit of prev_x's first prev_len[r] tokens before, optional
+    write-back of the state advanced over all tokens after (decode)."""
+    dims = _conv_dims(x, conv_pool, state_indices, activation)
+    dev = x.device
+    _need(weight, "weight", 2, dev); _need(y, "y", 3, dev)
+    if weight.shape != (dims.width, dims.channels) or weight.dtype != torch.float32:
+        raise ValueError(f"weight must be float32 [K, D] = [{dims.width}, {dims.channels}]")
+    if bias is not None:
+        _need(bias, "bias", 1, dev)
+        if bias.shape != (dims.channels,) or bias.dtype != torch.float32:
+            raise ValueError("bias must be float32 [D]")
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("y must match x")
+    T_prev = 0
+    if prev_x is not None:
+        _need(prev_x, "prev_x", 3, dev); _need(prev_len, "prev_len", 1, dev)
+        if prev_x.shape[0] != dims.batch or prev_x.shape[2] != dims.channels or prev_x.dtype != x.dtype:
+            raise ValueError("prev_x must be [B, T_prev, D] of x's dtype")
+        if prev_len.shape != (dims.batch,) or prev_len.dtype != torch.int32:
+            raise ValueError("prev_len must be int32 [B]")
+        T_prev = prev_x.shape[1]
+    st = lib().gdn_conv_update(ctypes.byref(dims), _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_pool),
+                               _ptr(state_indices), _ptr(prev_x), int(T_prev),
+                               _ptr(prev_len) if prev_x is not None else None, _ptr(y), int(bool(write_back)),
+                               _stream(dev, stream))
+    _raise(st, "gdn_conv_update")
+
+
+def gdn_conv_commit(x, conv_pool, state_indices, accept_len, *, stream=None) -> None:
+    """Accepted-prefix commit of the convolution state: each valid slot advances over the
+    first accept_len[r] tokens of x (1 <= accept_len[r] <= T; other rows untouched)."""
+    dims = _conv_dims(x, conv_pool, state_indices)
+    _need(accept_len, "accept_len", 1, x.device)
+    if accept_len.shape != (dims.batch,) or accept_len.dtype != torch.int32:
+        raise ValueError("accept_len must be int32 [B]")
+    st = lib().gdn_conv_commit(ctypes.byref(dims), _ptr(x), _ptr(conv_pool), _ptr(state_indices),
+                               _ptr(accept_len), _stream(x.device, stream))
+    _raise(st, "gdn_conv_commit")

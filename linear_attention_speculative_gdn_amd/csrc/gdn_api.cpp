@@ -99,6 +99,27 @@ void set_replay(gdn::RecurrentArgs& p, const gdn_tokens* rep, const int32_t* rle
   p.rcommit = commit ? 1 : 0;
 }
 
+// Checks of the convolution dims: sizes, dtype, geometry, grid limits.
+gdn_status check_conv_dims(const gdn_conv_dims* d) {
+  if (!d) return GDN_ERR_NULL;
+  if (d->batch < 0 || d->T < 1 || d->channels < 1 || d->width < 2 || d->pool_slots < 0) return GDN_ERR_SHAPE;
+  if (!dtype_ok(static_cast<gdn_dtype>(d->dtype))) return GDN_ERR_DTYPE;
+  if (d->activation != GDN_CONV_ACT_NONE && d->activation != GDN_CONV_ACT_SILU) return GDN_ERR_UNSUPPORTED;
+  const int ve = 16 / int(dsize(static_cast<gdn_dtype>(d->dtype)));
+  if (d->channels % ve != 0 || d->width > GDN_CONV_MAX_WIDTH || d->T > GDN_MAX_T) return GDN_ERR_UNSUPPORTED;
+  if (d->batch > 65535) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn::ConvArgs conv_args(const gdn_conv_dims* d) {
+  gdn::ConvArgs p;
+  p.x = nullptr; p.w = nullptr; p.bias = nullptr; p.pool = nullptr; p.idx = nullptr;
+  p.prev_x = nullptr; p.prev_len = nullptr; p.y = nullptr;
+  p.B = d->batch; p.T = d->T; p.D = d->channels; p.K = d->width; p.P = d->pool_slots; p.T_prev = 0;
+  p.write_back = 0; p.activation = d->activation;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,6 +218,41 @@ gdn_status gdn_commit_replay(const gdn_dims* dims, const float* A_log, const flo
   set_replay(p, replay, replay_len, 1);
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
                                              1, 2, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status gdn_conv_update(const gdn_conv_dims* dims, const void* x, const float* weight, const float* bias,
+                           void* conv_pool, const int32_t* state_indices, const void* prev_x, int32_t T_prev,
+                           const int32_t* prev_len, void* y, int32_t write_back, void* stream) {
+  gdn_status s = check_conv_dims(dims);
+  if (s != GDN_OK) return s;
+  if (prev_x && (T_prev < 1 || T_prev > GDN_MAX_T)) return GDN_ERR_SHAPE;
+  if (dims->batch == 0) return GDN_OK;
+  if (!x || !weight || !conv_pool || !state_indices || !y || (prev_x && !prev_len)) return GDN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(conv_pool, 16) || !aligned(weight, 16) ||
+      (bias && !aligned(bias, 16)) || (prev_x && !aligned(prev_x, 16)) || !aligned(state_indices, 4) ||
+      (prev_len && !aligned(prev_len, 4)))
+    return GDN_ERR_ALIGN;
+  gdn::ConvArgs p = conv_args(dims);
+  p.x = x; p.w = weight; p.bias = bias; p.pool = conv_pool; p.idx = state_indices; p.y = y;
+  p.prev_x = prev_x; p.prev_len = prev_x ? prev_len : nullptr; p.T_prev = prev_x ? T_prev : 0;
+  p.write_back = write_back ? 1 : 0;
+  const hipError_t e = gdn::launch_conv(static_cast<Dt>(dims->dtype), false, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status gdn_conv_commit(const gdn_conv_dims* dims, const void* x, void* conv_pool,
+                           const int32_t* state_indices, const int32_t* accept_len, void* stream) {
+  gdn_status s = check_conv_dims(dims);
+  if (s != GDN_OK) return s;
+  if (dims->batch == 0) return GDN_OK;
+  if (!x || !conv_pool || !state_indices || !accept_len) return GDN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(conv_pool, 16) || !aligned(state_indices, 4) || !aligned(accept_len, 4))
+    return GDN_ERR_ALIGN;
+  gdn::ConvArgs p = conv_args(dims);
+  p.pool = conv_pool; p.idx = state_indices;
+  p.prev_x = x; p.prev_len = accept_len; p.T_prev = dims->T;
+  const hipError_t e = gdn::launch_conv(static_cast<Dt>(dims->dtype), true, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

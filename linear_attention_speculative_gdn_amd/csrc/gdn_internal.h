@@ -1,5 +1,5 @@
 // gdn_internal.h -- launch descriptors shared by the host entry points (gdn_api.cpp)
-// and the gfx950 kernels (gdn_kernels.hip). Not part of the public ABI.
+// and the gfx950 kernels (gdn_kernels.hip, gdn_conv.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,6 +55,24 @@ struct CommitArgs {
 hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, const RecurrentArgs& p,
                             hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream);
+
+// One launch of the short causal convolution (update, or commit only).
+struct ConvArgs {
+  const void* x;               // [B][T][D] io dtype (commit only: the tokens to commit)
+  const float* w;              // [K][D] taps
+  const float* bias;           // [D] or nullptr
+  void* pool;                  // [P][K-1][D] io dtype
+  const int32_t* idx;          // [B]
+  const void* prev_x;          // [B][T_prev][D] or nullptr (commit only: = x)
+  const int32_t* prev_len;     // [B] tokens of prev_x to commit (nullptr: none)
+  void* y;                     // [B][T][D] io dtype (unused for commit only)
+  int32_t B, T, D, K, P, T_prev;
+  int32_t write_back;          // 1: store the state advanced over all T tokens
+  int32_t activation;          // 0: identity, 1: SiLU
+};
+
+// commit_only: advance each valid slot over prev_len tokens of prev_x and stop.
+hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t stream);
 
 constexpr int kCommitChunksPerThread = 4;
 constexpr int kThreads = 256;

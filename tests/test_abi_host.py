@@ -171,6 +171,53 @@ def test_commit_replay_validation(L):
     assert cr(dims(d_k=48)) == 5
 
 
+def cdims(**kw):
+    base = dict(batch=4, T=4, channels=2048, width=4, pool_slots=8, dtype=gdn.GDN_DTYPE_BF16, activation=1)
+    base.update(kw)
+    return gdn.GdnConvDims(**base)
+
+
+def test_conv_update_validation(L):
+    def cu(d, x=A16, w=A16 * 2, b=A16 * 3, pool=A16 * 4, idx=A16 * 5, px=None, T_prev=0, plen=None,
+           y=A16 * 6, wb=0):
+        return L.gdn_conv_update(ctypes.byref(d), x, w, b, pool, idx, px, T_prev, plen, y, wb, None)
+    assert cu(cdims(batch=0)) == 0
+    assert cu(cdims(batch=0), x=None, y=None) == 0
+    assert L.gdn_conv_update(None, A16, A16, A16, A16, A16, None, 0, None, A16, 0, None) == 1
+    assert cu(cdims(batch=-1)) == 2
+    assert cu(cdims(T=0)) == 2
+    assert cu(cdims(width=1)) == 2
+    assert cu(cdims(batch=0), px=A16 * 7, T_prev=0, plen=A16 * 8) == 2    # prev_x needs 1 <= T_prev
+    assert cu(cdims(dtype=7)) == 3
+    assert cu(cdims(activation=2)) == 5
+    assert cu(cdims(channels=2044)) == 5                                  # not a multiple of 8 bf16
+    assert cu(cdims(width=gdn.GDN_CONV_MAX_WIDTH + 1)) == 5
+    assert cu(cdims(T=gdn.GDN_MAX_T + 1)) == 5
+    assert cu(cdims(batch=65536, pool_slots=70000)) == 5
+    assert cu(cdims(), x=None) == 1
+    assert cu(cdims(), w=None) == 1
+    assert cu(cdims(), y=None) == 1
+    assert cu(cdims(), px=A16 * 7, T_prev=4, plen=None) == 1
+    assert cu(cdims(), x=A16 + 8) == 4
+    assert cu(cdims(), b=A16 * 3 + 4) == 4
+    assert cu(cdims(), pool=A16 * 4 + 2) == 4
+    assert cu(cdims(), px=A16 * 7 + 8, T_prev=4, plen=A16 * 8) == 4
+    assert cu(cdims(), px=A16 * 7, T_prev=4, plen=A16 * 8 + 2) == 4
+
+
+def test_conv_commit_validation(L):
+    def cc(d, x=A16, pool=A16 * 4, idx=A16 * 5, acc=A16 * 6):
+        return L.gdn_conv_commit(ctypes.byref(d), x, pool, idx, acc, None)
+    assert cc(cdims(batch=0)) == 0
+    assert cc(cdims(batch=0), acc=None) == 0
+    assert cc(cdims(T=0)) == 2
+    assert cc(cdims(), acc=None) == 1
+    assert cc(cdims(), x=None) == 1
+    assert cc(cdims(), x=A16 + 4) == 4
+    assert cc(cdims(), acc=A16 * 6 + 1) == 4
+    assert cc(cdims(width=9)) == 5
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1, 16)
