@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published figure
 INFINITY_CACHE_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "csrc", "gdn_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "csrc", f)
+               for f in ("gdn_kernels.hip", "gdn_device.h")]
 
 
 def log(*a):
@@ -38,14 +39,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source without comments and blank lines: a comment edit
-    does not invalidate counter figures taken on the same code."""
+    """Hash of the recurrent kernel's sources without comments and blank lines: a
+    comment edit does not invalidate counter figures taken on the same code."""
     code = []
-    with open(KERNEL_SRC) as fh:
-        for line in fh:
-            line = line.split("//", 1)[0].strip()
-            if line:
-                code.append(line)
+    for path in KERNEL_SRCS:
+        with open(path) as fh:
+            for line in fh:
+                line = line.split("//", 1)[0].strip()
+                if line:
+                    code.append(line)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
