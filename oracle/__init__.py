@@ -77,6 +77,8 @@ def lib():
         L.oracle_commit_replay.argtypes = ([ctypes.POINTER(Dims), _D, _D, _D, _I] + [_D] * 4 +
                                            [ctypes.c_int32, _I, ctypes.c_int32])
         L.oracle_commit_replay.restype = ctypes.c_int32
+        L.oracle_gated_norm.argtypes = [ctypes.c_int64, ctypes.c_int32, _D, _D, _D, ctypes.c_double, _D]
+        L.oracle_gated_norm.restype = None
         CD = ctypes.POINTER(ConvDims)
         L.oracle_conv_update.argtypes = [CD, _D, _D, _D, _D, _I, _D, ctypes.c_int32, _I, _D, ctypes.c_int32]
         L.oracle_conv_update.restype = ctypes.c_int32
@@ -212,6 +214,16 @@ def commit_replay(dims: Dims, A_log, dt_bias, pool, idx, rk, rv, ra, rb, rlen, *
     if rc:
         raise ValueError("oracle_commit_replay: invalid dimensions")
     return pool
+
+
+def gated_norm(o, z, weight, eps: float = 1e-6) -> np.ndarray:
+    """y = weight * o / sqrt(mean(o^2) + eps) * silu(z) over the last axis (d_v)."""
+    o, z, w = _f64(o), _f64(z), _f64(weight)
+    if z.shape != o.shape or w.shape != (o.shape[-1],):
+        raise ValueError("gated_norm: z must match o and weight must be [d_v]")
+    y = np.empty_like(o)
+    lib().oracle_gated_norm(int(o.size // o.shape[-1]), int(o.shape[-1]), _p(o), _p(z), _p(w), float(eps), _p(y))
+    return y
 
 
 def make_conv_dims(batch, T, channels, width, pool, activation="silu") -> ConvDims:

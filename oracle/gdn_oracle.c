@@ -372,3 +372,24 @@ int32_t oracle_commit_replay(const oracle_dims* d, const double* A_log, const do
   }
   return 0;
 }
+
+/* Gated RMS normalisation of the output, per (row, token, v-head) over its d_v values:
+ *     y[j] = weight[j] * o[j] / sqrt(mean_j o[j]^2 + eps) * silu(z[j]),
+ *     silu(z) = z / (1 + e^-z).
+ * TensorRT-LLM PR 20937, Per-File QA Perspective: the decode-rows GDN kernel carries a
+ * gated norm; the dense-FP8 notes name a token-major gated RMS norm. The pages do not
+ * print it; this is the standard form (normalise, scale, then gate), with one weight
+ * vector over d_v shared by the heads. o, z, y: [n][dv] (n = B*T*Hv vectors). */
+void oracle_gated_norm(int64_t n, int32_t dv, const double* o, const double* z, const double* weight,
+                       double eps, double* y) {
+  for (int64_t v = 0; v < n; ++v) {
+    const double* ov = o + v * dv;
+    double ss = 0.0;
+    for (int j = 0; j < dv; ++j) ss += ov[j] * ov[j];
+    const double inv = 1.0 / sqrt(ss / dv + eps);
+    for (int j = 0; j < dv; ++j) {
+      const double zj = z[v * dv + j];
+      y[v * dv + j] = weight[j] * ov[j] * inv * (zj / (1.0 + exp(-zj)));
+    }
+  }
+}

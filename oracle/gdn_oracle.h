@@ -70,6 +70,11 @@ int32_t oracle_commit_replay(const oracle_dims* d, const double* A_log, const do
                              const double* rk, const double* rv, const double* ra, const double* rb,
                              int32_t rT, const int32_t* rlen, int32_t nthreads);
 
+/* Gated RMS normalisation of n output vectors of length dv:
+ * y[j] = weight[j] * o[j] / sqrt(mean(o^2) + eps) * silu(z[j]). */
+void oracle_gated_norm(int64_t n, int32_t dv, const double* o, const double* z, const double* weight,
+                       double eps, double* y);
+
 #ifdef __cplusplus
 }
 #endif
