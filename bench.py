@@ -236,10 +236,11 @@ def main():
     ap.add_argument("--steps", type=int, default=8000)
     ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--workload", type=int, default=None, help="workload index (default: the MTP verify T=4 one)")
-    ap.add_argument("--mode", choices=("intermediate", "replay", "conv"), default="intermediate",
+    ap.add_argument("--mode", choices=("intermediate", "gated", "replay", "conv"), default="intermediate",
                     help="intermediate: verify storing every intermediate state, then commit (the "
                          "workload as defined); replay: cached-replay verify with in-kernel commit of the "
-                         "previous step's accepted prefix (one launch per step, no per-token states); conv: "
+                         "previous step's accepted prefix (one launch per step, no per-token states); gated: "
+                         "intermediate with the gated RMS-norm output epilogue fused into verify; conv: "
                          "the short causal convolution next to the GDN state (--workload indexes the "
                          "convolution workloads)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
@@ -270,6 +271,7 @@ def main():
     x = workloads.make_inputs(w, seed=0)
     idx = x["idx"].numpy()
     replay = args.mode == "replay"
+    gated = args.mode == "gated"
     if replay:
         if w.mode == "decode":
             sys.exit("bench.py: replay mode needs a verify workload")
@@ -281,6 +283,10 @@ def main():
     else:
         v_bytes = workloads.algorithmic_bytes(w, idx, "verify")
         c_bytes = workloads.algorithmic_bytes(w, idx, "commit") if w.commit else 0
+    if gated:  # z of valid rows and the norm weights are read as well
+        xg = workloads.make_gate_inputs(w, seed=3)
+        nvalid = int(((idx >= 0) & (idx < w.pool)).sum())
+        v_bytes += nvalid * w.T * w.Hv * w.dv * xg["z"].element_size() + w.dv * 4
 
     # Rotating buffer sets, so that every launch reads its state from HBM: the pool
     # reads of all sets together exceed the 256 MB Infinity Cache four times over
@@ -294,6 +300,9 @@ def main():
     R = min(R, 1024, max(2, int(16e9 // set_bytes)))   # tiny workloads: latency-bound anyway
     shared = {n: x[n].to(dev) for n in ("idx", "accept", "prev_accept") if n in x}
     base = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    if gated:
+        shared["norm_weight"] = xg["norm_weight"].to(dev)
+        base["z"] = xg["z"].to(dev)
     if replay:
         shared["rlen"] = torch.from_numpy(rlen).to(dev)
         base.update({"r" + n: xp[n].to(dev) for n in ("k", "v", "a", "b")})
@@ -319,6 +328,10 @@ def main():
             gdn.gdn_verify_replay(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"],
                                   s["pool"], s["idx"], s["rk"], s["rv"], s["ra"], s["rb"], s["rlen"], True,
                                   scale=w.scale)
+        elif gated:
+            gdn.gdn_verify_gated(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["z"],
+                                 s["norm_weight"], s["o"], s["pool"], s["idx"], s["cache"],
+                                 w.write_final or w.mode == "decode", s.get("prev_accept"), scale=w.scale)
         elif w.mode == "decode":
             gdn.gdn_decode(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"], s["pool"],
                            s["idx"], scale=w.scale)
@@ -386,18 +399,21 @@ def main():
                    "d_k": w.dk, "d_v": w.dv, "pool_slots": w.pool, "state_dtype": w.state_dtype,
                    "io_dtype": w.io_dtype,
                    "step": ("cached-replay verify with in-kernel commit (accept lengths U{1..T})" if replay else
-                            ("verify" if w.mode != "decode" else "decode") + (" + commit" if w.commit else "")),
+                            ("verify" if w.mode != "decode" else "decode") + (" with gated-norm output" if gated else "")
+                            + (" + commit" if w.commit else "")),
                    "rotating_buffer_sets": R,
                    "launch": "eager" if args.eager else "hip_graph", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None if replay else traffic_from_profiles(w.name),
-                     "kernel": ("gdn_verify_replay" if replay else "gdn_verify") + " (recurrent_kernel)",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None if (replay or gated) else traffic_from_profiles(w.name),
+                     "kernel": ("gdn_verify_replay" if replay else "gdn_verify_gated" if gated else "gdn_verify")
+                     + " (recurrent_kernel)",
                      "algorithmic_bytes_per_launch": v_bytes,
                      "avg_launch_us": us_ver},
         "verify_tokens_per_s": tokens / (us_ver * 1e-6),
         "copy_ceiling_GBps": copy_gbps,
     }
-    if not args.no_cpu and not replay:
+    if not args.no_cpu and not replay and not gated:
         log("[bench] CPU oracle baseline ...")
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
         log(f"[bench] CPU oracle: {res['cpu_baseline']['value']:.1f} tokens/s on {res['cpu_baseline']['cores']} threads")

@@ -139,6 +139,27 @@ GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int
                       const int32_t* state_indices, const int32_t* accept_len,
                       void* state_pool, void* stream);
 
+/* The gated RMS normalisation of the output, fused into verify or decode [P3] (Per-File QA
+ * Perspective: the decode-rows GDN kernel carries a gated norm; the dense-FP8 notes name
+ * a token-major gated RMS norm). The pages do not print it; this is the standard form,
+ * per (row, token, v-head) vector of d_v outputs o:
+ *     y[j] = weight[j] * o[j] / sqrt(mean_j o[j]^2 + eps) * silu(z[j]),
+ *     silu(x) = x / (1 + e^-x),  one weight vector over d_v shared by the heads. */
+typedef struct {
+  const void* z;        /* [B][T][Hv][d_v] io dtype, 16-byte aligned: the gate input */
+  const float* weight;  /* [d_v] fp32, 16-byte aligned */
+  float eps;            /* >= 0 */
+} gdn_out_gate;
+
+/* gdn_verify whose io->o receives y (above) instead of o; everything else (cache, write-
+ * back, fused commit, padding rows with y = 0) is as in gdn_verify. T = 1 with
+ * write_final = 1 and no cache is the gated decode. One workgroup then holds a head's
+ * whole d_v: d_v <= 128 is required for d_k >= 128 (GDN_ERR_UNSUPPORTED otherwise). */
+GDN_API gdn_status gdn_verify_gated(const gdn_dims* dims, const gdn_io* io, const gdn_out_gate* gate,
+                                    void* state_pool, const int32_t* state_indices, void* inter_cache,
+                                    int32_t cache_T, int32_t write_final, const int32_t* prev_accept_len,
+                                    void* stream);
+
 /* Per-token inputs of an earlier verify, kept by the caller for cached replay: the k,
  * v, a, b arrays that verify consumed (typically the previous step's io buffers, used
  * alternately with the current ones). io dtype, 16-byte aligned k and v. */

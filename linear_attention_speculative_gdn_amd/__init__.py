@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
-EXPORTED = ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
             "gdn_conv_update", "gdn_conv_commit", "gdn_status_string", "gdn_abi_version")
 GDN_CONV_MAX_WIDTH = 8
 GDN_MAX_T = 16
@@ -46,6 +46,10 @@ class GdnIo(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
                 ("dt_bias", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+class GdnOutGate(ctypes.Structure):
+    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 class GdnTokens(ctypes.Structure):
@@ -75,13 +79,14 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode.argtypes = [D, I, vp, vp, vp]
         L.gdn_verify.argtypes = [D, I, vp, vp, vp, i32, i32, vp, vp]
         L.gdn_commit.argtypes = [D, vp, i32, vp, vp, vp, vp]
+        L.gdn_verify_gated.argtypes = [D, I, ctypes.POINTER(GdnOutGate), vp, vp, vp, i32, i32, vp, vp]
         TK = ctypes.POINTER(GdnTokens)
         L.gdn_verify_replay.argtypes = [D, I, vp, vp, TK, vp, i32, vp]
         L.gdn_commit_replay.argtypes = [D, vp, vp, vp, vp, TK, vp, vp]
         CD = ctypes.POINTER(GdnConvDims)
         L.gdn_conv_update.argtypes = [CD, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp]
         L.gdn_conv_commit.argtypes = [CD, vp, vp, vp, vp, vp]
-        for f in ("gdn_decode", "gdn_verify", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
                   "gdn_conv_update", "gdn_conv_commit"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -171,27 +176,52 @@ def gdn_decode(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, *, s
     _raise(st, "gdn_decode")
 
 
-def gdn_verify(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, inter_cache=None,
-               write_final=False, prev_accept_len=None, *, scale=None, l2norm_eps=1e-6, stream=None) -> None:
-    """T tokens per row from its pool slot; see include/gdn.h for the cache, write_final
-    and fused-commit (prev_accept_len) semantics."""
-    dims, io = _dims_io(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, scale, l2norm_eps)
+def _cache_prev(dims, state_pool, inter_cache, prev_accept_len, device) -> int:
     cache_T = 0
     if inter_cache is not None:
-        _need(inter_cache, "inter_cache", 5, q.device)
+        _need(inter_cache, "inter_cache", 5, device)
         if inter_cache.shape[0] != dims.batch or inter_cache.shape[2:] != state_pool.shape[1:]:
             raise ValueError("inter_cache must be [B, cache_T, Hv, dv, dk]")
         if inter_cache.dtype != state_pool.dtype:
             raise TypeError("inter_cache must have the state dtype")
         cache_T = inter_cache.shape[1]
     if prev_accept_len is not None:
-        _need(prev_accept_len, "prev_accept_len", 1, q.device)
+        _need(prev_accept_len, "prev_accept_len", 1, device)
         if prev_accept_len.shape != (dims.batch,) or prev_accept_len.dtype != torch.int32:
             raise ValueError("prev_accept_len must be int32 [B]")
+    return cache_T
+
+
+def gdn_verify(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, inter_cache=None,
+               write_final=False, prev_accept_len=None, *, scale=None, l2norm_eps=1e-6, stream=None) -> None:
+    """T tokens per row from its pool slot; see include/gdn.h for the cache, write_final
+    and fused-commit (prev_accept_len) semantics."""
+    dims, io = _dims_io(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, scale, l2norm_eps)
+    cache_T = _cache_prev(dims, state_pool, inter_cache, prev_accept_len, q.device)
     st = lib().gdn_verify(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
                           _ptr(inter_cache), cache_T, int(bool(write_final)), _ptr(prev_accept_len),
                           _stream(q.device, stream))
     _raise(st, "gdn_verify")
+
+
+def gdn_verify_gated(q, k, v, a, b, A_log, dt_bias, z, norm_weight, y, state_pool, state_indices,
+                     inter_cache=None, write_final=False, prev_accept_len=None, *, norm_eps=1e-6, scale=None,
+                     l2norm_eps=1e-6, stream=None) -> None:
+    """gdn_verify whose output y [B,T,Hv,dv] is the gated RMS normalisation
+    norm_weight * o / sqrt(mean(o^2) + norm_eps) * silu(z) of each (row, token, v-head)
+    vector, z [B,T,Hv,dv] in the io dtype, norm_weight [dv] fp32."""
+    dims, io = _dims_io(q, k, v, a, b, A_log, dt_bias, y, state_pool, state_indices, scale, l2norm_eps)
+    _need(z, "z", 4, q.device); _need(norm_weight, "norm_weight", 1, q.device)
+    if z.shape != v.shape or z.dtype != v.dtype:
+        raise ValueError("z must match v in shape and dtype")
+    if norm_weight.shape != (dims.d_v,) or norm_weight.dtype != torch.float32:
+        raise ValueError("norm_weight must be float32 [dv]")
+    cache_T = _cache_prev(dims, state_pool, inter_cache, prev_accept_len, q.device)
+    gate = GdnOutGate(z.data_ptr(), norm_weight.data_ptr(), float(norm_eps))
+    st = lib().gdn_verify_gated(ctypes.byref(dims), ctypes.byref(io), ctypes.byref(gate), _ptr(state_pool),
+                                _ptr(state_indices), _ptr(inter_cache), cache_T, int(bool(write_final)),
+                                _ptr(prev_accept_len), _stream(q.device, stream))
+    _raise(st, "gdn_verify_gated")
 
 
 def gdn_commit(inter_cache, state_indices, accept_len, state_pool, *, stream=None) -> None:

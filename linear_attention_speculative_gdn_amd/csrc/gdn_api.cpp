@@ -50,8 +50,14 @@ int pick_shape(const gdn_dims* d) {
 
 gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const int32_t* idx,
                          void* cache, int32_t cache_T, int32_t write_final,
-                         const int32_t* prev_accept, void* stream) {
+                         const int32_t* prev_accept, void* stream, const gdn_out_gate* gate = nullptr) {
+  if (gate) {
+    if (!(gate->eps >= 0.f)) return GDN_ERR_SHAPE;
+    if (d->d_k >= 128 && d->d_v > 128) return GDN_ERR_UNSUPPORTED;  // one workgroup holds a head's d_v
+  }
   if (d->batch == 0) return GDN_OK;
+  if (gate && (!gate->z || !gate->weight)) return GDN_ERR_NULL;
+  if (gate && (!aligned(gate->z, 16) || !aligned(gate->weight, 16))) return GDN_ERR_ALIGN;
   if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
       !pool || !idx)
     return GDN_ERR_NULL;
@@ -77,8 +83,11 @@ gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const 
   p.rlen = nullptr;
   p.rT = 0;
   p.rcommit = 0;
+  p.z = gate ? gate->z : nullptr;
+  p.gw = gate ? gate->weight : nullptr;
+  p.geps = gate ? gate->eps : 0.f;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(d->state_dtype), static_cast<Dt>(d->io_dtype),
-                                             pick_shape(d), 0, p, static_cast<hipStream_t>(stream));
+                                             pick_shape(d), gate ? 3 : 0, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -141,6 +150,16 @@ gdn_status gdn_verify(const gdn_dims* dims, const gdn_io* io, void* state_pool,
                        prev_accept_len, stream);
 }
 
+gdn_status gdn_verify_gated(const gdn_dims* dims, const gdn_io* io, const gdn_out_gate* gate, void* state_pool,
+                            const int32_t* state_indices, void* inter_cache, int32_t cache_T, int32_t write_final,
+                            const int32_t* prev_accept_len, void* stream) {
+  const gdn_status s = check_dims(dims, true);
+  if (s != GDN_OK) return s;
+  if (!gate) return GDN_ERR_NULL;
+  return run_recurrent(dims, io, state_pool, state_indices, inter_cache, cache_T, write_final,
+                       prev_accept_len, stream, gate);
+}
+
 gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cache_T,
                       const int32_t* state_indices, const int32_t* accept_len, void* state_pool,
                       void* stream) {
@@ -189,6 +208,7 @@ gdn_status gdn_verify_replay(const gdn_dims* dims, const gdn_io* io, void* state
   p.write_final = 0;
   p.scale = dims->scale; p.eps = dims->l2norm_eps;
   set_replay(p, replay, replay_len, commit);
+  p.z = nullptr; p.gw = nullptr; p.geps = 0.f;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
                                              1, 1, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
@@ -216,6 +236,7 @@ gdn_status gdn_commit_replay(const gdn_dims* dims, const float* A_log, const flo
   p.write_final = 0;
   p.scale = dims->scale; p.eps = dims->l2norm_eps;
   set_replay(p, replay, replay_len, 1);
+  p.z = nullptr; p.gw = nullptr; p.geps = 0.f;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
                                              1, 2, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;

@@ -36,6 +36,10 @@ struct RecurrentArgs {
   const int32_t* rlen;         // [B] tokens to replay per row
   int32_t rT;                  // tokens per row in the replay arrays (>= 1)
   int32_t rcommit;             // 1: write the replayed state to the slot
+  // gated-norm output epilogue (mode 3)
+  const void* z;               // [B][T][Hv][DV] io dtype
+  const float* gw;             // [DV] norm weights
+  float geps;                  // RMS epsilon
 };
 
 // One launch of the accepted-prefix commit copy.
@@ -51,7 +55,9 @@ struct CommitArgs {
 
 // shape: 1 = one value row per lane, 4 waves; 2 = two rows per lane, 4 waves;
 // 12 = one row per lane, 2 waves; 14 = one row per lane, 8 waves (d_k = 128 only).
-// mode: 0 decode / verify, 1 cached-replay verify, 2 replay commit (shape 1 only).
+// mode: 0 decode / verify, 1 cached-replay verify, 2 replay commit, 3 decode / verify
+// with the gated-norm output epilogue (modes 1-3 use their own fixed shapes).
+// Mode 3 needs d_v <= 256 for d_k <= 64 and d_v <= 128 for d_k >= 128.
 hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, const RecurrentArgs& p,
                             hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream);

@@ -126,10 +126,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Replayed and new tokens go through the same per-token code, in one sequence (the
 // replayed ones first), so a replay reproduces the states a verify computed bit for bit.
 //
+// GATE (MODE 0 only, one workgroup per (row, v-head): RPW >= DV): the outputs are not
+// stored as o but as the gated RMS normalisation y = w * o / sqrt(mean_j o^2 + eps) *
+// silu(z) of each (row, token, v-head) vector. The outputs of all tokens collect in LDS;
+// after the token loop one wave per token sums the squares, and every thread writes its
+// 16-byte slice of y.
+//
 // Every global load is unconditional, from an address clamped into its buffer, and
 // out-of-range lanes discard the value afterwards: a load inside a branch would be
 // waited on at the end of the branch, which serialises the memory round trips.
-template <typename ST, typename IT, int DK, int R, int NW, int MODE>
+template <typename ST, typename IT, int DK, int R, int NW, int MODE, bool GATE = false>
 __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs p) {
   constexpr bool NEW = MODE != 2;        // this call has its own tokens (and outputs)
   constexpr bool REPLAY = MODE != 0;
@@ -155,6 +161,8 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
   float* s_beta = s_g + TMAX;       // [TMAX] write strength
   float* s_kq = s_beta + TMAX;      // [TMAX] k^.q^
   float* s_o = s_kq + TMAX;         // [NW][R*RW] outputs of one token, per wave
+  float* s_og = s_o + NW * R * RW;  // GATE: [T][RPW] outputs of all tokens
+  float* s_rs = s_og + T * RPW;     // GATE: [T] 1 / rms of each token's outputs
 
   // grid (v-block, v-head, row): no integer division on the way to the first loads.
   // Workgroups are dealt to the 8 XCDs round-robin by linear id, so the v-blocks of
@@ -217,6 +225,21 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
     const int tg = min(tid, T - 1);
     a_in = ld_io(ap + size_t(row * T + tg) * p.Hv + h);
     b_in = ld_io(bp + size_t(row * T + tg) * p.Hv + h);
+  }
+  // GATE: the gate input z (laid out like v) and the norm weights of the same vectors
+  u32x4 zraw[GATE ? NV : 1];
+  f32x4 gwr[GATE ? NV : 1][VE / 4];
+  if constexpr (GATE) {
+    const IT* zp = static_cast<const IT*>(p.z);
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = min(tid + it * NT, nv - 1);
+      const int t = e / VVEC, c = e - t * VVEC;
+      const int j = min(c * VE, DV - VE);
+      zraw[it] = *reinterpret_cast<const u32x4*>(zp + (size_t(row * T + t) * p.Hv + h) * DV + j);
+#pragma unroll
+      for (int u = 0; u < VE / 4; ++u) gwr[it][u] = *reinterpret_cast<const f32x4*>(p.gw + j + 4 * u);
+    }
   }
   // keep the loads above issued before the wait on the slot index (they must not
   // be sunk into the non-padding branch)
@@ -473,10 +496,16 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
           for (int c = 0; c < NCH; ++c)
             st_nt(pool_tile + size_t(jrow[r]) * DK + (l + c * L) * CE, packed[c]);
         }
-        if (NEW && l == 0) s_o[wave * (R * RW) + r * RW + grp] = ov;
+        if (NEW && l == 0) {
+          if constexpr (GATE) {
+            if (t >= 0) s_og[t * RPW + (wave * R + r) * RW + grp] = ov;
+          } else {
+            s_o[wave * (R * RW) + r * RW + grp] = ov;
+          }
+        }
       }
     }
-    if constexpr (NEW) {
+    if constexpr (NEW && !GATE) {
       if (t >= 0) {
         // o of this wave's R*RW consecutive value rows, as whole 16-byte vectors. The
         // strip in LDS is private to the wave, and a wave's LDS accesses complete in
@@ -497,7 +526,46 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
     }
   }
 
-  // ---- 8. final state back to the slot
+  // ---- 8. GATE: y = w * o / sqrt(mean o^2 + eps) * silu(z) for every token
+  if constexpr (GATE) {
+    __syncthreads();
+    constexpr int PV = (RPW + 63) / 64;
+    for (int t = wave; t < T; t += NW) {
+      float ss = 0.f;
+#pragma unroll
+      for (int u = 0; u < PV; ++u) {
+        const int j = lane + u * 64;
+        const float x = (j < DV) ? s_og[t * RPW + j] : 0.f;
+        ss = fmaf(x, x, ss);
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) s_rs[t] = 1.f / sqrtf(ss / float(DV) + p.geps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e = tid + it * NT;
+      const int t = e / VVEC, c = e - t * VVEC;
+      if (e < nv && c * VE < DV) {
+        float zf[VE], y[VE];
+        unpack_io(zraw[it], zf, op);
+        const float rs = s_rs[t];
+#pragma unroll
+        for (int u = 0; u < VE / 4; ++u) {
+          const float wv[4] = {gwr[it][u].x, gwr[it][u].y, gwr[it][u].z, gwr[it][u].w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int mm = 4 * u + m;
+            const float zz = zf[mm];
+            y[mm] = (s_og[t * RPW + c * VE + mm] * rs) * wv[m] * (zz / (1.f + expf(-zz)));
+          }
+        }
+        *reinterpret_cast<u32x4*>(op + (size_t(row * T + t) * p.Hv + h) * DV + c * VE) = pack_io(y, op);
+      }
+    }
+  }
+
+  // ---- 9. final state back to the slot
   if (MODE == 0 && p.write_final) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -533,14 +601,16 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
   }
 }
 
-template <typename ST, typename IT, int DK, int R, int NW = 4, int MODE = 0>
+template <typename ST, typename IT, int DK, int R, int NW = 4, int MODE = 0, bool GATE = false>
 hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
   constexpr int RPW = NW * R * (64 / (DK / 16));
   const int nvb = (p.DV + RPW - 1) / RPW;
+  if (GATE && nvb != 1) return hipErrorInvalidValue;  // the norm needs a head's d_v in one workgroup
   const dim3 grid(unsigned(nvb), unsigned(p.Hv), unsigned(p.B));
   const size_t tmax = size_t(MODE == 2 ? 0 : p.T) + size_t(MODE == 0 ? 0 : p.rT);
-  const size_t lds = sizeof(float) * (2 * tmax * DK + tmax * RPW + 3 * tmax + RPW);
-  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW, MODE>), grid, dim3(NW * 64), lds, stream, p);
+  const size_t lds = sizeof(float) * (2 * tmax * DK + tmax * RPW + 3 * tmax + RPW +
+                                      (GATE ? size_t(p.T) * (RPW + 1) : 0));
+  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW, MODE, GATE>), grid, dim3(NW * 64), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -557,6 +627,16 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
       case 64: return launch_rec<ST, IT, 64, 1, 4, 1>(p, stream);
       case 128: return launch_rec<ST, IT, 128, 2, 8, 1>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 1, 4, 1>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (mode == 3) {  // verify with the gated-norm epilogue: one workgroup covers d_v
+    switch (p.DK) {
+      case 16: return launch_rec<ST, IT, 16, 1, 4, 0, true>(p, stream);    // 256 value rows
+      case 32: return launch_rec<ST, IT, 32, 1, 8, 0, true>(p, stream);    // 256
+      case 64: return launch_rec<ST, IT, 64, 2, 8, 0, true>(p, stream);    // 256
+      case 128: return launch_rec<ST, IT, 128, 2, 8, 0, true>(p, stream);  // 128
+      case 256: return launch_rec<ST, IT, 256, 4, 8, 0, true>(p, stream);  // 128
       default: return hipErrorInvalidValue;
     }
   }

@@ -309,3 +309,13 @@ def conv_bytes(w: ConvWorkload, idx: np.ndarray, prev_len: np.ndarray | None = N
         n = np.where(valid & (prev_len >= 1) & (prev_len <= T), prev_len, 0)
         total += int(np.sum(n >= 1)) * H * D * esz + int(np.minimum(n, H).sum()) * D * esz + B * 4
     return total
+
+
+def make_gate_inputs(w: Workload, seed: int = 0) -> dict:
+    """Inputs of the gated RMS normalisation of the output: the gate z ~ N(0,1) shaped like
+    v (io dtype) and the norm weight ~ U[0.5, 1.5) over d_v (fp32), from their own
+    ``numpy.random.default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((w.batch, w.T, w.Hv, w.dv))
+    weight = rng.uniform(0.5, 1.5, w.dv)
+    return dict(z=_store(z, w.io_dtype), norm_weight=torch.from_numpy(weight.astype(np.float32)))
