@@ -131,6 +131,23 @@ def test_commit_validation(L):
     assert com(dims(batch=0, d_v=8)) == 5
 
 
+def test_verify_gated_validation(L):
+    def vg(d, gate="ok", i=None, pool=A16 * 9, idx=A16 * 10, cache=None, cache_T=0):
+        i = io() if i is None else i
+        g = gdn.GdnOutGate(A16 * 20, A16 * 21, 1e-6) if gate == "ok" else gate
+        return L.gdn_verify_gated(ctypes.byref(d), ctypes.byref(i), ctypes.byref(g) if g is not None else None,
+                                  pool, idx, cache, cache_T, 0, None, None)
+    assert vg(dims(batch=0)) == 0
+    assert vg(dims(), gate=None) == 1
+    assert vg(dims(), gate=gdn.GdnOutGate(None, A16 * 21, 1e-6)) == 1
+    assert vg(dims(), gate=gdn.GdnOutGate(A16 * 20, None, 1e-6)) == 1
+    assert vg(dims(batch=0), gate=gdn.GdnOutGate(A16 * 20, A16 * 21, -1.0)) == 2
+    assert vg(dims(), gate=gdn.GdnOutGate(A16 * 20 + 8, A16 * 21, 1e-6)) == 4
+    assert vg(dims(), gate=gdn.GdnOutGate(A16 * 20, A16 * 21 + 4, 1e-6)) == 4
+    assert vg(dims(batch=0, d_k=128, d_v=256)) == 5        # a head's d_v must fit one workgroup
+    assert vg(dims(), i=io(q=None)) == 1
+
+
 def tokens(**kw):
     base = dict(k=A16 * 13, v=A16 * 14, a=A16 * 15, b=A16 * 16, T_src=4)
     base.update(kw)
