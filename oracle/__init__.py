@@ -77,6 +77,8 @@ def lib():
         L.oracle_commit_replay.argtypes = ([ctypes.POINTER(Dims), _D, _D, _D, _I] + [_D] * 4 +
                                            [ctypes.c_int32, _I, ctypes.c_int32])
         L.oracle_commit_replay.restype = ctypes.c_int32
+        L.oracle_prefill.argtypes = [ctypes.POINTER(Dims), _I] + [_D] * 7 + [_D, _I, _I, _D, ctypes.c_int32]
+        L.oracle_prefill.restype = ctypes.c_int32
         L.oracle_gated_norm.argtypes = [ctypes.c_int64, ctypes.c_int32, _D, _D, _D, ctypes.c_double, _D]
         L.oracle_gated_norm.restype = None
         CD = ctypes.POINTER(ConvDims)
@@ -214,6 +216,25 @@ def commit_replay(dims: Dims, A_log, dt_bias, pool, idx, rk, rv, ra, rb, rlen, *
     if rc:
         raise ValueError("oracle_commit_replay: invalid dimensions")
     return pool
+
+
+def prefill(dims: Dims, cu_seqlens, q, k, v, a, b, A_log, dt_bias, pool, idx, fresh=None, *,
+            nthreads: int | None = None) -> dict:
+    """Prefill of variable-length sequences packed along the first axis (q, k [N,Hk,dk],
+    v [N,Hv,dv], a, b [N,Hv]; cu_seqlens [B+1]) from pooled initial states (zero where
+    fresh[r] != 0). Returns dict(o [N,Hv,dv], pool)."""
+    q, k, v, a, b = map(_f64, (q, k, v, a, b))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    pool = _f64(pool).copy()
+    cu = _i32(cu_seqlens)
+    N = int(cu[-1])
+    o = np.zeros((N, dims.num_v_heads, dims.d_v), dtype=np.float64)
+    fr = None if fresh is None else _i32(fresh)
+    rc = lib().oracle_prefill(ctypes.byref(dims), _p(cu, _I), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log),
+                              _p(dt_bias), _p(pool), _p(_i32(idx), _I), _p(fr, _I), _p(o), _nthreads(nthreads))
+    if rc:
+        raise ValueError("oracle_prefill: invalid dimensions")
+    return dict(o=o, pool=pool)
 
 
 def gated_norm(o, z, weight, eps: float = 1e-6) -> np.ndarray:

@@ -393,3 +393,58 @@ void oracle_gated_norm(int64_t n, int32_t dv, const double* o, const double* z, 
     }
   }
 }
+
+/* Prefill of variable-length sequences with pooled initial states.
+ * TensorRT-LLM PR 20937, Per-File QA Perspective: the chunked gated-delta-rule prefill
+ * takes a bf16 state and an initial-state mask that zeroes fresh states. The pages do not
+ * print the chunked form; the oracle follows the definition token by token:
+ * for sequence r (tokens cu_seqlens[r] .. cu_seqlens[r+1]-1, packed along the first axis
+ * of q, k, v, a, b, o) and v-head h, S starts at pool[idx[r]] (zero when fresh[r] != 0),
+ * every token runs through the update above with no rounding between tokens, o is
+ * written for every token, and the final state is stored back to the slot (rounded to
+ * bf16 once, for a bf16 pool). A row whose slot is outside [0, P) gets o = 0 and no
+ * state access. */
+int32_t oracle_prefill(const oracle_dims* d, const int32_t* cu_seqlens, const double* q, const double* k,
+                       const double* v, const double* a, const double* b, const double* A_log,
+                       const double* dt_bias, double* pool, const int32_t* idx, const int32_t* fresh,
+                       double* o, int32_t nthreads) {
+  if (!d || d->batch < 0 || d->num_k_heads < 1 || d->num_v_heads % d->num_k_heads != 0 || d->d_k < 1 ||
+      d->d_v < 1)
+    return -1;
+  const int B = d->batch, Hk = d->num_k_heads, Hv = d->num_v_heads, dk = d->d_k, dv = d->d_v, G = Hv / Hk;
+  const size_t tile = (size_t)dk * dv;
+  for (int r = 0; r < B; ++r)
+    if (cu_seqlens[r + 1] < cu_seqlens[r]) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double* qh = (double*)malloc((size_t)dk * sizeof(double));
+    double* kh = (double*)malloc((size_t)dk * sizeof(double));
+    double* u = (double*)malloc((size_t)dv * sizeof(double));
+    double* S = (double*)malloc(tile * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic)
+#endif
+    for (int64_t th = 0; th < (int64_t)B * Hv; ++th) {
+      const int r = (int)(th / Hv), h = (int)(th % Hv), kh_i = h / G;
+      const int32_t s = idx[r];
+      const int32_t t0 = cu_seqlens[r], t1 = cu_seqlens[r + 1];
+      if (!slot_valid(s, d->pool_slots)) {
+        for (int32_t t = t0; t < t1; ++t)
+          for (int j = 0; j < dv; ++j) o[((size_t)t * Hv + h) * dv + j] = 0.0;
+        continue;
+      }
+      double* slot = pool + ((size_t)s * Hv + h) * tile;
+      for (size_t e = 0; e < tile; ++e) S[e] = (fresh && fresh[r]) ? 0.0 : slot[e];
+      for (int32_t t = t0; t < t1; ++t)
+        gdn_token(dk, dv, S, q + ((size_t)t * Hk + kh_i) * dk, k + ((size_t)t * Hk + kh_i) * dk,
+                  v + ((size_t)t * Hv + h) * dv, a[(size_t)t * Hv + h], b[(size_t)t * Hv + h], A_log[h],
+                  dt_bias[h], d->scale, d->eps, 0, o + ((size_t)t * Hv + h) * dv, qh, kh, u);
+      for (size_t e = 0; e < tile; ++e) slot[e] = d->state_bf16 ? oracle_round_bf16(S[e]) : S[e];
+    }
+    free(qh); free(kh); free(u); free(S);
+  }
+  return 0;
+}

@@ -70,6 +70,15 @@ int32_t oracle_commit_replay(const oracle_dims* d, const double* A_log, const do
                              const double* rk, const double* rv, const double* ra, const double* rb,
                              int32_t rT, const int32_t* rlen, int32_t nthreads);
 
+/* Prefill of d->batch variable-length sequences (cu_seqlens [B+1]; q, k [N][Hk][dk],
+ * v, o [N][Hv][dv], a, b [N][Hv] with N = cu_seqlens[B]) from pooled initial states
+ * (zero where fresh[r] != 0; fresh may be NULL), no rounding between tokens, final state
+ * stored to the slot (rounded once for a bf16 pool). d->T is not used. */
+int32_t oracle_prefill(const oracle_dims* d, const int32_t* cu_seqlens, const double* q, const double* k,
+                       const double* v, const double* a, const double* b, const double* A_log,
+                       const double* dt_bias, double* pool, const int32_t* idx, const int32_t* fresh,
+                       double* o, int32_t nthreads);
+
 /* Gated RMS normalisation of n output vectors of length dv:
  * y[j] = weight[j] * o[j] / sqrt(mean(o^2) + eps) * silu(z[j]). */
 void oracle_gated_norm(int64_t n, int32_t dv, const double* o, const double* z, const double* weight,

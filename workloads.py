@@ -319,3 +319,88 @@ def make_gate_inputs(w: Workload, seed: int = 0) -> dict:
     z = rng.standard_normal((w.batch, w.T, w.Hv, w.dv))
     weight = rng.uniform(0.5, 1.5, w.dv)
     return dict(z=_store(z, w.io_dtype), norm_weight=torch.from_numpy(weight.astype(np.float32)))
+
+
+# ---------------------------------------------------------------- chunked prefill
+# Prefill of variable-length sequences from pooled initial states, with a mask that zeroes
+# fresh states (TensorRT-LLM PR 20937, Per-File QA Perspective: the chunked gated delta
+# rule prefill with a bf16 state and an initial-state mask). Tokens of all sequences are
+# packed along the first axis (q, k [N,Hk,dk], v [N,Hv,dv], a, b [N,Hv]); cu_seqlens
+# [B+1] are the offsets.
+#
+# Recipe (one ``numpy.random.default_rng(seed)``, in this order): slot indices as for the
+# GDN workloads (n_pad rows set to -1); fresh flags: n_fresh distinct rows; q, k ~ N(0,1)
+# L2-normalised per vector; v, a, b ~ N(0,1); A_log = log U[1,16), dt_bias ~ N(0, 0.1);
+# the pool ~ N(0, 0.1) in float32.
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    seqlens: tuple
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    pool: int
+    state_dtype: str
+    io_dtype: str
+    n_fresh: int = 0
+    n_pad: int = 0
+    description: str = ""
+
+    @property
+    def batch(self) -> int:
+        return len(self.seqlens)
+
+    @property
+    def tokens(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def scale(self) -> float:
+        return self.dk ** -0.5
+
+
+PREFILL_WORKLOADS: list[PrefillWorkload] = [
+    PrefillWorkload("prefill-tiny-f32", seqlens=(5, 0, 19, 16), Hk=1, Hv=2, dk=16, dv=16, pool=6,
+                    state_dtype="f32", io_dtype="f32", n_fresh=1, n_pad=1,
+                    description="tiny: 4 sequences (one empty, one padding, one fresh), d=16"),
+    PrefillWorkload("prefill-mixed-bf16", seqlens=(1, 17, 64, 300, 1000, 16, 555, 33), Hk=4, Hv=8, dk=128, dv=128,
+                    pool=32, state_dtype="bf16", io_dtype="bf16", n_fresh=2, n_pad=1,
+                    description="mixed lengths 1..1000, Hk=4, Hv=8, d=128, bf16, 2 fresh, 1 padding"),
+    PrefillWorkload("prefill-8x2048-bf16", seqlens=(2048,) * 8, Hk=4, Hv=8, dk=128, dv=128, pool=64,
+                    state_dtype="bf16", io_dtype="bf16", n_fresh=4,
+                    description="8 sequences x 2048 tokens, Hk=4, Hv=8 (one GPU's share at TP=4), d=128, bf16"),
+    PrefillWorkload("prefill-4x4096-f32", seqlens=(4096,) * 4, Hk=16, Hv=32, dk=128, dv=128, pool=16,
+                    state_dtype="f32", io_dtype="bf16", n_fresh=2,
+                    description="4 sequences x 4096 tokens, Hk=16, Hv=32, d=128, fp32 state, bf16 io"),
+]
+PREFILL_HEADLINE = 2
+
+
+def make_prefill_inputs(w: PrefillWorkload, seed: int = 0) -> dict:
+    """Draw one prefill batch. Returns CPU torch tensors."""
+    rng = np.random.default_rng(seed)
+    B, N, Hk, Hv, dk, dv, P = w.batch, w.tokens, w.Hk, w.Hv, w.dk, w.dv, w.pool
+    assert B <= P, "more sequences than pool slots"
+    idx = rng.permutation(P)[:B].astype(np.int32)
+    if w.n_pad:
+        idx[rng.choice(B, size=w.n_pad, replace=False)] = -1
+    fresh = np.zeros(B, np.int32)
+    if w.n_fresh:
+        fresh[rng.choice(B, size=w.n_fresh, replace=False)] = 1
+    cu = np.concatenate([[0], np.cumsum(w.seqlens)]).astype(np.int32)
+    q = _unit(rng.standard_normal((N, Hk, dk)))
+    k = _unit(rng.standard_normal((N, Hk, dk)))
+    v = rng.standard_normal((N, Hv, dv))
+    a = rng.standard_normal((N, Hv))
+    b = rng.standard_normal((N, Hv))
+    A_log = np.log(rng.uniform(1.0, 16.0, Hv))
+    dt_bias = rng.normal(0.0, 0.1, Hv)
+    pool = rng.standard_normal((P, Hv, dk, dv), dtype=np.float32) * np.float32(0.1)
+    return dict(idx=torch.from_numpy(idx), fresh=torch.from_numpy(fresh), cu_seqlens=torch.from_numpy(cu),
+                q=_store(q, w.io_dtype), k=_store(k, w.io_dtype), v=_store(v, w.io_dtype),
+                a=_store(a, w.io_dtype), b=_store(b, w.io_dtype),
+                A_log=torch.from_numpy(A_log.astype(np.float32)), dt_bias=torch.from_numpy(dt_bias.astype(np.float32)),
+                pool=_store(pool, w.state_dtype))
