@@ -139,6 +139,22 @@ GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int
                       const int32_t* state_indices, const int32_t* accept_len,
                       void* state_pool, void* stream);
 
+/* Chunked prefill from pooled initial states [P3] (Per-File QA Perspective: the chunked
+ * gated delta rule prefill with a bf16 state and an initial-state mask that zeroes fresh
+ * states). dims->batch sequences of variable length; their tokens are packed along the
+ * first axis: q, k [N][Hk][d_k], v, o [N][Hv][d_v], a, b [N][Hv] (N = cu_seqlens[B];
+ * sequence r holds tokens cu_seqlens[r] .. cu_seqlens[r+1]-1, offsets non-decreasing);
+ * dims->T is ignored. Per valid row r and v-head h the state starts at
+ * state_pool[idx[r]] (zero where fresh[r] != 0; fresh may be NULL), every token runs
+ * through the update, o is written for every token, and the final state is stored back
+ * to the slot. Between tokens the state stays fp32 and is not rounded; a bf16 pool
+ * receives the final state rounded to nearest even once. Padding rows get o = 0 and no
+ * state access. The chunked form runs on the bf16 matrix cores: io must be bf16, d_k 128,
+ * d_v a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise). Valid slots must be distinct. */
+GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                               const int32_t* state_indices, const int32_t* cu_seqlens,
+                               const int32_t* fresh, void* stream);
+
 /* The gated RMS normalisation of the output, fused into verify or decode [P3] (Per-File QA
  * Perspective: the decode-rows GDN kernel carries a gated norm; the dense-FP8 notes name
  * a token-major gated RMS norm). The pages do not print it; this is the standard form,

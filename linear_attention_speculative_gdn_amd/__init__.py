@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
-EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
             "gdn_conv_update", "gdn_conv_commit", "gdn_status_string", "gdn_abi_version")
 GDN_CONV_MAX_WIDTH = 8
 GDN_MAX_T = 16
@@ -80,13 +80,14 @@ def lib() -> ctypes.CDLL:
         L.gdn_verify.argtypes = [D, I, vp, vp, vp, i32, i32, vp, vp]
         L.gdn_commit.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.gdn_verify_gated.argtypes = [D, I, ctypes.POINTER(GdnOutGate), vp, vp, vp, i32, i32, vp, vp]
+        L.gdn_prefill.argtypes = [D, I, vp, vp, vp, vp, vp]
         TK = ctypes.POINTER(GdnTokens)
         L.gdn_verify_replay.argtypes = [D, I, vp, vp, TK, vp, i32, vp]
         L.gdn_commit_replay.argtypes = [D, vp, vp, vp, vp, TK, vp, vp]
         CD = ctypes.POINTER(GdnConvDims)
         L.gdn_conv_update.argtypes = [CD, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp]
         L.gdn_conv_commit.argtypes = [CD, vp, vp, vp, vp, vp]
-        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
                   "gdn_conv_update", "gdn_conv_commit"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -358,3 +359,45 @@ def gdn_conv_commit(x, conv_pool, state_indices, accept_len, *, stream=None) -> 
     st = lib().gdn_conv_commit(ctypes.byref(dims), _ptr(x), _ptr(conv_pool), _ptr(state_indices),
                                _ptr(accept_len), _stream(x.device, stream))
     _raise(st, "gdn_conv_commit")
+
+
+# ---------------------------------------------------------------- chunked prefill
+# Tokens of all sequences packed along the first axis: q, k [N,Hk,dk], v, o [N,Hv,dv],
+# a, b [N,Hv]; cu_seqlens [B+1] int32 offsets; state_indices, fresh [B] int32.
+
+def gdn_prefill(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh=None, *,
+                scale=None, l2norm_eps=1e-6, stream=None) -> None:
+    """Prefill of variable-length sequences from pooled initial states (zero where fresh[r]);
+    o for every token, the final state back to each valid slot."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for n_, t_, nd in (("q", q, 3), ("k", k, 3), ("v", v, 3), ("o", o, 3), ("a", a, 2), ("b", b, 2),
+                       ("A_log", A_log, 1), ("dt_bias", dt_bias, 1), ("state_pool", state_pool, 4),
+                       ("state_indices", state_indices, 1), ("cu_seqlens", cu_seqlens, 1)):
+        _need(t_, n_, nd, dev)
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    B = state_indices.shape[0]
+    if k.shape != q.shape or v.shape != (N, Hv, dv) or o.shape != v.shape or a.shape != (N, Hv) or b.shape != (N, Hv):
+        raise ValueError("q/k [N,Hk,dk], v/o [N,Hv,dv], a/b [N,Hv] disagree")
+    if state_pool.shape[1:] != (Hv, dv, dk):
+        raise ValueError(f"state_pool must be [P, {Hv}, {dv}, {dk}]")
+    if cu_seqlens.shape != (B + 1,) or cu_seqlens.dtype != torch.int32 or state_indices.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32 [B+1], state_indices int32 [B]")
+    if fresh is not None:
+        _need(fresh, "fresh", 1, dev)
+        if fresh.shape != (B,) or fresh.dtype != torch.int32:
+            raise ValueError("fresh must be int32 [B]")
+    for n_, t_ in (("k", k), ("v", v), ("o", o), ("a", a), ("b", b)):
+        if t_.dtype != q.dtype:
+            raise TypeError(f"{n_} must have q's dtype")
+    if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise TypeError("A_log and dt_bias must be float32")
+    dims = GdnDims(B, 1, Hk, Hv, dk, dv, state_pool.shape[0], _dt(state_pool), _dt(q),
+                   float(dk ** -0.5 if scale is None else scale), float(l2norm_eps))
+    io = GdnIo(q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
+               dt_bias.data_ptr(), o.data_ptr())
+    st = lib().gdn_prefill(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
+                           _ptr(cu_seqlens), _ptr(fresh), _stream(dev, stream))
+    _raise(st, "gdn_prefill")

@@ -160,6 +160,32 @@ gdn_status gdn_verify_gated(const gdn_dims* dims, const gdn_io* io, const gdn_ou
                        prev_accept_len, stream, gate);
 }
 
+gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool, const int32_t* state_indices,
+                       const int32_t* cu_seqlens, const int32_t* fresh, void* stream) {
+  gdn_status s = check_dims(dims, false);
+  if (s != GDN_OK) return s;
+  if (dims->io_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;  // the matrix cores take bf16 tokens
+  if (dims->d_k != 128 || dims->d_v % 32 != 0) return GDN_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return GDN_OK;
+  if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
+      !state_pool || !state_indices || !cu_seqlens)
+    return GDN_ERR_NULL;
+  if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->o, 16) ||
+      !aligned(state_pool, 16) || !aligned(io->a, 2) || !aligned(io->b, 2) || !aligned(io->A_log, 4) ||
+      !aligned(io->dt_bias, 4) || !aligned(state_indices, 4) || !aligned(cu_seqlens, 4) ||
+      (fresh && !aligned(fresh, 4)))
+    return GDN_ERR_ALIGN;
+  gdn::PrefillArgs p;
+  p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
+  p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
+  p.pool = state_pool; p.idx = state_indices; p.fresh = fresh; p.cu = cu_seqlens;
+  p.B = dims->batch; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.DV = dims->d_v;
+  p.P = dims->pool_slots; p.G = dims->num_v_heads / dims->num_k_heads;
+  p.scale = dims->scale; p.eps = dims->l2norm_eps;
+  const hipError_t e = gdn::launch_prefill(static_cast<Dt>(dims->state_dtype), p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cache_T,
                       const int32_t* state_indices, const int32_t* accept_len, void* state_pool,
                       void* stream) {

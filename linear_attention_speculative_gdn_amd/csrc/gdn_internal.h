@@ -1,5 +1,6 @@
 // gdn_internal.h -- launch descriptors shared by the host entry points (gdn_api.cpp)
-// and the gfx950 kernels (gdn_kernels.hip, gdn_conv.hip). Not part of the public ABI.
+// and the gfx950 kernels (gdn_kernels.hip, gdn_conv.hip, gdn_prefill.hip). Not part of
+// the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -79,6 +80,26 @@ struct ConvArgs {
 
 // commit_only: advance each valid slot over prev_len tokens of prev_x and stop.
 hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t stream);
+
+// One launch of the chunked prefill (bf16 io, d_k = 128, d_v a multiple of 32).
+struct PrefillArgs {
+  const void* q;               // [N][Hk][128]
+  const void* k;
+  const void* v;               // [N][Hv][DV]
+  const void* a;               // [N][Hv]
+  const void* b;
+  const float* A_log;          // [Hv]
+  const float* dt_bias;
+  void* o;                     // [N][Hv][DV]
+  void* pool;                  // [P][Hv][DV][128] state dtype
+  const int32_t* idx;          // [B]
+  const int32_t* fresh;        // [B] or nullptr
+  const int32_t* cu;           // [B+1] token offsets
+  int32_t B, Hk, Hv, DV, P, G;
+  float scale, eps;
+};
+
+hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream);
 
 constexpr int kCommitChunksPerThread = 4;
 constexpr int kThreads = 256;

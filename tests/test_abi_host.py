@@ -148,6 +148,22 @@ def test_verify_gated_validation(L):
     assert vg(dims(), i=io(q=None)) == 1
 
 
+def test_prefill_validation(L):
+    def pf(d, i=None, pool=A16 * 9, idx=A16 * 10, cu=A16 * 11, fresh=None):
+        i = io() if i is None else i
+        return L.gdn_prefill(ctypes.byref(d), ctypes.byref(i), pool, idx, cu, fresh, None)
+    assert pf(dims(batch=0)) == 0
+    assert pf(dims(batch=0, T=0)) == 0                       # T is not used
+    assert pf(dims(io_dtype=gdn.GDN_DTYPE_F32)) == 5         # the matrix-core path takes bf16 tokens
+    assert pf(dims(batch=0, d_k=64)) == 5
+    assert pf(dims(batch=0, d_v=48)) == 5                    # d_v a multiple of 32
+    assert pf(dims(), cu=None) == 1
+    assert pf(dims(), i=io(v=None)) == 1
+    assert pf(dims(), cu=A16 * 11 + 2) == 4
+    assert pf(dims(), fresh=A16 * 12 + 1) == 4
+    assert pf(dims(), i=io(q=A16 + 8)) == 4
+
+
 def tokens(**kw):
     base = dict(k=A16 * 13, v=A16 * 14, a=A16 * 15, b=A16 * 16, T_src=4)
     base.update(kw)

@@ -1,0 +1,154 @@
+"""GPU tests of the chunked prefill (gdn_prefill) through the C ABI, against the float64
+oracle that runs the recurrence token by token.
+
+The kernel evaluates the chunked form on bf16 matrix cores: every product takes bf16
+operands (the stored keys, queries and values exactly; the state, the triangular inverse,
+W, U and the output mask rounded to nearest even, at most 2^-9 relative each) and
+accumulates in fp32. Errors are therefore measured relative to the scale of the result:
+per (sequence, v-head), max |o_gpu - o_ref| <= TOL_O * max |o_ref| and, for the stored
+state, max |S_gpu - S_ref| <= TOL_S * max |S_ref| (plus bf16 rounding of a bf16 pool).
+The bound: one chunk chains three rounded products into U (Tm, W S_0, then U itself in
+P U and in the state update), about 3 * 2^-8 relative to the magnitudes involved; the
+decays and the delta rule keep the state bounded, so the error does not grow with the
+number of chunks beyond that of one chunk's contributions. TOL_O = TOL_S = 2^-5 leaves a
+factor of about 2.5 over 3 * 2^-8 for the sums of a few such terms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_speculative_gdn_amd as gdn
+import oracle
+import workloads
+from gpu_harness import say
+from workloads import PrefillWorkload, from_device_state, to_device_state
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_O = 2.0 ** -5
+TOL_S = 2.0 ** -5
+
+
+def f64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def run_gpu(w, x):
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "fresh", "cu_seqlens")}
+    g["pool"] = to_device_state(x["pool"]).to(DEV)
+    pool0 = g["pool"].clone()
+    o = torch.full((w.tokens, w.Hv, w.dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    gdn.gdn_prefill(g["q"], g["k"], g["v"], g["a"], g["b"], g["A_log"], g["dt_bias"], o, g["pool"], g["idx"],
+                    g["cu_seqlens"], g["fresh"], scale=w.scale)
+    torch.cuda.synchronize()
+    return o, g["pool"], pool0
+
+
+def run_oracle(w, x):
+    d = oracle.make_dims(w.batch, 1, w.Hk, w.Hv, w.dk, w.dv, w.pool, w.state_dtype == "bf16", scale=w.scale)
+    return oracle.prefill(d, x["cu_seqlens"].numpy(), f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["a"]),
+                          f64(x["b"]), f64(x["A_log"]), f64(x["dt_bias"]), f64(x["pool"]), x["idx"].numpy(),
+                          x["fresh"].numpy())
+
+
+def check(w, x, label, seed=0):
+    o, pool, pool0 = run_gpu(w, x)
+    ref = run_oracle(w, x)
+    og, cu, idx = f64(o), x["cu_seqlens"].numpy(), x["idx"].numpy()
+    pg = from_device_state(pool.cpu()).double().numpy()
+    worst_o = worst_s = 0.0
+    for r in range(w.batch):
+        sl = slice(cu[r], cu[r + 1])
+        if not 0 <= idx[r] < w.pool:
+            assert np.all(og[sl] == 0.0), f"{label}: padding row {r} has o != 0"
+            continue
+        for h in range(w.Hv):
+            if cu[r + 1] > cu[r]:
+                scale_o = max(np.abs(ref["o"][sl, h]).max(), 1e-30)
+                worst_o = max(worst_o, np.abs(og[sl, h] - ref["o"][sl, h]).max() / scale_o)
+            Sr = ref["pool"][idx[r], h]
+            scale_s = max(np.abs(Sr).max(), 1e-30)
+            round_s = 2.0 ** -8 if w.state_dtype == "bf16" else 0.0
+            worst_s = max(worst_s, (np.abs(pg[idx[r], h] - Sr).max() - round_s * scale_s) / scale_s)
+    say(f"[prefill] {label}: o err {worst_o:.2e}, state err {worst_s:.2e} (relative to the per-head max)")
+    assert worst_o <= TOL_O and worst_s <= TOL_S
+    touched = np.zeros(w.pool, bool)
+    touched[idx[(idx >= 0) & (idx < w.pool)]] = True
+    ut = torch.from_numpy(np.nonzero(~touched)[0])
+    assert torch.equal(pool.cpu()[ut], pool0.cpu()[ut]), f"{label}: an untouched slot changed"
+
+
+@pytest.mark.parametrize("wi", [1, 2, 3], ids=[workloads.PREFILL_WORKLOADS[i].name for i in (1, 2, 3)])
+def test_prefill_parity(wi):
+    w = workloads.PREFILL_WORKLOADS[wi]
+    check(w, workloads.make_prefill_inputs(w, seed=0), w.name)
+
+
+GEOM = [
+    PrefillWorkload("edges-dv32-f32", seqlens=(0, 1, 15, 16, 17, 33, 48), Hk=1, Hv=2, dk=128, dv=32, pool=9,
+                    state_dtype="f32", io_dtype="bf16", n_fresh=2, n_pad=1),
+    PrefillWorkload("dv64-g4-bf16", seqlens=(70, 5, 129), Hk=1, Hv=4, dk=128, dv=64, pool=4,
+                    state_dtype="bf16", io_dtype="bf16", n_fresh=1),
+    PrefillWorkload("dv256-f32", seqlens=(40, 97), Hk=2, Hv=2, dk=128, dv=256, pool=3,
+                    state_dtype="f32", io_dtype="bf16"),
+    PrefillWorkload("long-3000-bf16", seqlens=(3000,), Hk=1, Hv=1, dk=128, dv=128, pool=2,
+                    state_dtype="bf16", io_dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("w", GEOM, ids=[w.name for w in GEOM])
+def test_prefill_geometries(w):
+    check(w, workloads.make_prefill_inputs(w, seed=1), w.name)
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+def test_prefill_slow_decay_long_memory(state):
+    """Weak decay (exp(A_log) = 0.02, g ~ 0.99 per token) keeps hundreds of tokens in the
+    state, so errors carried across chunks would show; the workloads' own decays forget
+    within a few tokens."""
+    w = PrefillWorkload(f"slow-{state}", seqlens=(2048, 333), Hk=2, Hv=4, dk=128, dv=128, pool=4,
+                        state_dtype=state, io_dtype="bf16", n_fresh=1)
+    x = workloads.make_prefill_inputs(w, seed=4)
+    x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
+    check(w, x, w.name)
+
+
+def test_prefill_split_continues_from_the_pool():
+    """Two calls (a chunked prefill across scheduler steps, cut off a chunk boundary)
+    follow the single call to the same tolerance."""
+    w = PrefillWorkload("whole", seqlens=(200,), Hk=1, Hv=2, dk=128, dv=128, pool=2, state_dtype="f32",
+                        io_dtype="bf16")
+    x = workloads.make_prefill_inputs(w, seed=2)
+    o_whole, pool_whole, _ = run_gpu(w, x)
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx")}
+    pool = to_device_state(x["pool"]).to(DEV)
+    outs = []
+    for a_, b_ in ((0, 77), (77, 200)):
+        o = torch.empty((b_ - a_, w.Hv, w.dv), dtype=torch.bfloat16, device=DEV)
+        gdn.gdn_prefill(g["q"][a_:b_], g["k"][a_:b_], g["v"][a_:b_], g["a"][a_:b_], g["b"][a_:b_], g["A_log"],
+                        g["dt_bias"], o, pool, g["idx"], torch.tensor([0, b_ - a_], dtype=torch.int32, device=DEV))
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_split = torch.cat(outs).double()
+    err = float((o_split - o_whole.double()).abs().max() / o_whole.double().abs().max())
+    serr = float((pool - pool_whole).abs().max() / pool_whole.abs().max())
+    say(f"[prefill] split vs whole: o {err:.2e}, state {serr:.2e}")
+    assert err <= TOL_O and serr <= TOL_S
+
+
+def test_prefill_unsupported_and_empty():
+    w = PrefillWorkload("e", seqlens=(4,), Hk=1, Hv=1, dk=128, dv=32, pool=1, state_dtype="f32", io_dtype="f32")
+    x = workloads.make_prefill_inputs(w)
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "cu_seqlens")}
+    pool = to_device_state(x["pool"]).to(DEV)
+    o = torch.empty((4, 1, 32), dtype=torch.float32, device=DEV)
+    with pytest.raises(gdn.GdnError) as e:      # fp32 tokens: the matrix-core path takes bf16
+        gdn.gdn_prefill(g["q"], g["k"], g["v"], g["a"], g["b"], g["A_log"], g["dt_bias"], o, pool, g["idx"],
+                        g["cu_seqlens"])
+    assert e.value.status == 5
+    q0 = torch.empty((0, 1, 128), dtype=torch.bfloat16, device=DEV)
+    v0 = torch.empty((0, 1, 32), dtype=torch.bfloat16, device=DEV)
+    ab0 = torch.empty((0, 1), dtype=torch.bfloat16, device=DEV)
+    gdn.gdn_prefill(q0, q0, v0, ab0, ab0, g["A_log"], g["dt_bias"], v0, pool, torch.empty(0, dtype=torch.int32,
+                    device=DEV), torch.zeros(1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
