@@ -230,17 +230,73 @@ def conv_main(args):
     print(json.dumps(res), flush=True)
 
 
+def prefill_main(args):
+    """The chunked prefill (gdn_prefill) on the prefill workloads: one call per step over
+    the whole batch of sequences; bound by the matrix cores, priced against the bf16 dense
+    MFMA peak with the flops of the chunked form."""
+    import torch
+
+    import linear_attention_speculative_gdn_amd as gdn
+    import workloads
+
+    wi = workloads.PREFILL_HEADLINE if args.workload is None else args.workload
+    w = workloads.PREFILL_WORKLOADS[wi]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] prefill workload {wi}: {w.description}")
+    x = workloads.make_prefill_inputs(w, seed=0)
+    flops = workloads.prefill_flops(w)
+    nbytes = workloads.prefill_bytes(w)
+    R = 2
+    sets = []
+    for _ in range(R):
+        s = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "fresh", "cu_seqlens")}
+        s["pool"] = workloads.to_device_state(x["pool"]).to(dev)
+        s["o"] = torch.empty((w.tokens, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+
+    def call(s):
+        gdn.gdn_prefill(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"], s["pool"],
+                        s["idx"], s["cu_seqlens"], s["fresh"], scale=w.scale)
+
+    call(sets[0])
+    torch.cuda.synchronize()
+    run = Runner(call, sets, torch.cuda.Stream(), args.eager, 2)
+    run.warm(args.warmup)
+    t = run.timed(args.steps)
+    us = t / args.steps * 1e6
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"[bench] prefill: {us:.1f} us/launch, {w.tokens / (us * 1e-6) / 1e6:.1f} M tokens/s, {tflops:.1f} TFLOP/s "
+        f"({flops / 1e9:.2f} GFLOP of the chunked form), {nbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+    res = {
+        "metric": "GDN chunked prefill tokens/s + achieved MFMA TFLOP/s vs bf16 dense peak",
+        "value": w.tokens / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.batch, "tokens": w.tokens, "num_k_heads": w.Hk,
+                   "num_v_heads": w.Hv, "d_k": w.dk, "d_v": w.dv, "state_dtype": w.state_dtype,
+                   "io_dtype": w.io_dtype, "chunk": 16, "launch": "eager" if args.eager else "hip_graph",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tflops / 2500.0, "traffic": None, "kernel": "gdn_prefill (prefill_kernel)",
+                     "algorithmic_flops_per_launch": flops, "avg_launch_us": us,
+                     "hbm_GBps_algorithmic": nbytes / (us * 1e-6) / 1e9},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=8000)
     ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--workload", type=int, default=None, help="workload index (default: the MTP verify T=4 one)")
-    ap.add_argument("--mode", choices=("intermediate", "gated", "replay", "conv"), default="intermediate",
+    ap.add_argument("--mode", choices=("intermediate", "gated", "replay", "conv", "prefill"), default="intermediate",
                     help="intermediate: verify storing every intermediate state, then commit (the "
                          "workload as defined); replay: cached-replay verify with in-kernel commit of the "
                          "previous step's accepted prefix (one launch per step, no per-token states); gated: "
-                         "intermediate with the gated RMS-norm output epilogue fused into verify; conv: "
+                         "intermediate with the gated RMS-norm output epilogue fused into verify; prefill: the chunked "
+                         "prefill on the matrix cores (--workload indexes the prefill workloads); conv: "
                          "the short causal convolution next to the GDN state (--workload indexes the "
                          "convolution workloads)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
@@ -256,6 +312,8 @@ def main():
         sys.exit(2)
     if args.mode == "conv":
         return conv_main(args)
+    if args.mode == "prefill":
+        return prefill_main(args)
 
     import numpy as np
     import torch

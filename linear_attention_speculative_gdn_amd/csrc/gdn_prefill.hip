@@ -46,6 +46,7 @@ constexpr int kNB = 32;       // value columns per wave
 constexpr int kKT = kDK / 16; // 16-row tiles of the key dimension
 constexpr int kNT = kNB / 16; // 16-column tiles of the wave's value block
 constexpr int kStr = kDK + 8; // LDS row stride (bf16) of 128-wide chunk matrices, padded
+constexpr int kTS = kC + 4;   // LDS row stride (bf16) of the transposed chunk matrices
 
 __device__ __forceinline__ f32x4 mfma(const s16x4& a, const s16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -65,25 +66,18 @@ __device__ __forceinline__ s16x4 ld4(const uint16_t* base, int row, int stride, 
   return *reinterpret_cast<const s16x4*>(base + row * stride + c);
 }
 
-// four bf16 of one column, rows r0..r0+3
-__device__ __forceinline__ s16x4 ld4col(const uint16_t* base, int r0, int stride, int c) {
-  s16x4 v;
-  v[0] = short(base[(r0 + 0) * stride + c]); v[1] = short(base[(r0 + 1) * stride + c]);
-  v[2] = short(base[(r0 + 2) * stride + c]); v[3] = short(base[(r0 + 3) * stride + c]);
-  return v;
-}
-
 struct __attribute__((aligned(16))) PrefillLds {
   uint16_t k[kC * kStr];   // the chunk's keys (stored bf16 values; zero rows past the end)
   uint16_t q[kC * kStr];   // queries
   uint16_t w[kC * kStr];   // W = Tm diag(beta Gam rk) K, bf16
-  uint16_t v[kC * kNB];    // the wave's value columns
+  uint16_t kt[kDK * kTS];  // K^T: the keys by dimension, for column operands
+  uint16_t vt[kNB * kTS];  // V^T: the wave's value columns by column
   uint16_t tw[kC * kC];    // Tm diag(beta Gam rk), bf16
   uint16_t tv[kC * kC];    // Tm diag(beta), bf16
   uint16_t pm[kC * kC];    // P = M o (rq rk) Q K^T, bf16
   uint16_t o[kC * kNB];    // the chunk's outputs, bf16, for 16-byte stores
   float a[kC * kC];        // A (fp32) for the triangular solve
-  float rk[kC], rq[kC], beta[kC], G[kC], logg[kC];
+  float rk[kC], rq[kC], beta[kC], G[kC];
 };
 
 template <typename ST>
@@ -139,57 +133,94 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
 
   const float A_neg = -expf(p.A_log[h]), dtb = p.dt_bias[h];
 
+  // The chunk's raw inputs, loaded one chunk ahead: the loads of chunk i+1 are in flight
+  // while chunk i computes. Token indices are clamped into the sequence, so every load
+  // is unconditional (a load in a branch is waited on at the branch end).
+  u32x4 kr[4], qr[4], vr;
+  uint16_t ar, br;
+  auto fetch = [&](int cs_) {
+    const int last = t1 - 1;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const size_t src = (size_t(min(cs_ + it * 4 + l4, last)) * p.Hk + kh) * kDK + 8 * l16;
+      kr[it] = *reinterpret_cast<const u32x4*>(kg + src);
+      qr[it] = *reinterpret_cast<const u32x4*>(qg + src);
+    }
+    vr = *reinterpret_cast<const u32x4*>(vg + (size_t(min(cs_ + (l >> 2), last)) * p.Hv + h) * p.DV + c0 + 8 * (l & 3));
+    const size_t tg = size_t(min(cs_ + l16, last)) * p.Hv + h;
+    ar = ag[tg];
+    br = bg[tg];
+  };
+  if (t1 > t0) fetch(t0);
+
   for (int cs = t0; cs < t1; cs += kC) {
     const int n = min(kC, t1 - cs);
-    // ---- 1. stage the chunk: k and q rows (256 B each), the wave's 32 value columns
+    // ---- 1. stage the chunk: k and q rows (256 B each), the wave's 32 value columns;
+    //         gates of token l (l < 16); tokens past the end: zero inputs, no decay, no write
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int t = it * 4 + l4, seg = l16;
-      const size_t src = (size_t(cs + min(t, n - 1)) * p.Hk + kh) * kDK + 8 * seg;
-      u32x4 kk = *reinterpret_cast<const u32x4*>(kg + src);
-      u32x4 qq = *reinterpret_cast<const u32x4*>(qg + src);
-      if (t >= n) kk = qq = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 kk = (t < n) ? kr[it] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 qq = (t < n) ? qr[it] : u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint2*>(L.k + t * kStr + 8 * seg) = uint2{kk.x, kk.y};
       *reinterpret_cast<uint2*>(L.k + t * kStr + 8 * seg + 4) = uint2{kk.z, kk.w};
       *reinterpret_cast<uint2*>(L.q + t * kStr + 8 * seg) = uint2{qq.x, qq.y};
       *reinterpret_cast<uint2*>(L.q + t * kStr + 8 * seg + 4) = uint2{qq.z, qq.w};
+      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        L.kt[(8 * seg + 2 * e) * kTS + t] = uint16_t(kw[e]);
+        L.kt[(8 * seg + 2 * e + 1) * kTS + t] = uint16_t(kw[e] >> 16);
+      }
     }
     {
       const int t = l >> 2, seg = l & 3;
-      u32x4 vv = *reinterpret_cast<const u32x4*>(vg + (size_t(cs + min(t, n - 1)) * p.Hv + h) * p.DV + c0 + 8 * seg);
-      if (t >= n) vv = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(L.v + t * kNB + 8 * seg) = vv;
+      const u32x4 vv = (t < n) ? vr : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        L.vt[(8 * seg + 2 * e) * kTS + t] = uint16_t(vw[e]);
+        L.vt[(8 * seg + 2 * e + 1) * kTS + t] = uint16_t(vw[e] >> 16);
+      }
     }
-    // gates of token l (l < 16); tokens past the end: no decay, no write
-    if (l < kC) {
-      const int tc = cs + min(l, n - 1);
-      const float x = bf(ag[size_t(tc) * p.Hv + h]) + dtb;
-      const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    {  // gates of token l (lanes < 16) and the inclusive prefix sum of the log-decays
       const bool live = l < n;
-      L.logg[l] = live ? A_neg * sp : 0.f;
-      L.beta[l] = live ? 1.f / (1.f + expf(-bf(bg[size_t(tc) * p.Hv + h]))) : 0.f;
+      const float x = bf(ar) + dtb;
+      float lg = live ? A_neg * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : 0.f;
+#pragma unroll
+      for (int d = 1; d < kC; d *= 2) {
+        const float y = __shfl_up(lg, d);
+        if (l16 >= d) lg += y;
+      }
+      if (l < kC) {
+        L.G[l] = lg;
+        L.beta[l] = live ? 1.f / (1.f + expf(-bf(br))) : 0.f;
+      }
     }
+    fetch(cs + kC);  // the next chunk (clamped: harmless past the end)
     __syncthreads();
     // ---- 2. inverse L2 norms (4 lanes per token) and the cumulative log-decay
-    {
+    {  // inverse L2 norms, 4 lanes per token, 16-byte LDS reads
       const int t = l >> 2, part = l & 3;
       float sk = 0.f, sq = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const float kv = bf(L.k[t * kStr + 32 * part + e]), qv = bf(L.q[t * kStr + 32 * part + e]);
-        sk = fmaf(kv, kv, sk);
-        sq = fmaf(qv, qv, sq);
+      for (int e8 = 0; e8 < 4; ++e8) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(L.k + t * kStr + 32 * part + 8 * e8);
+        const u32x4 qq = *reinterpret_cast<const u32x4*>(L.q + t * kStr + 32 * part + 8 * e8);
+        float kf[8], qf[8];
+        unpack_io(kk, kf, static_cast<const bf16s*>(nullptr));
+        unpack_io(qq, qf, static_cast<const bf16s*>(nullptr));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sk = fmaf(kf[e], kf[e], sk);
+          sq = fmaf(qf[e], qf[e], sq);
+        }
       }
       sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
       sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
       if (part == 0) {
         L.rk[t] = 1.f / sqrtf(sk + p.eps);
         L.rq[t] = 1.f / sqrtf(sq + p.eps);
-      }
-      if (l < kC) {
-        float g = 0.f;
-        for (int s = 0; s <= l; ++s) g += L.logg[s];
-        L.G[l] = g;
       }
     }
     __syncthreads();
@@ -239,7 +270,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       const s16x4 twA = ld4(L.tw, l16, kC, 4 * l4);
 #pragma unroll
       for (int j = 0; j < kKT; ++j) {
-        const f32x4 W = mfma(twA, ld4col(L.k, 4 * l4, kStr, 16 * j + l16), f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 W = mfma(twA, ld4(L.kt, 16 * j + l16, kTS, 4 * l4), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) L.w[(4 * l4 + i) * kStr + 16 * j + l16] = to_bf(W[i]);
       }
@@ -249,7 +280,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       const s16x4 tvA = ld4(L.tv, l16, kC, 4 * l4);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
-        U[nt] = mfma(tvA, ld4col(L.v, 4 * l4, kNB, 16 * nt + l16), f32x4{0.f, 0.f, 0.f, 0.f});
+        U[nt] = mfma(tvA, ld4(L.vt, 16 * nt + l16, kTS, 4 * l4), f32x4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();
     // ---- 6. U = U~ - W S_0 and Q S_0, with S_0 converted to bf16 B operands in place
@@ -298,7 +329,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       }
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) {
-        const s16x4 kT = ld4col(L.k, 4 * l4, kStr, 16 * kt + l16);
+        const s16x4 kT = ld4(L.kt, 16 * kt + l16, kTS, 4 * l4);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) S[kt][nt] = mfma(kT, uB[nt], S[kt][nt] * gC);
       }

@@ -404,3 +404,22 @@ def make_prefill_inputs(w: PrefillWorkload, seed: int = 0) -> dict:
                 a=_store(a, w.io_dtype), b=_store(b, w.io_dtype),
                 A_log=torch.from_numpy(A_log.astype(np.float32)), dt_bias=torch.from_numpy(dt_bias.astype(np.float32)),
                 pool=_store(pool, w.state_dtype))
+
+
+def prefill_flops(w: PrefillWorkload, chunk: int = 16) -> int:
+    """Flops of the chunked form per call (each product counted once, 2 flop per
+    multiply-add): per chunk of C tokens and v-head, K K^T, Q K^T and W (2 C^2 d_k each),
+    U~ and P U (2 C^2 d_v each), W S_0, Q S_0 and the state update (2 C d_k d_v each).
+    Padding rows count nothing."""
+    per_chunk = 3 * 2 * chunk * chunk * w.dk + 2 * 2 * chunk * chunk * w.dv + 3 * 2 * chunk * w.dk * w.dv
+    chunks = sum((L + chunk - 1) // chunk for L in w.seqlens)
+    return per_chunk * chunks * w.Hv
+
+
+def prefill_bytes(w: PrefillWorkload) -> int:
+    """Bytes one prefill must move: q, k (per k-head), v, a, b and o of every token, and
+    each valid sequence's state tiles read once and written once (bf16 io)."""
+    esz = 2
+    ssz = 4 if w.state_dtype == "f32" else 2
+    tok = w.tokens * (2 * w.Hk * w.dk + 2 * w.Hv * w.dv + 2 * w.Hv) * esz
+    return tok + 2 * w.batch * w.Hv * w.dk * w.dv * ssz
