@@ -42,9 +42,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 16;        // tokens per chunk
 constexpr int kDK = 128;      // key dimension
-constexpr int kNB = 32;       // value columns per wave
 constexpr int kKT = kDK / 16; // 16-row tiles of the key dimension
-constexpr int kNT = kNB / 16; // 16-column tiles of the wave's value block
 constexpr int kStr = kDK + 8; // LDS row stride (bf16) of 128-wide chunk matrices, padded
 constexpr int kTS = kC + 4;   // LDS row stride (bf16) of the transposed chunk matrices
 
@@ -59,6 +57,12 @@ __device__ __forceinline__ s16x4 bf16x4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
+// Phase boundary of the one-wave workgroup: a wave's LDS operations complete in order, so
+// it is enough that its own LDS accesses have retired (and that the compiler does not move
+// memory accesses across). A __syncthreads() here would also wait for the next chunk's
+// global loads still in flight.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint16_t to_bf(float x) { return uint16_t(pack_bf16x2(x, 0.f)); }
 
 // four bf16 of one row at column c (8-byte aligned)
@@ -66,6 +70,7 @@ __device__ __forceinline__ s16x4 ld4(const uint16_t* base, int row, int stride, 
   return *reinterpret_cast<const s16x4*>(base + row * stride + c);
 }
 
+template <int kNB>
 struct __attribute__((aligned(16))) PrefillLds {
   uint16_t k[kC * kStr];   // the chunk's keys (stored bf16 values; zero rows past the end)
   uint16_t q[kC * kStr];   // queries
@@ -96,10 +101,11 @@ __device__ __forceinline__ void store_state(bf16s* dst, const f32x4& s) {
   *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
 }
 
-// grid (value blocks of 32, v-heads, sequences), one wave each. io is bf16.
-template <typename ST>
+// grid (value blocks of kNB columns, v-heads, sequences), one wave each. io is bf16.
+template <typename ST, int kNB>
 __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
-  __shared__ PrefillLds L;
+  constexpr int kNT = kNB / 16;  // 16-column tiles of the wave's value block
+  __shared__ PrefillLds<kNB> L;
   const int vb = blockIdx.x, h = blockIdx.y, row = blockIdx.z;
   const int l = threadIdx.x, l16 = l & 15, l4 = l >> 4;
   const int c0 = vb * kNB;
@@ -115,8 +121,9 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
   uint16_t* og = static_cast<uint16_t*>(p.o);
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
-    for (int t = t0 + (l >> 2); t < t1; t += 16)
-      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + c0 + 8 * (l & 3)) = u32x4{0u, 0u, 0u, 0u};
+    for (int t = t0 + l / (kNB / 8); t < t1; t += 64 / (kNB / 8))
+      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + c0 + 8 * (l % (kNB / 8))) =
+          u32x4{0u, 0u, 0u, 0u};
     return;
   }
 
@@ -146,7 +153,8 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       kr[it] = *reinterpret_cast<const u32x4*>(kg + src);
       qr[it] = *reinterpret_cast<const u32x4*>(qg + src);
     }
-    vr = *reinterpret_cast<const u32x4*>(vg + (size_t(min(cs_ + (l >> 2), last)) * p.Hv + h) * p.DV + c0 + 8 * (l & 3));
+    vr = *reinterpret_cast<const u32x4*>(vg + (size_t(min(cs_ + l / (kNB / 8), last)) * p.Hv + h) * p.DV + c0 +
+                                          8 * (l % (kNB / 8)));
     const size_t tg = size_t(min(cs_ + l16, last)) * p.Hv + h;
     ar = ag[tg];
     br = bg[tg];
@@ -173,8 +181,8 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
         L.kt[(8 * seg + 2 * e + 1) * kTS + t] = uint16_t(kw[e] >> 16);
       }
     }
-    {
-      const int t = l >> 2, seg = l & 3;
+    if (l < kC * (kNB / 8)) {
+      const int t = l / (kNB / 8), seg = l % (kNB / 8);
       const u32x4 vv = (t < n) ? vr : u32x4{0u, 0u, 0u, 0u};
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       }
     }
     fetch(cs + kC);  // the next chunk (clamped: harmless past the end)
-    __syncthreads();
+    lds_sync();
     // ---- 2. inverse L2 norms (4 lanes per token) and the cumulative log-decay
     {  // inverse L2 norms, 4 lanes per token, 16-byte LDS reads
       const int t = l >> 2, part = l & 3;
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
         L.rq[t] = 1.f / sqrtf(sq + p.eps);
       }
     }
-    __syncthreads();
+    lds_sync();
     // ---- 3. K K^T and Q K^T (16 x 16, contraction over d_k = 128)
     f32x4 KK = {0.f, 0.f, 0.f, 0.f}, QK = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -245,18 +253,19 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
         L.pm[t * kC + s] = to_bf(L.rq[t] * rks * dec * QK[i]);
       }
     }
-    __syncthreads();
-    // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16)
+    lds_sync();
+    // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16),
+    //         column-oriented: once x[s] is final it is applied to every later row at once,
+    //         so the dependent chain is 15 steps deep instead of 120
     if (l < kC) {
       const int c = l;
       float x[kC];
 #pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        float acc = (t == c) ? 1.f : 0.f;
+      for (int t = 0; t < kC; ++t) x[t] = (t == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < t; ++s) acc = fmaf(-L.a[t * kC + s], x[s], acc);
-        x[t] = acc;
-      }
+      for (int s = 0; s < kC - 1; ++s)
+#pragma unroll
+        for (int t = s + 1; t < kC; ++t) x[t] = fmaf(-L.a[t * kC + s], x[s], x[t]);
       const float cw = L.beta[c] * expf(L.G[c]) * L.rk[c], cv = L.beta[c];
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
         L.tv[t * kC + c] = to_bf(x[t] * cv);
       }
     }
-    __syncthreads();
+    lds_sync();
     // ---- 5. W = Tm diag(beta Gam rk) K  (16 x 128) and U~ = Tm diag(beta) V  (16 x 32)
     {
       const s16x4 twA = ld4(L.tw, l16, kC, 4 * l4);
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       for (int nt = 0; nt < kNT; ++nt)
         U[nt] = mfma(tvA, ld4(L.vt, 16 * nt + l16, kTS, 4 * l4), f32x4{0.f, 0.f, 0.f, 0.f});
     }
-    __syncthreads();
+    lds_sync();
     // ---- 6. U = U~ - W S_0 and Q S_0, with S_0 converted to bf16 B operands in place
     f32x4 QS[kNT];
 #pragma unroll
@@ -334,14 +343,14 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
         for (int nt = 0; nt < kNT; ++nt) S[kt][nt] = mfma(kT, uB[nt], S[kt][nt] * gC);
       }
     }
-    __syncthreads();
+    lds_sync();
     {
-      const int t = l >> 2, seg = l & 3;
-      if (t < n)
+      const int t = l / (kNB / 8), seg = l % (kNB / 8);
+      if (t < n && l < kC * (kNB / 8))
         *reinterpret_cast<u32x4*>(og + (size_t(cs + t) * p.Hv + h) * p.DV + c0 + 8 * seg) =
             *reinterpret_cast<const u32x4*>(L.o + t * kNB + 8 * seg);
     }
-    __syncthreads();
+    lds_sync();
   }
 
   // ---- the final state back to the slot (rounded once for a bf16 pool)
@@ -352,15 +361,22 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs p) {
       store_state(pool_tile + size_t(c0 + 16 * nt + l16) * kDK + 16 * kt + 4 * l4, S[kt][nt]);
 }
 
+template <typename ST, int NB>
+hipError_t launch_nb(const PrefillArgs& p, hipStream_t stream) {
+  const dim3 grid(unsigned(p.DV / NB), unsigned(p.Hv), unsigned(p.B));
+  hipLaunchKernelGGL((prefill_kernel<ST, NB>), grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// The chunks of a sequence run one after another in one wave, so a launch is bound by
+// that chain; 16-column waves give twice the waves of 32-column ones, for grids that
+// would leave SIMDs idle.
 hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
-  const dim3 grid(unsigned(p.DV / kNB), unsigned(p.Hv), unsigned(p.B));
-  if (state == Dt::F32)
-    hipLaunchKernelGGL((prefill_kernel<float>), grid, dim3(64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<bf16s>), grid, dim3(64), 0, stream, p);
-  return hipGetLastError();
+  const bool narrow = int64_t(p.B) * p.Hv * (p.DV / 32) < 1024;
+  if (state == Dt::F32) return narrow ? launch_nb<float, 16>(p, stream) : launch_nb<float, 32>(p, stream);
+  return narrow ? launch_nb<bf16s, 16>(p, stream) : launch_nb<bf16s, 32>(p, stream);
 }
 
 }  // namespace gdn
