@@ -248,16 +248,20 @@ def prefill_main(args):
     flops = workloads.prefill_flops(w)
     nbytes = workloads.prefill_bytes(w)
     R = 2
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(w.batch, w.tokens, w.Hk, w.Hv, w.dk, w.dv,
+                                               workloads.torch_dtype(w.state_dtype))
     sets = []
     for _ in range(R):
         s = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "fresh", "cu_seqlens")}
         s["pool"] = workloads.to_device_state(x["pool"]).to(dev)
         s["o"] = torch.empty((w.tokens, w.Hv, w.dv), dtype=torch.bfloat16, device=dev)
+        s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         sets.append(s)
+    log(f"[bench] prefill workspace {ws_bytes / 2**20:.1f} MiB per call")
 
     def call(s):
         gdn.gdn_prefill(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"], s["dt_bias"], s["o"], s["pool"],
-                        s["idx"], s["cu_seqlens"], s["fresh"], scale=w.scale)
+                        s["idx"], s["cu_seqlens"], s["fresh"], scale=w.scale, workspace=s["ws"])
 
     call(sets[0])
     torch.cuda.synchronize()
@@ -278,7 +282,7 @@ def prefill_main(args):
                    "io_dtype": w.io_dtype, "chunk": 16, "launch": "eager" if args.eager else "hip_graph",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": tflops / 2500.0, "traffic": None, "kernel": "gdn_prefill (prefill_kernel)",
+                     "frac": tflops / 2500.0, "traffic": None, "kernel": "gdn_prefill (chunk_kernel + scan_kernel)",
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": us,
                      "hbm_GBps_algorithmic": nbytes / (us * 1e-6) / 1e9},
     }

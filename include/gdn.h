@@ -46,9 +46,9 @@
  * - Host-checkable faults return an error before anything is launched; nothing is
  *   written. A failed launch returns GDN_ERR_LAUNCH.
  * - The library allocates nothing, never synchronises, keeps no global state and
- *   launches exactly one kernel per call on `stream` (a hipStream_t; NULL is the
- *   default stream). Calls are therefore thread-safe and may be captured in a HIP
- *   graph.
+ *   launches its kernels (one per call; two for gdn_prefill) on `stream` (a
+ *   hipStream_t; NULL is the default stream). Calls are therefore thread-safe and may
+ *   be captured in a HIP graph.
  * - Supported geometry: d_k in {16, 32, 64, 128, 256}; d_v a multiple of 16 in
  *   [16, 256]; Hv a multiple of Hk; 1 <= T <= GDN_MAX_T.
  * - Alignment: q, k, v, o, state_pool and inter_cache 16-byte aligned; the others
@@ -59,13 +59,14 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_API __attribute__((visibility("default")))
 #define GDN_MAX_T 16
 
@@ -150,10 +151,28 @@ GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int
  * to the slot. Between tokens the state stays fp32 and is not rounded; a bf16 pool
  * receives the final state rounded to nearest even once. Padding rows get o = 0 and no
  * state access. The chunked form runs on the bf16 matrix cores: io must be bf16, d_k 128,
- * d_v a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise). Valid slots must be distinct. */
+ * d_v a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise). Valid slots must be distinct.
+ *
+ * num_tokens is the length of the packed token axis of q, k, v, a, b and o;
+ * cu_seqlens[B] <= num_tokens is required (not checked: the offsets live on the device),
+ * and num_tokens * Hv * d_v and num_tokens * Hk * d_k must stay below 2^30 elements
+ * (GDN_ERR_UNSUPPORTED otherwise).
+ * The call runs in two kernels: the first prepares, for every 16-token chunk and v-head,
+ * the state-independent products in `workspace` (device memory owned by the caller,
+ * 256-byte aligned, at least gdn_prefill_workspace_bytes(dims, num_tokens) bytes,
+ * GDN_ERR_SHAPE if smaller); the second walks each sequence's chunks in order. The
+ * workspace holds nothing between calls; calls that overlap in time need their own. */
 GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
                                const int32_t* state_indices, const int32_t* cu_seqlens,
-                               const int32_t* fresh, void* stream);
+                               const int32_t* fresh, int64_t num_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace size of gdn_prefill: (floor(num_tokens / 16) + batch) * num_v_heads *
+ * (9472 + 32 * d_v) bytes: one record per chunk and v-head, holding 2 * 4096 bytes of bf16
+ * chunk x d_k operands, 2 * 512 of 16 x 16 bf16 matrices, the per-token factors and
+ * padding, and the chunk's values (16 x d_v bf16). Writes it to *bytes; GDN_ERR_SHAPE for
+ * a negative num_tokens, the gdn_prefill geometry checks otherwise. */
+GDN_API gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens, size_t* bytes);
 
 /* The gated RMS normalisation of the output, fused into verify or decode [P3] (Per-File QA
  * Perspective: the decode-rows GDN kernel carries a gated norm; the dense-FP8 notes name

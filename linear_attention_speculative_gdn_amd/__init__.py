@@ -23,8 +23,9 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
-EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
-            "gdn_conv_update", "gdn_conv_commit", "gdn_status_string", "gdn_abi_version")
+EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_commit",
+            "gdn_verify_replay", "gdn_commit_replay", "gdn_conv_update", "gdn_conv_commit", "gdn_status_string",
+            "gdn_abi_version")
 GDN_CONV_MAX_WIDTH = 8
 GDN_MAX_T = 16
 
@@ -80,15 +81,16 @@ def lib() -> ctypes.CDLL:
         L.gdn_verify.argtypes = [D, I, vp, vp, vp, i32, i32, vp, vp]
         L.gdn_commit.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.gdn_verify_gated.argtypes = [D, I, ctypes.POINTER(GdnOutGate), vp, vp, vp, i32, i32, vp, vp]
-        L.gdn_prefill.argtypes = [D, I, vp, vp, vp, vp, vp]
+        L.gdn_prefill.argtypes = [D, I, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_size_t, vp]
+        L.gdn_prefill_workspace_bytes.argtypes = [D, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
         TK = ctypes.POINTER(GdnTokens)
         L.gdn_verify_replay.argtypes = [D, I, vp, vp, TK, vp, i32, vp]
         L.gdn_commit_replay.argtypes = [D, vp, vp, vp, vp, TK, vp, vp]
         CD = ctypes.POINTER(GdnConvDims)
         L.gdn_conv_update.argtypes = [CD, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp]
         L.gdn_conv_commit.argtypes = [CD, vp, vp, vp, vp, vp]
-        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
-                  "gdn_conv_update", "gdn_conv_commit"):
+        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_prefill_workspace_bytes",
+                  "gdn_commit", "gdn_verify_replay", "gdn_commit_replay", "gdn_conv_update", "gdn_conv_commit"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
@@ -365,10 +367,30 @@ def gdn_conv_commit(x, conv_pool, state_indices, accept_len, *, stream=None) -> 
 # Tokens of all sequences packed along the first axis: q, k [N,Hk,dk], v, o [N,Hv,dv],
 # a, b [N,Hv]; cu_seqlens [B+1] int32 offsets; state_indices, fresh [B] int32.
 
+def _prefill_dims(B, N, Hk, Hv, dk, dv, P, state_dt, io_dt, scale, eps):
+    return GdnDims(B, 1, Hk, Hv, dk, dv, P, state_dt, io_dt, float(dk ** -0.5 if scale is None else scale),
+                   float(eps))
+
+
+def gdn_prefill_workspace_bytes(batch, num_tokens, num_k_heads, num_v_heads, d_k, d_v, state_dtype=torch.float32,
+                                io_dtype=torch.bfloat16) -> int:
+    """Bytes of the device workspace gdn_prefill needs for `batch` sequences with
+    `num_tokens` packed tokens."""
+    dims = _prefill_dims(batch, num_tokens, num_k_heads, num_v_heads, d_k, d_v, 0,
+                         GDN_DTYPE_F32 if state_dtype == torch.float32 else GDN_DTYPE_BF16,
+                         GDN_DTYPE_F32 if io_dtype == torch.float32 else GDN_DTYPE_BF16, None, 1e-6)
+    out = ctypes.c_size_t(0)
+    _raise(lib().gdn_prefill_workspace_bytes(ctypes.byref(dims), int(num_tokens), ctypes.byref(out)),
+           "gdn_prefill_workspace_bytes")
+    return int(out.value)
+
+
 def gdn_prefill(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh=None, *,
-                scale=None, l2norm_eps=1e-6, stream=None) -> None:
+                scale=None, l2norm_eps=1e-6, workspace=None, stream=None) -> None:
     """Prefill of variable-length sequences from pooled initial states (zero where fresh[r]);
-    o for every token, the final state back to each valid slot."""
+    o for every token, the final state back to each valid slot. `workspace` is a device
+    uint8 tensor of at least gdn_prefill_workspace_bytes(...) bytes (allocated per call when
+    omitted); cu_seqlens[-1] must not exceed q.shape[0]."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a HIP device")
@@ -394,10 +416,17 @@ def gdn_prefill(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_
             raise TypeError(f"{n_} must have q's dtype")
     if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
         raise TypeError("A_log and dt_bias must be float32")
-    dims = GdnDims(B, 1, Hk, Hv, dk, dv, state_pool.shape[0], _dt(state_pool), _dt(q),
-                   float(dk ** -0.5 if scale is None else scale), float(l2norm_eps))
+    dims = _prefill_dims(B, N, Hk, Hv, dk, dv, state_pool.shape[0], _dt(state_pool), _dt(q), scale, l2norm_eps)
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        _raise(lib().gdn_prefill_workspace_bytes(ctypes.byref(dims), N, ctypes.byref(need)), "gdn_prefill")
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", 1, dev)
+    if workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
     io = GdnIo(q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
                dt_bias.data_ptr(), o.data_ptr())
     st = lib().gdn_prefill(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
-                           _ptr(cu_seqlens), _ptr(fresh), _stream(dev, stream))
+                           _ptr(cu_seqlens), _ptr(fresh), N, _ptr(workspace), workspace.numel(),
+                           _stream(dev, stream))
     _raise(st, "gdn_prefill")

@@ -11,11 +11,15 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("gdn_kernels.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_api.cpp")]
 
-# gfx950 only. Packed fp32 ops are switched off for every HIP translation unit.
+# gfx950 only. Packed fp32 ops are switched off for every HIP translation unit. Matrix-core
+# results go to ordinary VGPRs (the prefill scan converts and rescales its accumulators
+# every chunk; accumulation registers would add a copy each way); only the prefill uses
+# the matrix cores.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -1,5 +1,6 @@
 // gdn_api.cpp -- the C ABI of include/gdn.h: argument validation, kernel choice and
-// launch. No allocation, no synchronisation, no global state; one launch per call.
+// launch. No allocation, no synchronisation, no global state; one launch per call (two
+// for the prefill).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -129,6 +130,23 @@ gdn::ConvArgs conv_args(const gdn_conv_dims* d) {
   return p;
 }
 
+// Records of the prefill workspace: chunk j of sequence r takes record
+// floor(cu[r] / 16) + j + r, below floor(N / 16) + B for N tokens.
+int64_t prefill_records(const gdn_dims* d, int64_t num_tokens) { return num_tokens / 16 + d->batch; }
+
+gdn_status check_prefill(const gdn_dims* d, int64_t num_tokens) {
+  const gdn_status s = check_dims(d, false);
+  if (s != GDN_OK) return s;
+  if (num_tokens < 0) return GDN_ERR_SHAPE;
+  if (d->io_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;  // the matrix cores take bf16 tokens
+  if (d->d_k != 128 || d->d_v % 32 != 0) return GDN_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside the token tensors
+  if (num_tokens * d->num_v_heads * d->d_v >= (int64_t(1) << 30) ||
+      num_tokens * d->num_k_heads * d->d_k >= (int64_t(1) << 30))
+    return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,25 +178,38 @@ gdn_status gdn_verify_gated(const gdn_dims* dims, const gdn_io* io, const gdn_ou
                        prev_accept_len, stream, gate);
 }
 
-gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool, const int32_t* state_indices,
-                       const int32_t* cu_seqlens, const int32_t* fresh, void* stream) {
-  gdn_status s = check_dims(dims, false);
+
+gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens, size_t* bytes) {
+  const gdn_status s = check_prefill(dims, num_tokens);
   if (s != GDN_OK) return s;
-  if (dims->io_dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;  // the matrix cores take bf16 tokens
-  if (dims->d_k != 128 || dims->d_v % 32 != 0) return GDN_ERR_UNSUPPORTED;
+  if (!bytes) return GDN_ERR_NULL;
+  *bytes = size_t(prefill_records(dims, num_tokens)) * size_t(dims->num_v_heads) *
+           size_t(gdn::prefill_record_bytes(dims->d_v));
+  return GDN_OK;
+}
+
+gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool, const int32_t* state_indices,
+                       const int32_t* cu_seqlens, const int32_t* fresh, int64_t num_tokens, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const gdn_status s = check_prefill(dims, num_tokens);
+  if (s != GDN_OK) return s;
   if (dims->batch == 0) return GDN_OK;
+  const int64_t records = prefill_records(dims, num_tokens);
+  if (workspace_bytes < size_t(records) * size_t(dims->num_v_heads) * size_t(gdn::prefill_record_bytes(dims->d_v)))
+    return GDN_ERR_SHAPE;
   if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
-      !state_pool || !state_indices || !cu_seqlens)
+      !state_pool || !state_indices || !cu_seqlens || !workspace)
     return GDN_ERR_NULL;
   if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->o, 16) ||
       !aligned(state_pool, 16) || !aligned(io->a, 2) || !aligned(io->b, 2) || !aligned(io->A_log, 4) ||
       !aligned(io->dt_bias, 4) || !aligned(state_indices, 4) || !aligned(cu_seqlens, 4) ||
-      (fresh && !aligned(fresh, 4)))
+      (fresh && !aligned(fresh, 4)) || !aligned(workspace, 256))
     return GDN_ERR_ALIGN;
   gdn::PrefillArgs p;
   p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
   p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
   p.pool = state_pool; p.idx = state_indices; p.fresh = fresh; p.cu = cu_seqlens;
+  p.work = workspace; p.records = records; p.rec_bytes = gdn::prefill_record_bytes(dims->d_v);
   p.B = dims->batch; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.DV = dims->d_v;
   p.P = dims->pool_slots; p.G = dims->num_v_heads / dims->num_k_heads;
   p.scale = dims->scale; p.eps = dims->l2norm_eps;

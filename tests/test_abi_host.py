@@ -148,15 +148,40 @@ def test_verify_gated_validation(L):
     assert vg(dims(), i=io(q=None)) == 1
 
 
+def prefill_ws(L, d, n):
+    out = ctypes.c_size_t(0)
+    st = L.gdn_prefill_workspace_bytes(ctypes.byref(d), n, ctypes.byref(out))
+    return st, out.value
+
+
+def test_prefill_workspace_size(L):
+    """One (9472 + 32 d_v)-byte record per (16-token chunk, v-head), floor(N/16) + B chunks."""
+    assert prefill_ws(L, dims(batch=4, num_v_heads=4), 64) == (0, (4 + 4) * 4 * (9472 + 32 * 128))
+    assert prefill_ws(L, dims(batch=3, num_v_heads=32, d_v=64), 16384 + 15) == (0, (1024 + 3) * 32 * (9472 + 2048))
+    assert prefill_ws(L, dims(batch=0), 0) == (0, 0)
+    assert prefill_ws(L, dims(), -1)[0] == 2
+    assert prefill_ws(L, dims(d_k=64), 16)[0] == 5
+    assert prefill_ws(L, dims(io_dtype=gdn.GDN_DTYPE_F32), 16)[0] == 5
+    assert L.gdn_prefill_workspace_bytes(ctypes.byref(dims()), 16, None) == 1
+
+
 def test_prefill_validation(L):
-    def pf(d, i=None, pool=A16 * 9, idx=A16 * 10, cu=A16 * 11, fresh=None):
+    need = prefill_ws(L, dims(), 64)[1]
+
+    def pf(d, i=None, pool=A16 * 9, idx=A16 * 10, cu=A16 * 11, fresh=None, n=64, ws=A16 * 20, wsb=need):
         i = io() if i is None else i
-        return L.gdn_prefill(ctypes.byref(d), ctypes.byref(i), pool, idx, cu, fresh, None)
-    assert pf(dims(batch=0)) == 0
+        return L.gdn_prefill(ctypes.byref(d), ctypes.byref(i), pool, idx, cu, fresh, n, ws, wsb, None)
+    assert pf(dims(batch=0), ws=None, wsb=0) == 0
     assert pf(dims(batch=0, T=0)) == 0                       # T is not used
     assert pf(dims(io_dtype=gdn.GDN_DTYPE_F32)) == 5         # the matrix-core path takes bf16 tokens
     assert pf(dims(batch=0, d_k=64)) == 5
     assert pf(dims(batch=0, d_v=48)) == 5                    # d_v a multiple of 32
+    assert pf(dims(), n=-1) == 2
+    assert pf(dims(), n=1 << 24) == 5                        # 32-bit offsets: N * Hv * d_v < 2^30
+    assert pf(dims(), wsb=need - 1) == 2                     # workspace too small
+    assert pf(dims(), n=80) == 2                             # ... for more tokens
+    assert pf(dims(), ws=None) == 1
+    assert pf(dims(), ws=A16 * 20 + 128) == 4                # 256-byte aligned
     assert pf(dims(), cu=None) == 1
     assert pf(dims(), i=io(v=None)) == 1
     assert pf(dims(), cu=A16 * 11 + 2) == 4

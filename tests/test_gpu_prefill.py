@@ -152,3 +152,51 @@ def test_prefill_unsupported_and_empty():
     gdn.gdn_prefill(q0, q0, v0, ab0, ab0, g["A_log"], g["dt_bias"], v0, pool, torch.empty(0, dtype=torch.int32,
                     device=DEV), torch.zeros(1, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
+
+
+def test_prefill_caller_workspace_reused_and_graph_replay():
+    """A caller-owned workspace serves consecutive calls of different sizes; the two
+    launches of one call replay from a HIP graph like the eager call; a workspace one
+    byte short is refused before anything runs."""
+    w = PrefillWorkload("ws", seqlens=(50, 0, 130, 7), Hk=2, Hv=4, dk=128, dv=64, pool=6, state_dtype="bf16",
+                        io_dtype="bf16", n_fresh=1, n_pad=1)
+    x = workloads.make_prefill_inputs(w, seed=7)
+    need = gdn.gdn_prefill_workspace_bytes(w.batch, w.tokens, w.Hk, w.Hv, w.dk, w.dv, torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "fresh", "cu_seqlens")}
+
+    def call(pool, o, workspace):
+        gdn.gdn_prefill(g["q"], g["k"], g["v"], g["a"], g["b"], g["A_log"], g["dt_bias"], o, pool, g["idx"],
+                        g["cu_seqlens"], g["fresh"], scale=w.scale, workspace=workspace)
+
+    pool_ref = to_device_state(x["pool"]).to(DEV)
+    o_ref = torch.empty((w.tokens, w.Hv, w.dv), dtype=torch.bfloat16, device=DEV)
+    call(pool_ref, o_ref, None)                       # per-call workspace
+    small = PrefillWorkload("ws-small", seqlens=(20,), Hk=2, Hv=4, dk=128, dv=64, pool=6, state_dtype="bf16",
+                            io_dtype="bf16")
+    xs = workloads.make_prefill_inputs(small, seed=8)
+    gs = {n: xs[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "cu_seqlens")}
+    os_ = torch.empty((small.tokens, small.Hv, small.dv), dtype=torch.bfloat16, device=DEV)
+    gdn.gdn_prefill(gs["q"], gs["k"], gs["v"], gs["a"], gs["b"], gs["A_log"], gs["dt_bias"], os_,
+                    to_device_state(xs["pool"]).to(DEV), gs["idx"], gs["cu_seqlens"], workspace=ws)
+    pool = to_device_state(x["pool"]).to(DEV)
+    o = torch.empty_like(o_ref)
+    call(pool, o, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(pool, pool_ref)
+    with pytest.raises(gdn.GdnError) as e:
+        call(pool, o, ws[: need - 1])
+    assert e.value.status == 2
+
+    pool_g = to_device_state(x["pool"]).to(DEV)
+    o_g = torch.empty_like(o_ref)
+    graph, stream = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=stream):
+        call(pool_g, o_g, ws)
+    for rep in range(3):
+        pool_g.copy_(to_device_state(x["pool"]).to(DEV))
+        o_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_ref) and torch.equal(pool_g, pool_ref), rep
