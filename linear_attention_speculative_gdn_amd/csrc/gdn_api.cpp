@@ -183,8 +183,7 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens,
   const gdn_status s = check_prefill(dims, num_tokens);
   if (s != GDN_OK) return s;
   if (!bytes) return GDN_ERR_NULL;
-  *bytes = size_t(prefill_records(dims, num_tokens)) * size_t(dims->num_v_heads) *
-           size_t(gdn::prefill_record_bytes(dims->d_v));
+  *bytes = size_t(prefill_records(dims, num_tokens)) * size_t(dims->num_v_heads) * gdn::kPrefillRecordBytes;
   return GDN_OK;
 }
 
@@ -195,7 +194,7 @@ gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
   if (s != GDN_OK) return s;
   if (dims->batch == 0) return GDN_OK;
   const int64_t records = prefill_records(dims, num_tokens);
-  if (workspace_bytes < size_t(records) * size_t(dims->num_v_heads) * size_t(gdn::prefill_record_bytes(dims->d_v)))
+  if (workspace_bytes < size_t(records) * size_t(dims->num_v_heads) * gdn::kPrefillRecordBytes)
     return GDN_ERR_SHAPE;
   if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
       !state_pool || !state_indices || !cu_seqlens || !workspace)
@@ -209,7 +208,7 @@ gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
   p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
   p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
   p.pool = state_pool; p.idx = state_indices; p.fresh = fresh; p.cu = cu_seqlens;
-  p.work = workspace; p.records = records; p.rec_bytes = gdn::prefill_record_bytes(dims->d_v);
+  p.work = workspace; p.records = records;
   p.B = dims->batch; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.DV = dims->d_v;
   p.P = dims->pool_slots; p.G = dims->num_v_heads / dims->num_k_heads;
   p.scale = dims->scale; p.eps = dims->l2norm_eps;

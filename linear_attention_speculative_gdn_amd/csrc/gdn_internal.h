@@ -81,10 +81,8 @@ struct ConvArgs {
 // commit_only: advance each valid slot over prev_len tokens of prev_x and stop.
 hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t stream);
 
-// Bytes of one (chunk, v-head) record of the prefill workspace: 9472 bytes of key-side
-// operands and factors, then V^T in 16-column blocks (a multiple of 256 for d_v % 32 == 0).
-constexpr int kPrefillRecordFixed = 9472;
-inline int64_t prefill_record_bytes(int dv) { return kPrefillRecordFixed + 32 * int64_t(dv); }
+// Bytes of one (chunk, v-head) record of the prefill workspace (a multiple of 256).
+constexpr int kPrefillRecordBytes = 9472;
 
 // One launch of the chunked prefill (bf16 io, d_k = 128, d_v a multiple of 32).
 struct PrefillArgs {
@@ -100,9 +98,8 @@ struct PrefillArgs {
   const int32_t* idx;          // [B]
   const int32_t* fresh;        // [B] or nullptr
   const int32_t* cu;           // [B+1] token offsets
-  void* work;                  // [records][Hv] records of rec_bytes
+  void* work;                  // [records][Hv] records of kPrefillRecordBytes
   int64_t records;             // floor(N / 16) + B for N tokens
-  int64_t rec_bytes;           // prefill_record_bytes(DV)
   int32_t B, Hk, Hv, DV, P, G;
   float scale, eps;
 };

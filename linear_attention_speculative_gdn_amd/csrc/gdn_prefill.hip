@@ -52,10 +52,8 @@ typedef __bf16 bf16v8 __attribute__((ext_vector_type(8)));
 constexpr int kC = 16;        // tokens per chunk
 constexpr int kDK = 128;      // key dimension
 constexpr int kKT = kDK / 16; // 16-row tiles of the key dimension
-constexpr int kStr = kDK + 8; // LDS row stride (bf16) of 128-wide chunk matrices, padded
-constexpr int kTS = kC + 4;   // LDS row stride (bf16) of the transposed chunk matrices
 
-// Workspace record of one (chunk, v-head): byte offsets (prefill_record_bytes(d_v) in total).
+// Workspace record of one (chunk, v-head): byte offsets (kPrefillRecordBytes in total).
 // Every matrix is stored in the lane layout of the matrix-core operand that reads it, so
 // a pass-2 lane fetches its part with one 8- or 16-byte load.
 constexpr int kRecW = 0;       // -W, A operand of 16x16x32: [32-key block m][lane][8 bf16]
@@ -65,9 +63,7 @@ constexpr int kRecP = 8704;    // P = M o (rq rk) Q K^T, A operand: [lane][4 bf1
 constexpr int kRecF = 9216;    // f_t = rk_t Gam_C / Gam_t [16] fp32
 constexpr int kRecGQ = 9280;   // Gam_t rq_t [16] fp32
 constexpr int kRecGC = 9344;   // Gam_C fp32
-constexpr int kRecV = 9472;    // V, B operand of 16x16x16 by 16-column blocks: [block][lane][4 bf16]
-static_assert(kRecGC + 4 <= kRecV && kRecV == kPrefillRecordFixed && kRecV % 256 == 0, "record layout");
-constexpr int kVSegMax = 8;    // 16-byte value segments per lane and chunk (d_v <= 256)
+static_assert(kRecGC + 4 <= kPrefillRecordBytes && kPrefillRecordBytes % 256 == 0, "record layout");
 
 __device__ __forceinline__ f32x4 mfma(const s16x4& a, const s16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -107,21 +103,33 @@ __device__ __forceinline__ s16x4 ld4(const uint16_t* base, int row, int stride, 
 
 __device__ __forceinline__ int64_t record_id(int32_t cu_r, int row, int j) { return (cu_r >> 4) + j + row; }
 
+// B operand of the 16x16 identity: multiplying an A-layout tile X (lane (row r, group g)
+// holding X[r][4g .. 4g+3]) by it gives X itself in the accumulator layout (lane (g, n)
+// holding X[4g .. 4g+3][n]), i.e. X^T in the A layout: an exact transpose through the
+// matrix core (each sum has a single 1.0 * x term).
+__device__ __forceinline__ s16x4 identity_b(int l16, int l4) {
+  const int e = l16 - 4 * l4;  // the lane's 1.0, if in its four rows
+  return s16x4{short(e == 0 ? 0x3F80 : 0), short(e == 1 ? 0x3F80 : 0), short(e == 2 ? 0x3F80 : 0),
+               short(e == 3 ? 0x3F80 : 0)};
+}
+
+__device__ __forceinline__ s16x4 bf16x4(const f32x4& x) { return bf16x4(x.x, x.y, x.z, x.w); }
+
+__device__ __forceinline__ s16x4 lo4(const s16x8& x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
+__device__ __forceinline__ s16x4 hi4(const s16x8& x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
+
 // ============================================================ pass 1: chunk records
 struct __attribute__((aligned(16))) ChunkLds {
-  uint16_t k[kC * kStr];   // the chunk's keys (stored bf16 values; zero rows past the end)
-  uint16_t q[kC * kStr];   // queries
-  uint16_t w[kC * kStr];   // W, bf16
-  uint16_t kt[kDK * kTS];  // K^T
-  uint16_t tw[kC * kC];    // Tm diag(beta Gam rk), bf16
-  uint16_t tv[kC * kC];    // Tm diag(beta), bf16
-  uint16_t pm[kC * kC];    // P, bf16
   float a[kC * kC];        // A (fp32) for the triangular solve
-  float rk[kC], rq[kC], beta[kC], G[kC];
+  uint16_t tw[kC * kC];    // -Tm diag(beta Gam rk), bf16
+  uint16_t tv[kC * kC];    // Tm diag(beta), bf16
 };
 
 // grid (chunk strides, v-heads, sequences), one wave each; wave x handles chunks x,
-// x + gridDim.x, ... of its sequence.
+// x + gridDim.x, ... of its sequence. Every product takes its operands straight from
+// registers: keys and queries are loaded in the operand layout, K^T comes from the
+// identity product, and W^T = K^T TW^T and (Q K^T)^T = K Q^T come out of the matrix core
+// already in the layout their A operands need. LDS holds only the 16 x 16 solve.
 __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   __shared__ ChunkLds L;
   const int h = blockIdx.y, row = blockIdx.z;
@@ -131,176 +139,129 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
   const int nchunks = (t1 - t0 + kC - 1) / kC;
   const int kh = h / p.G;
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k);
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + size_t(kh) * kDK + 4 * l4;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + size_t(kh) * kDK + 4 * l4;
   const uint16_t* ag = static_cast<const uint16_t*>(p.a);
   const uint16_t* bg = static_cast<const uint16_t*>(p.b);
   const float A_neg = -expf(p.A_log[h]), dtb = p.dt_bias[h];
+  const s16x4 eye = identity_b(l16, l4);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int j = blockIdx.x; j < nchunks; j += gridDim.x) {
     const int64_t rid = record_id(t0, row, j);
     if (rid >= p.records) return;  // workspace too small for the tokens: write nothing
-    char* rec = static_cast<char*>(p.work) + (rid * p.Hv + h) * p.rec_bytes;
+    char* rec = static_cast<char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
     const int cs = t0 + j * kC, n = min(kC, t1 - cs), last = t1 - 1;
-    // the chunk's values, 16-byte segments: segment s = l + 64 i is token s / (d_v / 8),
-    // columns 8 (s % (d_v / 8)) .. + 7 (rows past the end meet zero columns of Tm diag(beta))
-    const int vsegs = p.DV / 8;
-    u32x4 vv[kVSegMax];
-#pragma unroll
-    for (int i = 0; i < kVSegMax; ++i) {
-      const int sgi = min(l + 64 * i, kC * vsegs - 1);
-      vv[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.v) +
-                                              (size_t(min(cs + sgi / vsegs, last)) * p.Hv + h) * p.DV +
-                                              8 * (sgi % vsegs));
-    }
-    // ---- 1. stage k and q rows (256 B each, zero past the end), K^T; gates and the
-    //         inclusive prefix sum of the log-decays (no decay, no write past the end)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int t = it * 4 + l4, seg = l16;
-      const size_t src = (size_t(min(cs + t, last)) * p.Hk + kh) * kDK + 8 * seg;
-      u32x4 kk = *reinterpret_cast<const u32x4*>(kg + src);
-      u32x4 qq = *reinterpret_cast<const u32x4*>(qg + src);
-      if (t >= n) kk = qq = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<uint2*>(L.k + t * kStr + 8 * seg) = uint2{kk.x, kk.y};
-      *reinterpret_cast<uint2*>(L.k + t * kStr + 8 * seg + 4) = uint2{kk.z, kk.w};
-      *reinterpret_cast<uint2*>(L.q + t * kStr + 8 * seg) = uint2{qq.x, qq.y};
-      *reinterpret_cast<uint2*>(L.q + t * kStr + 8 * seg + 4) = uint2{qq.z, qq.w};
-      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        L.kt[(8 * seg + 2 * e) * kTS + t] = uint16_t(kw[e]);
-        L.kt[(8 * seg + 2 * e + 1) * kTS + t] = uint16_t(kw[e] >> 16);
-      }
-    }
+    const bool live = l16 < n;  // token t = l16 of the chunk exists
+    // ---- 1. keys and queries of token l16 in the A layout of 16x16x32 (lane (t, g):
+    //         keys 32m + 4g .. +3 and 32m + 16 + 4g .. +3), zero past the end; gates
+    s16x8 kA[kKT / 2], qA[kKT / 2];
     {
-      const bool live = l16 < n;
-      const size_t tg = size_t(min(cs + l16, last)) * p.Hv + h;
-      const float x = bf(ag[tg]) + dtb;
-      float lg = live ? A_neg * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : 0.f;
-      const float be = live ? 1.f / (1.f + expf(-bf(bg[tg]))) : 0.f;
+      const size_t rowoff = size_t(min(cs + l16, last)) * p.Hk * kDK;
 #pragma unroll
-      for (int d = 1; d < kC; d *= 2) {
-        const float y = __shfl_up(lg, d);
-        if (l16 >= d) lg += y;
-      }
-      if (l < kC) {
-        L.G[l] = lg;
-        L.beta[l] = be;
+      for (int m = 0; m < kKT / 2; ++m) {
+        const s16x4 k0 = *reinterpret_cast<const s16x4*>(kg + rowoff + 32 * m);
+        const s16x4 k1 = *reinterpret_cast<const s16x4*>(kg + rowoff + 32 * m + 16);
+        const s16x4 q0 = *reinterpret_cast<const s16x4*>(qg + rowoff + 32 * m);
+        const s16x4 q1 = *reinterpret_cast<const s16x4*>(qg + rowoff + 32 * m + 16);
+        const s16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        kA[m] = live ? cat8(k0, k1) : z8;
+        qA[m] = live ? cat8(q0, q1) : z8;
       }
     }
-    lds_sync();
-    // ---- 2. inverse L2 norms, 4 lanes per token, 16-byte LDS reads
+    const size_t tg = size_t(min(cs + l16, last)) * p.Hv + h;
+    const float x = bf(ag[tg]) + dtb;
+    float G = live ? A_neg * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : 0.f;  // log-decay
+    const float beta = live ? 1.f / (1.f + expf(-bf(bg[tg]))) : 0.f;
+#pragma unroll
+    for (int d = 1; d < kC; d *= 2) {  // inclusive prefix sum over the 16 tokens (per group)
+      const float y = __shfl_up(G, d, 16);
+      if (l16 >= d) G += y;
+    }
+    // ---- 2. inverse L2 norms of token l16: each group holds 32 of its 128 keys
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kv = bf(uint16_t(kA[m][e])), qv = bf(uint16_t(qA[m][e]));
+        sk = fmaf(kv, kv, sk);
+        sq = fmaf(qv, qv, sq);
+      }
+    sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+    sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+    const float rk = 1.f / sqrtf(sk + p.eps), rq = 1.f / sqrtf(sq + p.eps);
+    // per-token values of the lane's four accumulator rows 4g + i (from group 0's lanes)
+    float Gr[4], br[4], rkr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Gr[i] = __shfl(G, 4 * l4 + i);
+      br[i] = __shfl(beta, 4 * l4 + i);
+      rkr[i] = __shfl(rk, 4 * l4 + i);
+    }
+    // ---- 3. K K^T (rows t = 4g + i, column s = l16) and K Q^T = (Q K^T)^T (rows s,
+    //         column t = l16: the A layout of Q K^T)
+    f32x4 KK = zero4, KQ = zero4;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) {
+      KK = mfma32(kA[m], kA[m], KK);
+      KQ = mfma32(kA[m], qA[m], KQ);
+    }
+    // A_ts = beta_t (Gam_t / Gam_s) rk_t rk_s k_t.k_s (s < t) -> LDS for the solve;
+    // P_ts = (Gam_t / Gam_s) rq_t rk_s q_t.k_s (s <= t) in its A layout (t = l16, s = 4g + i)
+    s16x4 pA;
     {
-      const int t = l >> 2, part = l & 3;
-      float sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int e8 = 0; e8 < 4; ++e8) {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(L.k + t * kStr + 32 * part + 8 * e8);
-        const u32x4 qq = *reinterpret_cast<const u32x4*>(L.q + t * kStr + 32 * part + 8 * e8);
-        float kf[8], qf[8];
-        unpack_io(kk, kf, static_cast<const bf16s*>(nullptr));
-        unpack_io(qq, qf, static_cast<const bf16s*>(nullptr));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sk = fmaf(kf[e], kf[e], sk);
-          sq = fmaf(qf[e], qf[e], sq);
-        }
-      }
-      sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
-      sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
-      if (part == 0) {
-        L.rk[t] = 1.f / sqrtf(sk + p.eps);
-        L.rq[t] = 1.f / sqrtf(sq + p.eps);
-      }
-    }
-    lds_sync();
-    // ---- 3. K K^T and Q K^T (contraction over d_k); A (strict lower) and P (lower)
-    f32x4 KK = {0.f, 0.f, 0.f, 0.f}, QK = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      const s16x4 kA = ld4(L.k, l16, kStr, 16 * kt + 4 * l4);
-      const s16x4 qA = ld4(L.q, l16, kStr, 16 * kt + 4 * l4);
-      KK = mfma(kA, kA, KK);
-      QK = mfma(qA, kA, QK);
-    }
-    {
-      const int s = l16;
-      const float rks = L.rk[s], Gs = L.G[s];
+      float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 4 * l4 + i;
-        const float dec = (s <= t) ? expf(L.G[t] - Gs) : 0.f;
-        L.a[t * kC + s] = (s < t) ? L.beta[t] * L.rk[t] * rks * dec * KK[i] : 0.f;
-        L.pm[t * kC + s] = to_bf(L.rq[t] * rks * dec * QK[i]);
+        const int t = 4 * l4 + i, s_ = l16;
+        L.a[t * kC + s_] = (s_ < t) ? br[i] * rkr[i] * rk * expf(Gr[i] - G) * KK[i] : 0.f;
+        const int sp = 4 * l4 + i, tp = l16;
+        pv[i] = (sp <= tp) ? rq * rkr[i] * expf(G - Gr[i]) * KQ[i] : 0.f;
       }
+      pA = bf16x4(pv[0], pv[1], pv[2], pv[3]);
     }
     lds_sync();
     // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16),
     //         column-oriented: once x[s] is final it updates every later row at once
     if (l < kC) {
       const int c = l;
-      float x[kC];
+      float xs[kC];
 #pragma unroll
-      for (int t = 0; t < kC; ++t) x[t] = (t == c) ? 1.f : 0.f;
+      for (int t = 0; t < kC; ++t) xs[t] = (t == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < kC - 1; ++s)
+      for (int s_ = 0; s_ < kC - 1; ++s_)
 #pragma unroll
-        for (int t = s + 1; t < kC; ++t) x[t] = fmaf(-L.a[t * kC + s], x[s], x[t]);
-      const float cw = -L.beta[c] * expf(L.G[c]) * L.rk[c], cv = L.beta[c];
+        for (int t = s_ + 1; t < kC; ++t) xs[t] = fmaf(-L.a[t * kC + s_], xs[s_], xs[t]);
+      const float cw = -beta * expf(G) * rk, cv = beta;  // lane c holds token c's values
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
-        L.tw[t * kC + c] = to_bf(x[t] * cw);
-        L.tv[t * kC + c] = to_bf(x[t] * cv);
+        L.tw[t * kC + c] = to_bf(xs[t] * cw);
+        L.tv[t * kC + c] = to_bf(xs[t] * cv);
       }
     }
     lds_sync();
-    // ---- 5. -W = -Tm diag(beta Gam rk) K (16 x 128); the K^T operands are the record's
-    {
-      const s16x4 twA = ld4(L.tw, l16, kC, 4 * l4);
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        const s16x4 kB = ld4(L.kt, 16 * kt + l16, kTS, 4 * l4);
-        *reinterpret_cast<s16x4*>(rec + kRecKT + kt * 512 + l * 8) = kB;
-        const f32x4 W = mfma(twA, kB, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) L.w[(4 * l4 + i) * kStr + 16 * kt + l16] = to_bf(W[i]);
-      }
-    }
-    lds_sync();
-    // ---- 6. the rest of the record: -W by 32-key blocks (lane (t, g) holds keys
-    //         32m + 4g .. 4g+3 and 32m + 16 + 4g .. 4g+3 of row t), Tm diag(beta), P, factors
+    const s16x4 twA = ld4(L.tw, l16, kC, 4 * l4), tvA = ld4(L.tv, l16, kC, 4 * l4);
+    // ---- 5. K^T tiles by the identity product (lane (g, key 16kt + l16): tokens 4g ..),
+    //         stored; -W^T = K^T (-TW)^T gives -W in the A layout (lane (t, g): keys
+    //         16kt + 4g ..), stored by 32-key blocks
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) {
-      const s16x4 lo = ld4(L.w, l16, kStr, 32 * m + 4 * l4), hi = ld4(L.w, l16, kStr, 32 * m + 16 + 4 * l4);
-      *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(lo, hi);
+      const s16x4 kt0 = bf16x4(mfma(lo4(kA[m]), eye, zero4));
+      const s16x4 kt1 = bf16x4(mfma(hi4(kA[m]), eye, zero4));
+      *reinterpret_cast<s16x4*>(rec + kRecKT + (2 * m) * 512 + l * 8) = kt0;
+      *reinterpret_cast<s16x4*>(rec + kRecKT + (2 * m + 1) * 512 + l * 8) = kt1;
+      const s16x4 w0 = bf16x4(mfma(kt0, twA, zero4));
+      const s16x4 w1 = bf16x4(mfma(kt1, twA, zero4));
+      *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
     }
-    *reinterpret_cast<s16x4*>(rec + kRecTV + l * 8) = ld4(L.tv, l16, kC, 4 * l4);
-    *reinterpret_cast<s16x4*>(rec + kRecP + l * 8) = ld4(L.pm, l16, kC, 4 * l4);
-    // V^T blocks through the K^T buffer (free after step 5), 128 columns at a time
-    for (int c128 = 0; c128 < p.DV; c128 += kDK) {
-#pragma unroll
-      for (int i = 0; i < kVSegMax; ++i) {
-        const int sgi = l + 64 * i, t = sgi / vsegs, col = 8 * (sgi % vsegs) - c128;
-        if (sgi < kC * vsegs && col >= 0 && col < kDK) {
-          const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            L.kt[(col + 2 * e) * kTS + t] = uint16_t(w4[e]);
-            L.kt[(col + 2 * e + 1) * kTS + t] = uint16_t(w4[e] >> 16);
-          }
-        }
-      }
-      lds_sync();
-      const int nb = min(kDK, p.DV - c128) / 16;
-      for (int b = 0; b < nb; ++b)
-        *reinterpret_cast<s16x4*>(rec + kRecV + (c128 / 16 + b) * 512 + l * 8) = ld4(L.kt, 16 * b + l16, kTS, 4 * l4);
-      lds_sync();
-    }
+    // ---- 6. Tm diag(beta), P, the per-token factors
+    *reinterpret_cast<s16x4*>(rec + kRecTV + l * 8) = tvA;
+    *reinterpret_cast<s16x4*>(rec + kRecP + l * 8) = pA;
+    const float Gl = __shfl(G, kC - 1);
     if (l < kC) {
-      const float Gl = L.G[kC - 1], Gt = L.G[l];
-      reinterpret_cast<float*>(rec + kRecF)[l] = L.rk[l] * expf(Gl - Gt);
-      reinterpret_cast<float*>(rec + kRecGQ)[l] = expf(Gt) * L.rq[l];
+      reinterpret_cast<float*>(rec + kRecF)[l] = rk * expf(Gl - G);
+      reinterpret_cast<float*>(rec + kRecGQ)[l] = expf(G) * rq;
       if (l == 0) *reinterpret_cast<float*>(rec + kRecGC) = expf(Gl);
     }
     lds_sync();  // LDS is reused by the next chunk
@@ -326,12 +287,11 @@ __device__ __forceinline__ void store_state(bf16s* dst, const f32x4& s) {
 
 // Partial products of the KS waves of a workgroup, double-buffered by chunk parity (one
 // barrier per chunk: a wave writes buffer j & 1 only after the barrier of chunk j - 1,
-// which every wave passes after its reads of chunk j - 2), and the output tile.
+// which every wave passes after its reads of chunk j - 2).
 template <int KS>
 struct __attribute__((aligned(16))) ScanLds {
   f32x4 u[2][KS][64];   // U partials: wave 0 holds Tm diag(beta) V - W S_0 over its keys
-  f32x4 qs[2][KS][64];  // Q S_0 partials
-  uint16_t o[kC * 16];  // the chunk's 16 x 16 output tile, bf16
+  f32x4 qs[2][KS][64];  // (Q S_0)^T partials
 };
 
 // One chunk's operands for wave `wk` (keys 128/KS * wk ..), loaded one to two chunks ahead.
@@ -342,9 +302,9 @@ struct ChunkOps {
   s16x8 q[KM];   // Q (stored values), same layout
   s16x4 kt[KT];  // K^T, A layout of 16x16x16
   s16x4 tv, pm;  // Tm diag(beta) and P, A layout
-  s16x4 v;       // V, B layout (tokens 4 l4 .. of column l16)
-  f32x4 f, gq;   // factors of tokens 4 l4 .. 4 l4 + 3
-  float gc;
+  s16x4 v;       // V of token l16, columns 4 l4 .. 4 l4 + 3 (A layout; transposed in use)
+  f32x4 f;       // f of tokens 4 l4 .. 4 l4 + 3
+  float gq, gc;  // gq of token l16; Gam_C
 };
 
 constexpr int kXcds = 8;  // workgroups go to the chip's 8 XCDs round-robin by linear id
@@ -371,6 +331,7 @@ __global__ __launch_bounds__(64 * KS) void scan_kernel(const PrefillArgs p) {
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
   const int kh = h / p.G;
   const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
   uint16_t* og = static_cast<uint16_t*>(p.o);
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
@@ -397,18 +358,21 @@ __global__ __launch_bounds__(64 * KS) void scan_kernel(const PrefillArgs p) {
   // 2^31 elements), so the loads take a scalar base and keep their lane offsets in VGPRs
   // that do not change from chunk to chunk.
   const char* qbase = reinterpret_cast<const char*>(qg + size_t(kh) * kDK + key0);
-  const uint32_t qrow_b = uint32_t(p.Hk) * kDK * 2u;
+  const char* vbase = reinterpret_cast<const char*>(vg + size_t(h) * p.DV + c0);
+  const uint32_t qrow_b = uint32_t(p.Hk) * kDK * 2u, vrow_b = uint32_t(p.Hv) * uint32_t(p.DV) * 2u;
   const uint32_t o_w = uint32_t(kRecW + wk * KM * 1024 + l * 16), o_kt = uint32_t(kRecKT + wk * KT * 512 + l * 8);
-  const uint32_t o_ab = uint32_t(l * 8), o_fg = uint32_t(16 * l4), o_v = uint32_t(kRecV + cb * 512 + l * 8);
+  const uint32_t o_ab = uint32_t(l * 8), o_f = uint32_t(kRecF + 16 * l4), o_gq = uint32_t(kRecGQ + 4 * l16);
+  const s16x4 eye = identity_b(l16, l4);
   // Every load is unconditional: the record index and the tokens are clamped into range
   // (a load in a branch is waited on at the branch end). Operands of tokens past the end
   // meet zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
   auto fetch = [&](int j) -> ChunkOps<KS> {
     ChunkOps<KS> c;
     const int64_t rid = min(rid0 + j, p.records - 1);
-    const char* rec = static_cast<const char*>(p.work) + (rid * p.Hv + h) * p.rec_bytes;
+    const char* rec = static_cast<const char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
     const int cs = t0 + j * kC;
-    const uint32_t oq = uint32_t(min(cs + l16, last)) * qrow_b + 8u * l4;
+    const uint32_t tok = uint32_t(min(cs + l16, last));
+    const uint32_t oq = tok * qrow_b + 8u * l4;
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
       c.w[m] = *reinterpret_cast<const s16x8*>(rec + o_w + m * 1024);
@@ -419,24 +383,26 @@ __global__ __launch_bounds__(64 * KS) void scan_kernel(const PrefillArgs p) {
     for (int kt = 0; kt < KT; ++kt) c.kt[kt] = *reinterpret_cast<const s16x4*>(rec + o_kt + kt * 512);
     c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTV + o_ab);
     c.pm = *reinterpret_cast<const s16x4*>(rec + kRecP + o_ab);
-    c.f = *reinterpret_cast<const f32x4*>(rec + kRecF + o_fg);
-    c.gq = *reinterpret_cast<const f32x4*>(rec + kRecGQ + o_fg);
+    c.f = *reinterpret_cast<const f32x4*>(rec + o_f);
+    c.gq = *reinterpret_cast<const float*>(rec + o_gq);
     c.gc = *reinterpret_cast<const float*>(rec + kRecGC);
-    c.v = *reinterpret_cast<const s16x4*>(rec + o_v);
+    c.v = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4);
     return c;
   };
 
   auto step = [&](const ChunkOps<KS>& c, int j) {
     const int cs = t0 + j * kC, n = min(kC, t1 - cs), buf = j & 1;
-    // ---- U partial = [wave 0: Tm diag(beta) V] - W S_0 and Q S_0 over the wave's keys
-    f32x4 u = (wk == 0) ? mfma(c.tv, c.v, f32x4{0.f, 0.f, 0.f, 0.f}) : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+    // ---- U partial = [wave 0: Tm diag(beta) V] - W S_0, and (Q S_0)^T = S_0^T Q^T, over
+    //      the wave's keys. V enters transposed by the identity product (V rows are loaded
+    //      whole); the bf16 state serves as B of W S_0 and, unchanged, as A of S_0^T Q^T.
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 u = (wk == 0) ? mfma(c.tv, bf16x4(mfma(c.v, eye, zero4)), zero4) : zero4;
+    f32x4 qs = zero4;
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
-      const f32x4 a = S[2 * m], b = S[2 * m + 1];
-      const s16x8 sB = cat8(bf16x4(a.x, a.y, a.z, a.w), bf16x4(b.x, b.y, b.z, b.w));
+      const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
       u = mfma32(c.w[m], sB, u);
-      qs = mfma32(c.q[m], sB, qs);
+      qs = mfma32(sB, c.q[m], qs);
     }
     if constexpr (KS > 1) {  // sum the partials in wave order (every wave gets the same U)
       L.u[buf][wk][l] = u;
@@ -451,18 +417,16 @@ __global__ __launch_bounds__(64 * KS) void scan_kernel(const PrefillArgs p) {
         for (int w = 1; w < KS; ++w) qs += L.qs[buf][w][l];
       }
     }
-    // ---- O = scale (diag(Gam rq) Q S_0 + P U), by the last wave, 16-byte stores from LDS
+    // ---- O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T), by the last wave: lane (g, t)
+    //      holds columns 4g .. 4g+3 of token t's output, one 8-byte store
     if (wk == KS - 1) {
-      const f32x4 pu = mfma(c.pm, bf16x4(u.x, u.y, u.z, u.w), f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 pu = mfma(bf16x4(u), c.pm, zero4);
+      float ov[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) L.o[(4 * l4 + i) * 16 + l16] = to_bf(p.scale * (c.gq[i] * qs[i] + pu[i]));
-      lds_sync();
-      if (l < 2 * kC) {
-        const int t = l >> 1, half = l & 1;
-        const u32x4 ov = *reinterpret_cast<const u32x4*>(L.o + t * 16 + 8 * half);
-        if (t < n) *reinterpret_cast<u32x4*>(og + (size_t(cs + t) * p.Hv + h) * p.DV + c0 + 8 * half) = ov;
-      }
-      lds_sync();
+      for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
+      if (l16 < n)
+        *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + h) * p.DV + c0 + 4 * l4) =
+            uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
     }
     // ---- S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U over the wave's keys
     const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
