@@ -167,8 +167,8 @@ GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* sta
                                const int32_t* fresh, int64_t num_tokens, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Workspace size of gdn_prefill: (floor(num_tokens / 16) + batch) * num_v_heads * 9472
- * bytes: one record per chunk and v-head, holding 2 * 4096 bytes of bf16 chunk x d_k
+/* Workspace size of gdn_prefill: (floor(num_tokens / 16) + batch) * num_v_heads * 13568
+ * bytes: one record per chunk and v-head, holding 3 * 4096 bytes of bf16 chunk x d_k
  * operands, 2 * 512 of 16 x 16 bf16 matrices, the per-token factors and padding. Writes it
  * to *bytes; GDN_ERR_SHAPE for a negative num_tokens, the gdn_prefill geometry checks
  * otherwise. */

@@ -82,7 +82,7 @@ struct ConvArgs {
 hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t stream);
 
 // Bytes of one (chunk, v-head) record of the prefill workspace (a multiple of 256).
-constexpr int kPrefillRecordBytes = 9472;
+constexpr int kPrefillRecordBytes = 13568;
 
 // One launch of the chunked prefill (bf16 io, d_k = 128, d_v a multiple of 32).
 struct PrefillArgs {

@@ -55,14 +55,14 @@ constexpr int kKT = kDK / 16; // 16-row tiles of the key dimension
 
 // Workspace record of one (chunk, v-head): byte offsets (kPrefillRecordBytes in total).
 // Every matrix is stored in the lane layout of the matrix-core operand that reads it, so
-// a pass-2 lane fetches its part with one 8- or 16-byte load.
+// a pass-2 lane fetches its part with 16-byte loads of contiguous 1 KiB blocks.
 constexpr int kRecW = 0;       // -W, A operand of 16x16x32: [32-key block m][lane][8 bf16]
-constexpr int kRecKT = 4096;   // K^T, A operand of 16x16x16: [16-key tile][lane][4 bf16]
-constexpr int kRecTV = 8192;   // Tm diag(beta), A operand: [lane][4 bf16]
-constexpr int kRecP = 8704;    // P = M o (rq rk) Q K^T, A operand: [lane][4 bf16]
-constexpr int kRecF = 9216;    // f_t = rk_t Gam_C / Gam_t [16] fp32
-constexpr int kRecGQ = 9280;   // Gam_t rq_t [16] fp32
-constexpr int kRecGC = 9344;   // Gam_C fp32
+constexpr int kRecQ = 4096;    // Q (stored values), same layout
+constexpr int kRecKT = 8192;   // K^T, A operand of 16x16x16, tiles 2m, 2m+1: [m][lane][2 x 4 bf16]
+constexpr int kRecTP = 12288;  // Tm diag(beta) and P = M o (rq rk) Q K^T, A operands: [lane][2 x 4 bf16]
+constexpr int kRecF = 13312;   // f_t = rk_t Gam_C / Gam_t [16] fp32
+constexpr int kRecGQ = 13376;  // Gam_t rq_t [16] fp32
+constexpr int kRecGC = 13440;  // Gam_C fp32
 static_assert(kRecGC + 4 <= kPrefillRecordBytes && kPrefillRecordBytes % 256 == 0, "record layout");
 
 __device__ __forceinline__ f32x4 mfma(const s16x4& a, const s16x4& b, const f32x4& c) {
@@ -249,15 +249,14 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     for (int m = 0; m < kKT / 2; ++m) {
       const s16x4 kt0 = bf16x4(mfma(lo4(kA[m]), eye, zero4));
       const s16x4 kt1 = bf16x4(mfma(hi4(kA[m]), eye, zero4));
-      *reinterpret_cast<s16x4*>(rec + kRecKT + (2 * m) * 512 + l * 8) = kt0;
-      *reinterpret_cast<s16x4*>(rec + kRecKT + (2 * m + 1) * 512 + l * 8) = kt1;
+      *reinterpret_cast<s16x8*>(rec + kRecKT + m * 1024 + l * 16) = cat8(kt0, kt1);
       const s16x4 w0 = bf16x4(mfma(kt0, twA, zero4));
       const s16x4 w1 = bf16x4(mfma(kt1, twA, zero4));
       *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
+      *reinterpret_cast<s16x8*>(rec + kRecQ + m * 1024 + l * 16) = qA[m];  // zero past the end
     }
-    // ---- 6. Tm diag(beta), P, the per-token factors
-    *reinterpret_cast<s16x4*>(rec + kRecTV + l * 8) = tvA;
-    *reinterpret_cast<s16x4*>(rec + kRecP + l * 8) = pA;
+    // ---- 6. Tm diag(beta) and P, the per-token factors
+    *reinterpret_cast<s16x8*>(rec + kRecTP + l * 16) = cat8(tvA, pA);
     const float Gl = __shfl(G, kC - 1);
     if (l < kC) {
       reinterpret_cast<float*>(rec + kRecF)[l] = rk * expf(Gl - G);
@@ -285,224 +284,220 @@ __device__ __forceinline__ void store_state(bf16s* dst, const f32x4& s) {
   *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
 }
 
-// Partial products of the KS waves of a workgroup, double-buffered by chunk parity (one
-// barrier per chunk: a wave writes buffer j & 1 only after the barrier of chunk j - 1,
-// which every wave passes after its reads of chunk j - 2).
-template <int KS>
+// What the state wave hands to the output wave per chunk, double-buffered by chunk parity:
+// one barrier per chunk suffices, since a wave writes buffer j & 1 only after the barrier
+// of chunk j - 1, which the output wave reaches after its reads of chunk j - 2 completed.
 struct __attribute__((aligned(16))) ScanLds {
-  f32x4 u[2][KS][64];   // U partials: wave 0 holds Tm diag(beta) V - W S_0 over its keys
-  f32x4 qs[2][KS][64];  // (Q S_0)^T partials
+  s16x8 s[2][kKT / 2][64];  // bf16 S_0 in the B layout of 16x16x32, by 32-key block
+  s16x4 u[2][64];           // bf16 U in the accumulator layout
 };
 
-// One chunk's operands for wave `wk` (keys 128/KS * wk ..), loaded one to two chunks ahead.
-template <int KS>
-struct ChunkOps {
-  static constexpr int KT = kKT / KS, KM = KT / 2;
-  s16x8 w[KM];   // -W, A layout of 16x16x32
-  s16x8 q[KM];   // Q (stored values), same layout
-  s16x4 kt[KT];  // K^T, A layout of 16x16x16
-  s16x4 tv, pm;  // Tm diag(beta) and P, A layout
-  s16x4 v;       // V of token l16, columns 4 l4 .. 4 l4 + 3 (A layout; transposed in use)
-  f32x4 f;       // f of tokens 4 l4 .. 4 l4 + 3
-  float gq, gc;  // gq of token l16; Gam_C
+// Operands of one chunk, loaded two chunks ahead: the state wave's and the output wave's.
+struct StateOps {
+  s16x8 w[kKT / 2];   // -W, A layout of 16x16x32
+  s16x8 kt[kKT / 2];  // K^T tiles 2m, 2m+1, A layout of 16x16x16
+  s16x4 tv;           // Tm diag(beta), A layout
+  s16x4 v;            // V of token l16, columns 4 l4 .. 4 l4 + 3 (A layout; transposed in use)
+  f32x4 f;            // f of tokens 4 l4 .. 4 l4 + 3
+  float gc;           // Gam_C
+};
+struct OutOps {
+  s16x8 q[kKT / 2];   // Q (stored values), A layout of 16x16x32
+  s16x4 pm;           // P, A layout
+  float gq;           // Gam_t rq_t of token l16
 };
 
 constexpr int kXcds = 8;  // workgroups go to the chip's 8 XCDs round-robin by linear id
 
-// One workgroup per (sequence, v-head, block of 16 value columns); KS waves per workgroup
-// split the key dimension: wave wk holds S rows 128/KS * wk .. as 16-key tiles. io is bf16.
+// Keeps a chunk's loads after the step that frees their registers: the empty asm takes
+// the given values (so the step's last products are done) and clobbers memory (so no
+// load moves above it). Hoisted above the step, the loads would need fresh registers and
+// copies at the loop's back edge, and a copy waits for its load.
+template <typename T>
+__device__ __forceinline__ void keep_after(T& x) {
+  asm volatile("" : "+v"(x)::"memory");
+}
+
+// Runs chunks 0 .. n-1 through step(ops, j) with the operands of chunk j + 2 loading while
+// chunk j computes: pairs of chunks with no exit inside a pair (nothing sinks into the
+// next one), then an odd last chunk alone; each operand set keeps its registers (no copies
+// between them), and nothing is in flight at the loop's start (the wait counts inside
+// the loop then follow from its own loads alone).
+template <typename Ops, typename Fetch, typename Step, typename After>
+__device__ __forceinline__ void run_chunks(int n, Fetch fetch, Step step, After after) {
+  if (n <= 0) return;
+  Ops c0 = fetch(0), c1 = fetch(1);
+  __builtin_amdgcn_s_waitcnt(0);
+  int j = 0;
+  for (; j + 1 < n; j += 2) {
+    step(c0, j);
+    after();
+    c0 = fetch(j + 2);
+    step(c1, j + 1);
+    after();
+    c1 = fetch(j + 3);
+  }
+  if (j < n) step(c0, j);
+}
+
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One workgroup of two waves per (sequence, v-head, block of 16 value columns). io is
+// bf16. Wave 0 carries the state chain: U = Tm diag(beta) V - W S_0 and the update; it
+// hands bf16 S_0 and U to wave 1, which computes the outputs (Q S_0, P U) one chunk
+// behind, so the chain never waits for them.
 // 1-D grid, XCD-aware: the column blocks of a (sequence, v-head) read the same records,
 // so they are given ids on one XCD (id % 8 equal) and share its L2. Head unit u (=
 // row * Hv + h) and column block cb take id (u % 8) + 8 (cb + nb (u / 8)).
-template <typename ST, int KS>
-__global__ __launch_bounds__(64 * KS) void scan_kernel(const PrefillArgs p) {
-  constexpr int KT = kKT / KS, KM = KT / 2;
-  static_assert(KM >= 1, "at least one 32-key block per wave");
-  __shared__ ScanLds<KS> L;
+template <typename ST>
+__global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
+  __shared__ ScanLds L;
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
-  const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = p.DV / 16;
   const int rest = int(blockIdx.x) / kXcds, cb = rest % nb;
-  const int u = (rest / nb) * kXcds + int(blockIdx.x) % kXcds;
-  if (u >= p.B * p.Hv) return;  // the padding of the last group of 8 head units
-  const int c0 = cb * 16, h = u % p.Hv, row = u / p.Hv;
+  const int unit = (rest / nb) * kXcds + int(blockIdx.x) % kXcds;
+  if (unit >= p.B * p.Hv) return;  // the padding of the last group of 8 head units
+  const int c0 = cb * 16, h = unit % p.Hv, row = unit / p.Hv;
   const int32_t slot = p.idx[row];
-  const int32_t fresh = p.fresh ? p.fresh[row] : 0;
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
-  const int kh = h / p.G;
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v);
   uint16_t* og = static_cast<uint16_t*>(p.o);
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
-    for (int t = t0 + wk * 32 + (l >> 1); t < t1; t += 32 * KS)
+    for (int t = t0 + wave * 32 + (l >> 1); t < t1; t += 64)
       *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + c0 + 8 * (l & 1)) = u32x4{0u, 0u, 0u, 0u};
     return;
-  }
-
-  // the state: tile kt of lane l holds S[key0 + 16kt + 4 l4 + i][c0 + l16]
-  const int key0 = wk * (kDK / KS);
-  ST* const pool_tile = static_cast<ST*>(p.pool) + (size_t(slot) * p.Hv + h) * size_t(p.DV) * kDK;
-  ST* const my_state = pool_tile + size_t(c0 + l16) * kDK + key0 + 4 * l4;
-  f32x4 S[KT];
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
-    S[kt] = fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : s;
   }
 
   const int nchunks = (t1 - t0 + kC - 1) / kC;
   const int64_t rid0 = record_id(t0, row, 0);
   const int last = max(t1 - 1, 0);
-  // Uniform bases and 32-bit lane byte offsets (the host bounds every token tensor below
-  // 2^31 elements), so the loads take a scalar base and keep their lane offsets in VGPRs
-  // that do not change from chunk to chunk.
-  const char* qbase = reinterpret_cast<const char*>(qg + size_t(kh) * kDK + key0);
-  const char* vbase = reinterpret_cast<const char*>(vg + size_t(h) * p.DV + c0);
-  const uint32_t qrow_b = uint32_t(p.Hk) * kDK * 2u, vrow_b = uint32_t(p.Hv) * uint32_t(p.DV) * 2u;
-  const uint32_t o_w = uint32_t(kRecW + wk * KM * 1024 + l * 16), o_kt = uint32_t(kRecKT + wk * KT * 512 + l * 8);
-  const uint32_t o_ab = uint32_t(l * 8), o_f = uint32_t(kRecF + 16 * l4), o_gq = uint32_t(kRecGQ + 4 * l16);
-  const s16x4 eye = identity_b(l16, l4);
+  // chunks with a record (all of them unless the workspace is too small for the tokens)
+  const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - rid0)));
   // Every load is unconditional: the record index and the tokens are clamped into range
   // (a load in a branch is waited on at the branch end). Operands of tokens past the end
   // meet zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
-  auto fetch = [&](int j) -> ChunkOps<KS> {
-    ChunkOps<KS> c;
+  // Uniform bases and 32-bit lane offsets (the host bounds the token tensors below 2^30
+  // elements) keep the lane offsets in VGPRs that do not change from chunk to chunk.
+  auto record = [&](int j) {
     const int64_t rid = min(rid0 + j, p.records - 1);
-    const char* rec = static_cast<const char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
-    const int cs = t0 + j * kC;
-    const uint32_t tok = uint32_t(min(cs + l16, last));
-    const uint32_t oq = tok * qrow_b + 8u * l4;
-#pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      c.w[m] = *reinterpret_cast<const s16x8*>(rec + o_w + m * 1024);
-      c.q[m] = cat8(*reinterpret_cast<const s16x4*>(qbase + oq + 64 * m),
-                    *reinterpret_cast<const s16x4*>(qbase + oq + 64 * m + 32));
-    }
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) c.kt[kt] = *reinterpret_cast<const s16x4*>(rec + o_kt + kt * 512);
-    c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTV + o_ab);
-    c.pm = *reinterpret_cast<const s16x4*>(rec + kRecP + o_ab);
-    c.f = *reinterpret_cast<const f32x4*>(rec + o_f);
-    c.gq = *reinterpret_cast<const float*>(rec + o_gq);
-    c.gc = *reinterpret_cast<const float*>(rec + kRecGC);
-    c.v = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4);
-    return c;
+    return static_cast<const char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
   };
+  const uint32_t o_l = uint32_t(l * 16);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const ChunkOps<KS>& c, int j) {
-    const int cs = t0 + j * kC, n = min(kC, t1 - cs), buf = j & 1;
-    // ---- U partial = [wave 0: Tm diag(beta) V] - W S_0, and (Q S_0)^T = S_0^T Q^T, over
-    //      the wave's keys. V enters transposed by the identity product (V rows are loaded
-    //      whole); the bf16 state serves as B of W S_0 and, unchanged, as A of S_0^T Q^T.
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 u = (wk == 0) ? mfma(c.tv, bf16x4(mfma(c.v, eye, zero4)), zero4) : zero4;
-    f32x4 qs = zero4;
+  if (wave == 0) {
+    // ---- the state chain. Tile kt of lane l holds S[16kt + 4 l4 + i][c0 + l16].
+    ST* const my_state =
+        static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + c0 + l16) * kDK + 4 * l4;
+    const int32_t fresh = p.fresh ? p.fresh[row] : 0;
+    f32x4 S[kKT];
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
-      u = mfma32(c.w[m], sB, u);
-      qs = mfma32(sB, c.q[m], qs);
+    for (int kt = 0; kt < kKT; ++kt) {
+      const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
+      S[kt] = fresh ? zero4 : s;
     }
-    if constexpr (KS > 1) {  // sum the partials in wave order (every wave gets the same U)
-      L.u[buf][wk][l] = u;
-      L.qs[buf][wk][l] = qs;
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      u = L.u[buf][0][l];
+    const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV + c0);
+    const uint32_t vrow_b = uint32_t(p.Hv) * uint32_t(p.DV) * 2u;
+    const uint32_t o_f = uint32_t(kRecF + 16 * l4);
+    const s16x4 eye = identity_b(l16, l4);
+    auto fetch = [&](int j) -> StateOps {
+      StateOps c;
+      const char* rec = record(j);
 #pragma unroll
-      for (int w = 1; w < KS; ++w) u += L.u[buf][w][l];
-      if (wk == KS - 1) {
-        qs = L.qs[buf][0][l];
-#pragma unroll
-        for (int w = 1; w < KS; ++w) qs += L.qs[buf][w][l];
+      for (int m = 0; m < kKT / 2; ++m) {
+        c.w[m] = *reinterpret_cast<const s16x8*>(rec + kRecW + m * 1024 + o_l);
+        c.kt[m] = *reinterpret_cast<const s16x8*>(rec + kRecKT + m * 1024 + o_l);
       }
-    }
-    // ---- O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T), by the last wave: lane (g, t)
-    //      holds columns 4g .. 4g+3 of token t's output, one 8-byte store
-    if (wk == KS - 1) {
-      const f32x4 pu = mfma(bf16x4(u), c.pm, zero4);
+      c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l);  // the lower half
+      c.f = *reinterpret_cast<const f32x4*>(rec + o_f);
+      c.gc = *reinterpret_cast<const float*>(rec + kRecGC);
+      const uint32_t tok = uint32_t(min(t0 + j * kC + l16, last));
+      c.v = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4);
+      return c;
+    };
+    auto step = [&](const StateOps& c, int j) {
+      const int buf = j & 1;
+      // U = Tm diag(beta) V - W S_0 (V transposed by the identity product). The asm pins
+      // the state-independent products to this step: hoisted to the loop's start, they
+      // would wait for loads issued just before.
+      s16x4 v = c.v, tv = c.tv;
+      asm volatile("" : "+v"(v), "+v"(tv));
+      f32x4 u = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) {
+        const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
+        L.s[buf][m][l] = sB;
+        u = mfma32(c.w[m], sB, u);
+      }
+      L.u[buf][l] = bf16x4(u);
+      barrier_lds();
+      // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
+      const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt)
+        S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
+    };
+    auto after = [&]() {
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) keep_after(S[kt]);
+    };
+    run_chunks<StateOps>(nrun, fetch, step, after);
+    // the final state back to the slot (rounded once for a bf16 pool)
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+  } else {
+    // ---- the outputs: O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T) with
+    //      (Q S_0)^T = S_0^T Q^T: lane (g, t) holds columns 4g .. 4g+3 of token t
+    const uint32_t o_gq = uint32_t(kRecGQ + 4 * l16);
+    auto fetch = [&](int j) -> OutOps {
+      OutOps c;
+      const char* rec = record(j);
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(rec + kRecQ + m * 1024 + o_l);
+      c.pm = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l + 8);  // the upper half
+      c.gq = *reinterpret_cast<const float*>(rec + o_gq);
+      return c;
+    };
+    auto step = [&](const OutOps& c, int j) {
+      const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
+      barrier_lds();  // chunk j's S_0 and U are in buffer j & 1
+      f32x4 qs = zero4;
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(L.s[buf][m][l], c.q[m], qs);
+      const f32x4 pu = mfma(L.u[buf][l], c.pm, zero4);
       float ov[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
       if (l16 < n)
         *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + h) * p.DV + c0 + 4 * l4) =
             uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-    }
-    // ---- S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U over the wave's keys
-    const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) S[kt] = mfma(c.kt[kt], uB, S[kt] * c.gc);
-  };
-
-  // two chunks in flight: the operands of chunk j + 2 load while chunk j computes. The
-  // loads are kept after the step that frees their registers: the empty asm takes the
-  // updated state (so the step's last products are done) and clobbers memory (so no load
-  // moves above it). Hoisted above the step, the loads would need fresh registers and
-  // copies at the loop's back edge, and a copy waits for its load.
-  auto fence = [&]() {
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) asm volatile("" : "+v"(S[kt])::"memory");
-  };
-  // chunks with a record (all of them unless the workspace is too small for the tokens)
-  const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - rid0)));
-  if (nrun > 0) {
-    ChunkOps<KS> c0p = fetch(0), c1p = fetch(1);
-    int j = 0;
-    if (nrun & 1) {  // an odd count: the first chunk alone, then pairs
-      step(c0p, 0);
-      c0p = c1p;
-      c1p = fetch(2);
-      j = 1;
-    }
-    // Start the loop with nothing in flight (the first step needs its operands anyway):
-    // the wait counts inside the loop then follow from its own loads alone.
-    __builtin_amdgcn_s_waitcnt(0);
-    for (; j < nrun; j += 2) {  // no exit inside the pair: nothing sinks into the next one
-      step(c0p, j);
-      fence();
-      c0p = fetch(j + 2);
-      step(c1p, j + 1);
-      fence();
-      c1p = fetch(j + 3);
-    }
+    };
+    // the step ends in its store, so a memory clobber keeps the next loads after it
+    auto after = [&]() { asm volatile("" ::: "memory"); };
+    run_chunks<OutOps>(nrun, fetch, step, after);
   }
-
-  // ---- the final state back to the slot (rounded once for a bf16 pool)
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) store_state(my_state + 16 * kt, S[kt]);
 }
 
-template <typename ST, int KS>
+template <typename ST>
 hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (int64_t(p.B) * p.Hv + kXcds - 1) / kXcds * kXcds;
   const dim3 grid(unsigned(units * (p.DV / 16)));
-  hipLaunchKernelGGL((scan_kernel<ST, KS>), grid, dim3(64 * KS), 0, stream, p);
+  hipLaunchKernelGGL((scan_kernel<ST>), grid, dim3(128), 0, stream, p);
   return hipGetLastError();
-}
-
-// One wave per 16 value columns measured fastest down to 512 such tiles (half a wave per
-// SIMD), the key split's partial sums costing more than its shorter chain saves; the split
-// is kept for grids too small to give every SIMD work.
-template <typename ST>
-hipError_t launch_scan_split(const PrefillArgs& p, hipStream_t stream) {
-  const int64_t tiles = int64_t(p.B) * p.Hv * (p.DV / 16);
-  if (tiles >= 256) return launch_scan<ST, 1>(p, stream);
-  if (tiles >= 128) return launch_scan<ST, 2>(p, stream);
-  return launch_scan<ST, 4>(p, stream);
 }
 
 }  // namespace
 
 // Pass 1 gets enough waves to fill the chip whatever the batch: each (sequence, v-head)
-// gets `strides` waves that share its chunks. Pass 2 splits the key dimension over 2 or 4
-// waves only when one wave per 16 value columns would leave most SIMDs idle.
+// gets `strides` waves that share its chunks.
 hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
   const int64_t heads = int64_t(p.B) * p.Hv;
   const unsigned strides = unsigned(std::min<int64_t>(1024, std::max<int64_t>(1, (4096 + heads - 1) / heads)));
   hipLaunchKernelGGL(chunk_kernel, dim3(strides, unsigned(p.Hv), unsigned(p.B)), dim3(64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return state == Dt::F32 ? launch_scan_split<float>(p, stream) : launch_scan_split<bf16s>(p, stream);
+  return state == Dt::F32 ? launch_scan<float>(p, stream) : launch_scan<bf16s>(p, stream);
 }
 
 }  // namespace gdn
