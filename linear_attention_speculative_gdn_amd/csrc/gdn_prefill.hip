@@ -423,13 +423,22 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
       // would wait for loads issued just before.
       s16x4 v = c.v, tv = c.tv;
       asm volatile("" : "+v"(v), "+v"(tv));
-      f32x4 u = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+      const f32x4 tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+      // -W S_0 in two interleaved accumulators (half the dependent chain). The 16x16x16
+      // product above joins them through a vector add, not as an accumulator: a 16x16x32
+      // product reading the result of a 16x16x16 one needs five wait states, and the
+      // compiler does not always place them.
+      f32x4 u0 = zero4, u1 = zero4;
 #pragma unroll
       for (int m = 0; m < kKT / 2; ++m) {
         const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
         L.s[buf][m][l] = sB;
-        u = mfma32(c.w[m], sB, u);
+        if (m & 1)
+          u1 = mfma32(c.w[m], sB, u1);
+        else
+          u0 = mfma32(c.w[m], sB, u0);
       }
+      const f32x4 u = (u0 + u1) + tvv;
       L.u[buf][l] = bf16x4(u);
       barrier_lds();
       // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
@@ -462,10 +471,17 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
     auto step = [&](const OutOps& c, int j) {
       const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
       barrier_lds();  // chunk j's S_0 and U are in buffer j & 1
+      // Every operand read from LDS gets its own registers and has arrived before the
+      // first product: no LDS return lands in a register a pending product still reads.
+      s16x8 sA[kKT / 2];
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) sA[m] = L.s[buf][m][l];
+      s16x4 uA = L.u[buf][l];
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA));
       f32x4 qs = zero4;
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(L.s[buf][m][l], c.q[m], qs);
-      const f32x4 pu = mfma(L.u[buf][l], c.pm, zero4);
+      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], c.q[m], qs);
+      const f32x4 pu = mfma(uA, c.pm, zero4);
       float ov[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
@@ -493,7 +509,7 @@ hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
 // gets `strides` waves that share its chunks.
 hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
   const int64_t heads = int64_t(p.B) * p.Hv;
-  const unsigned strides = unsigned(std::min<int64_t>(1024, std::max<int64_t>(1, (4096 + heads - 1) / heads)));
+  const unsigned strides = unsigned(std::min<int64_t>(1024, std::max<int64_t>(1, (8192 + heads - 1) / heads)));
   hipLaunchKernelGGL(chunk_kernel, dim3(strides, unsigned(p.Hv), unsigned(p.B)), dim3(64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
