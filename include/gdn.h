@@ -167,11 +167,12 @@ GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* sta
                                const int32_t* fresh, int64_t num_tokens, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Workspace size of gdn_prefill: (floor(num_tokens / 16) + batch) * num_v_heads * 13568
- * bytes: one record per chunk and v-head, holding 3 * 4096 bytes of bf16 chunk x d_k
- * operands, 2 * 512 of 16 x 16 bf16 matrices, the per-token factors and padding. Writes it
- * to *bytes; GDN_ERR_SHAPE for a negative num_tokens, the gdn_prefill geometry checks
- * otherwise. */
+/* Workspace size of gdn_prefill: (floor(num_tokens / 16) + batch) * (num_v_heads * 5376
+ * + num_k_heads * 8192) bytes. Per chunk, one record per v-head holds a 4096-byte bf16
+ * chunk x d_k operand, two 512-byte 16 x 16 bf16 matrices, the per-token factors and
+ * padding; one record per k-head holds the chunk's queries and transposed keys (2 * 4096
+ * bytes of bf16), shared by the k-head's v-heads. Writes it to *bytes; GDN_ERR_SHAPE for a
+ * negative num_tokens, the gdn_prefill geometry checks otherwise. */
 GDN_API gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens, size_t* bytes);
 
 /* The gated RMS normalisation of the output, fused into verify or decode [P3] (Per-File QA

@@ -134,6 +134,11 @@ gdn::ConvArgs conv_args(const gdn_conv_dims* d) {
 // floor(cu[r] / 16) + j + r, below floor(N / 16) + B for N tokens.
 int64_t prefill_records(const gdn_dims* d, int64_t num_tokens) { return num_tokens / 16 + d->batch; }
 
+size_t prefill_workspace(const gdn_dims* d, int64_t num_tokens) {
+  return size_t(prefill_records(d, num_tokens)) *
+         (size_t(d->num_v_heads) * gdn::kPrefillRecordBytes + size_t(d->num_k_heads) * gdn::kPrefillKeyRecordBytes);
+}
+
 gdn_status check_prefill(const gdn_dims* d, int64_t num_tokens) {
   const gdn_status s = check_dims(d, false);
   if (s != GDN_OK) return s;
@@ -183,7 +188,7 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens,
   const gdn_status s = check_prefill(dims, num_tokens);
   if (s != GDN_OK) return s;
   if (!bytes) return GDN_ERR_NULL;
-  *bytes = size_t(prefill_records(dims, num_tokens)) * size_t(dims->num_v_heads) * gdn::kPrefillRecordBytes;
+  *bytes = prefill_workspace(dims, num_tokens);
   return GDN_OK;
 }
 
@@ -194,8 +199,7 @@ gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
   if (s != GDN_OK) return s;
   if (dims->batch == 0) return GDN_OK;
   const int64_t records = prefill_records(dims, num_tokens);
-  if (workspace_bytes < size_t(records) * size_t(dims->num_v_heads) * gdn::kPrefillRecordBytes)
-    return GDN_ERR_SHAPE;
+  if (workspace_bytes < prefill_workspace(dims, num_tokens)) return GDN_ERR_SHAPE;
   if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
       !state_pool || !state_indices || !cu_seqlens || !workspace)
     return GDN_ERR_NULL;

@@ -81,8 +81,11 @@ struct ConvArgs {
 // commit_only: advance each valid slot over prev_len tokens of prev_x and stop.
 hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t stream);
 
-// Bytes of one (chunk, v-head) record of the prefill workspace (a multiple of 256).
-constexpr int kPrefillRecordBytes = 13568;
+// The prefill workspace holds, per 16-token chunk, one record per v-head (the products
+// that involve the gates) and then one per k-head (its queries and transposed keys, shared
+// by the k-head's v-heads). Both sizes are multiples of 256 bytes.
+constexpr int kPrefillRecordBytes = 5376;
+constexpr int kPrefillKeyRecordBytes = 8192;
 
 // One launch of the chunked prefill (bf16 io, d_k = 128, d_v a multiple of 32).
 struct PrefillArgs {
@@ -98,7 +101,8 @@ struct PrefillArgs {
   const int32_t* idx;          // [B]
   const int32_t* fresh;        // [B] or nullptr
   const int32_t* cu;           // [B+1] token offsets
-  void* work;                  // [records][Hv] records of kPrefillRecordBytes
+  void* work;                  // [records][Hv] records of kPrefillRecordBytes, then
+                               // [records][Hk] of kPrefillKeyRecordBytes
   int64_t records;             // floor(N / 16) + B for N tokens
   int32_t B, Hk, Hv, DV, P, G;
   float scale, eps;

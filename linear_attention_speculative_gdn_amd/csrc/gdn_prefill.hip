@@ -19,8 +19,10 @@
 // Design for gfx950:
 // - Pass 1 (chunk_kernel) computes, for every (chunk, v-head) in parallel, everything that
 //   does not depend on the state -- W = Tm diag(beta Gam rk) K, Tm diag(beta), the output
-//   mask P, K^T and the per-token factors -- into a workspace record. That is most of a
-//   chunk's instructions, and none of it is sequential.
+//   mask P, K^T and the per-token factors -- into workspace records. That is most of a
+//   chunk's instructions, and none of it is sequential. Queries and K^T do not depend on
+//   the gates: they go to one record per k-head, written by its first v-head, which the
+//   other v-heads of the group read too.
 // - Pass 2 (scan_kernel) walks each sequence's chunks in order with the state in MFMA
 //   accumulators: U~ = Tm diag(beta) V, W S_0, Q S_0, P U and the state update only. The
 //   next chunk's record and queries are loaded while the current chunk computes.
@@ -53,17 +55,19 @@ constexpr int kC = 16;        // tokens per chunk
 constexpr int kDK = 128;      // key dimension
 constexpr int kKT = kDK / 16; // 16-row tiles of the key dimension
 
-// Workspace record of one (chunk, v-head): byte offsets (kPrefillRecordBytes in total).
-// Every matrix is stored in the lane layout of the matrix-core operand that reads it, so
-// a pass-2 lane fetches its part with 16-byte loads of contiguous 1 KiB blocks.
+// Workspace records: byte offsets. Every matrix is stored in the lane layout of the
+// matrix-core operand that reads it, so a pass-2 lane fetches its part with 16-byte loads
+// of contiguous 1 KiB blocks. Per (chunk, v-head), kPrefillRecordBytes in total:
 constexpr int kRecW = 0;       // -W, A operand of 16x16x32: [32-key block m][lane][8 bf16]
-constexpr int kRecQ = 4096;    // Q (stored values), same layout
-constexpr int kRecKT = 8192;   // K^T, A operand of 16x16x16, tiles 2m, 2m+1: [m][lane][2 x 4 bf16]
-constexpr int kRecTP = 12288;  // Tm diag(beta) and P = M o (rq rk) Q K^T, A operands: [lane][2 x 4 bf16]
-constexpr int kRecF = 13312;   // f_t = rk_t Gam_C / Gam_t [16] fp32
-constexpr int kRecGQ = 13376;  // Gam_t rq_t [16] fp32
-constexpr int kRecGC = 13440;  // Gam_C fp32
+constexpr int kRecTP = 4096;   // Tm diag(beta) and P = M o (rq rk) Q K^T, A operands: [lane][2 x 4 bf16]
+constexpr int kRecF = 5120;    // f_t = rk_t Gam_C / Gam_t [16] fp32
+constexpr int kRecGQ = 5184;   // Gam_t rq_t [16] fp32
+constexpr int kRecGC = 5248;   // Gam_C fp32
 static_assert(kRecGC + 4 <= kPrefillRecordBytes && kPrefillRecordBytes % 256 == 0, "record layout");
+// per (chunk, k-head), kPrefillKeyRecordBytes in total, after all the v-head records:
+constexpr int kKeyQ = 0;       // Q (stored values), A operand of 16x16x32, like -W
+constexpr int kKeyKT = 4096;   // K^T, A operand of 16x16x16, tiles 2m, 2m+1: [m][lane][2 x 4 bf16]
+static_assert(kKeyKT + 4096 == kPrefillKeyRecordBytes, "key record layout");
 
 __device__ __forceinline__ f32x4 mfma(const s16x4& a, const s16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -103,6 +107,14 @@ __device__ __forceinline__ s16x4 ld4(const uint16_t* base, int row, int stride, 
 
 __device__ __forceinline__ int64_t record_id(int32_t cu_r, int row, int j) { return (cu_r >> 4) + j + row; }
 
+// record of (chunk record rid, v-head h) and of (rid, k-head kh)
+__device__ __forceinline__ char* head_record(const PrefillArgs& p, int64_t rid, int h) {
+  return static_cast<char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
+}
+__device__ __forceinline__ char* key_record(const PrefillArgs& p, int64_t rid, int kh) {
+  return static_cast<char*>(p.work) + p.records * p.Hv * kPrefillRecordBytes + (rid * p.Hk + kh) * kPrefillKeyRecordBytes;
+}
+
 // B operand of the 16x16 identity: multiplying an A-layout tile X (lane (row r, group g)
 // holding X[r][4g .. 4g+3]) by it gives X itself in the accumulator layout (lane (g, n)
 // holding X[4g .. 4g+3][n]), i.e. X^T in the A layout: an exact transpose through the
@@ -139,6 +151,7 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
   const int nchunks = (t1 - t0 + kC - 1) / kC;
   const int kh = h / p.G;
+  const bool key_writer = h == kh * p.G;  // the k-head's first v-head writes its key record
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + size_t(kh) * kDK + 4 * l4;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + size_t(kh) * kDK + 4 * l4;
   const uint16_t* ag = static_cast<const uint16_t*>(p.a);
@@ -150,7 +163,8 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   for (int j = blockIdx.x; j < nchunks; j += gridDim.x) {
     const int64_t rid = record_id(t0, row, j);
     if (rid >= p.records) return;  // workspace too small for the tokens: write nothing
-    char* rec = static_cast<char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
+    char* rec = head_record(p, rid, h);
+    char* krec = key_record(p, rid, kh);
     const int cs = t0 + j * kC, n = min(kC, t1 - cs), last = t1 - 1;
     const bool live = l16 < n;  // token t = l16 of the chunk exists
     // ---- 1. keys and queries of token l16 in the A layout of 16x16x32 (lane (t, g):
@@ -249,11 +263,13 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     for (int m = 0; m < kKT / 2; ++m) {
       const s16x4 kt0 = bf16x4(mfma(lo4(kA[m]), eye, zero4));
       const s16x4 kt1 = bf16x4(mfma(hi4(kA[m]), eye, zero4));
-      *reinterpret_cast<s16x8*>(rec + kRecKT + m * 1024 + l * 16) = cat8(kt0, kt1);
+      if (key_writer) {
+        *reinterpret_cast<s16x8*>(krec + kKeyKT + m * 1024 + l * 16) = cat8(kt0, kt1);
+        *reinterpret_cast<s16x8*>(krec + kKeyQ + m * 1024 + l * 16) = qA[m];  // zero past the end
+      }
       const s16x4 w0 = bf16x4(mfma(kt0, twA, zero4));
       const s16x4 w1 = bf16x4(mfma(kt1, twA, zero4));
       *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
-      *reinterpret_cast<s16x8*>(rec + kRecQ + m * 1024 + l * 16) = qA[m];  // zero past the end
     }
     // ---- 6. Tm diag(beta) and P, the per-token factors
     *reinterpret_cast<s16x8*>(rec + kRecTP + l * 16) = cat8(tvA, pA);
@@ -379,10 +395,9 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   // meet zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
   // Uniform bases and 32-bit lane offsets (the host bounds the token tensors below 2^30
   // elements) keep the lane offsets in VGPRs that do not change from chunk to chunk.
-  auto record = [&](int j) {
-    const int64_t rid = min(rid0 + j, p.records - 1);
-    return static_cast<const char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
-  };
+  const int kh = h / p.G;
+  auto record = [&](int j) -> const char* { return head_record(p, min(rid0 + j, p.records - 1), h); };
+  auto krecord = [&](int j) -> const char* { return key_record(p, min(rid0 + j, p.records - 1), kh); };
   const uint32_t o_l = uint32_t(l * 16);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -404,10 +419,11 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
     auto fetch = [&](int j) -> StateOps {
       StateOps c;
       const char* rec = record(j);
+      const char* krec = krecord(j);
 #pragma unroll
       for (int m = 0; m < kKT / 2; ++m) {
         c.w[m] = *reinterpret_cast<const s16x8*>(rec + kRecW + m * 1024 + o_l);
-        c.kt[m] = *reinterpret_cast<const s16x8*>(rec + kRecKT + m * 1024 + o_l);
+        c.kt[m] = *reinterpret_cast<const s16x8*>(krec + kKeyKT + m * 1024 + o_l);
       }
       c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l);  // the lower half
       c.f = *reinterpret_cast<const f32x4*>(rec + o_f);
@@ -462,8 +478,9 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
     auto fetch = [&](int j) -> OutOps {
       OutOps c;
       const char* rec = record(j);
+      const char* krec = krecord(j);
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(rec + kRecQ + m * 1024 + o_l);
+      for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(krec + kKeyQ + m * 1024 + o_l);
       c.pm = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l + 8);  // the upper half
       c.gq = *reinterpret_cast<const float*>(rec + o_gq);
       return c;

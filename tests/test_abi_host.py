@@ -155,9 +155,10 @@ def prefill_ws(L, d, n):
 
 
 def test_prefill_workspace_size(L):
-    """One 13568-byte record per (16-token chunk, v-head), floor(N/16) + B chunks."""
-    assert prefill_ws(L, dims(batch=4, num_v_heads=4), 64) == (0, (4 + 4) * 4 * 13568)
-    assert prefill_ws(L, dims(batch=3, num_v_heads=32, d_v=64), 16384 + 15) == (0, (1024 + 3) * 32 * 13568)
+    """Per 16-token chunk (floor(N/16) + B of them) a 5376-byte record per v-head and an
+    8192-byte one per k-head."""
+    assert prefill_ws(L, dims(batch=4, num_v_heads=4), 64) == (0, (4 + 4) * (4 * 5376 + 2 * 8192))
+    assert prefill_ws(L, dims(batch=3, num_v_heads=32, d_v=64), 16384 + 15) == (0, (1024 + 3) * (32 * 5376 + 2 * 8192))
     assert prefill_ws(L, dims(batch=0), 0) == (0, 0)
     assert prefill_ws(L, dims(), -1)[0] == 2
     assert prefill_ws(L, dims(d_k=64), 16)[0] == 5
