@@ -49,6 +49,22 @@ int pick_shape(const gdn_dims* d) {
   return 1;
 }
 
+// Load policy of the initial state. Nontemporal loads do not keep the state's lines in
+// the XCD's L2. That matters where the same lines are stored to later, by the launch
+// itself (decode's write-back, an in-kernel commit) or by the commit launch that
+// follows a verify: the stores then no longer hit resident lines, which appears to
+// spare a write-back of dirty L2 lines at the end of the launch. Measured (plain ->
+// nontemporal, cold pools): decode fp32 B=64 15.1 -> 13.7 us, B=256 51.2 -> 46.4 us;
+// verify + commit on the MTP T=4 bf16 batch 27.1 -> 22.4 us per step, verify alone
+// 1-2 % faster at B = 64..512; cached replay 19.3 -> 16.2 us; gated verify + commit
+// 29.3 -> 26.3 us. Slower: T = 8 with 32 v-heads (fused 227 -> 247 us at B = 128, plain
+// 205 -> 216 us, 2-6 % at B = 32..96) and the 2-wave fp32 shape (T = 4, 8192 tiles:
+// 468 -> 482 us). Replay calls always take them.
+bool pick_nt_loads(const gdn_dims* d, bool replay) {
+  if (replay) return true;
+  return d->T <= 4 && pick_shape(d) == 1;
+}
+
 gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const int32_t* idx,
                          void* cache, int32_t cache_T, int32_t write_final,
                          const int32_t* prev_accept, void* stream, const gdn_out_gate* gate = nullptr) {
@@ -88,7 +104,8 @@ gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const 
   p.gw = gate ? gate->weight : nullptr;
   p.geps = gate ? gate->eps : 0.f;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(d->state_dtype), static_cast<Dt>(d->io_dtype),
-                                             pick_shape(d), gate ? 3 : 0, p, static_cast<hipStream_t>(stream));
+                                             pick_shape(d), gate ? 3 : 0, pick_nt_loads(d, false), p,
+                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -270,7 +287,7 @@ gdn_status gdn_verify_replay(const gdn_dims* dims, const gdn_io* io, void* state
   set_replay(p, replay, replay_len, commit);
   p.z = nullptr; p.gw = nullptr; p.geps = 0.f;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
-                                             1, 1, p, static_cast<hipStream_t>(stream));
+                                             1, 1, pick_nt_loads(dims, true), p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -298,7 +315,7 @@ gdn_status gdn_commit_replay(const gdn_dims* dims, const float* A_log, const flo
   set_replay(p, replay, replay_len, 1);
   p.z = nullptr; p.gw = nullptr; p.geps = 0.f;
   const hipError_t e = gdn::launch_recurrent(static_cast<Dt>(dims->state_dtype), static_cast<Dt>(dims->io_dtype),
-                                             1, 2, p, static_cast<hipStream_t>(stream));
+                                             1, 2, pick_nt_loads(dims, true), p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -59,7 +59,9 @@ struct CommitArgs {
 // mode: 0 decode / verify, 1 cached-replay verify, 2 replay commit, 3 decode / verify
 // with the gated-norm output epilogue (modes 1-3 use their own fixed shapes).
 // Mode 3 needs d_v <= 256 for d_k <= 64 and d_v <= 128 for d_k >= 128.
-hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, const RecurrentArgs& p,
+// nt_loads: read the initial state with nontemporal loads (d_k = 128, shape 1 and the
+// fixed shapes of modes 1-3; ignored elsewhere).
+hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, bool nt_loads, const RecurrentArgs& p,
                             hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream);
 

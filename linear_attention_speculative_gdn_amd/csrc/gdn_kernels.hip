@@ -135,7 +135,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Every global load is unconditional, from an address clamped into its buffer, and
 // out-of-range lanes discard the value afterwards: a load inside a branch would be
 // waited on at the end of the branch, which serialises the memory round trips.
-template <typename ST, typename IT, int DK, int R, int NW, int MODE, bool GATE = false>
+template <typename ST, typename IT, int DK, int R, int NW, int MODE, bool GATE = false, bool NTL = false>
 __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs p) {
   constexpr bool NEW = MODE != 2;        // this call has its own tokens (and outputs)
   constexpr bool REPLAY = MODE != 0;
@@ -296,8 +296,10 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
     rv[r] = jrow[r] < DV;
     const int jr = min(jrow[r], DV - 1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      raw[r][c] = *reinterpret_cast<const u32x4*>(src + size_t(jr) * DK + (l + c * L) * CE);
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4* at = reinterpret_cast<const u32x4*>(src + size_t(jr) * DK + (l + c * L) * CE);
+      raw[r][c] = NTL ? __builtin_nontemporal_load(at) : *at;
+    }
   }
 
   // ---- 4. token inputs -> LDS (replayed tokens first, then this call's); gates.
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
   }
 }
 
-template <typename ST, typename IT, int DK, int R, int NW = 4, int MODE = 0, bool GATE = false>
+template <typename ST, typename IT, int DK, int R, int NW = 4, int MODE = 0, bool GATE = false, bool NTL = false>
 hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
   constexpr int RPW = NW * R * (64 / (DK / 16));
   const int nvb = (p.DV + RPW - 1) / RPW;
@@ -610,7 +612,7 @@ hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
   const size_t tmax = size_t(MODE == 2 ? 0 : p.T) + size_t(MODE == 0 ? 0 : p.rT);
   const size_t lds = sizeof(float) * (2 * tmax * DK + tmax * RPW + 3 * tmax + RPW +
                                       (GATE ? size_t(p.T) * (RPW + 1) : 0));
-  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW, MODE, GATE>), grid, dim3(NW * 64), lds, stream, p);
+  hipLaunchKernelGGL((recurrent_kernel<ST, IT, DK, R, NW, MODE, GATE, NTL>), grid, dim3(NW * 64), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -619,13 +621,15 @@ hipError_t launch_rec(const RecurrentArgs& p, hipStream_t stream) {
 // per-token stores): at d_k = 128 two rows per lane halve the k^/q^ reads from LDS
 // per state element, and 8 waves per workgroup keep more of them in flight.
 template <typename ST, typename IT>
-hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t stream) {
+hipError_t launch_dk(int shape, int mode, bool ntl, const RecurrentArgs& p, hipStream_t stream) {
   if (mode == 1) {
     switch (p.DK) {
       case 16: return launch_rec<ST, IT, 16, 1, 4, 1>(p, stream);
       case 32: return launch_rec<ST, IT, 32, 1, 4, 1>(p, stream);
       case 64: return launch_rec<ST, IT, 64, 1, 4, 1>(p, stream);
-      case 128: return launch_rec<ST, IT, 128, 2, 8, 1>(p, stream);
+      case 128:
+        return ntl ? launch_rec<ST, IT, 128, 2, 8, 1, false, true>(p, stream)
+                   : launch_rec<ST, IT, 128, 2, 8, 1>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 1, 4, 1>(p, stream);
       default: return hipErrorInvalidValue;
     }
@@ -635,7 +639,9 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
       case 16: return launch_rec<ST, IT, 16, 1, 4, 0, true>(p, stream);    // 256 value rows
       case 32: return launch_rec<ST, IT, 32, 1, 8, 0, true>(p, stream);    // 256
       case 64: return launch_rec<ST, IT, 64, 2, 8, 0, true>(p, stream);    // 256
-      case 128: return launch_rec<ST, IT, 128, 2, 8, 0, true>(p, stream);  // 128
+      case 128:  // 128
+        return ntl ? launch_rec<ST, IT, 128, 2, 8, 0, true, true>(p, stream)
+                   : launch_rec<ST, IT, 128, 2, 8, 0, true>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 4, 8, 0, true>(p, stream);  // 128
       default: return hipErrorInvalidValue;
     }
@@ -645,7 +651,9 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
       case 16: return launch_rec<ST, IT, 16, 1, 4, 2>(p, stream);
       case 32: return launch_rec<ST, IT, 32, 1, 4, 2>(p, stream);
       case 64: return launch_rec<ST, IT, 64, 1, 4, 2>(p, stream);
-      case 128: return launch_rec<ST, IT, 128, 2, 8, 2>(p, stream);
+      case 128:
+        return ntl ? launch_rec<ST, IT, 128, 2, 8, 2, false, true>(p, stream)
+                   : launch_rec<ST, IT, 128, 2, 8, 2>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 1, 4, 2>(p, stream);
       default: return hipErrorInvalidValue;
     }
@@ -658,7 +666,7 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
       if (shape == 2) return launch_rec<ST, IT, 128, 2>(p, stream);
       if (shape == 12) return launch_rec<ST, IT, 128, 1, 2>(p, stream);
       if (shape == 14) return launch_rec<ST, IT, 128, 1, 8>(p, stream);
-      return launch_rec<ST, IT, 128, 1>(p, stream);
+      return ntl ? launch_rec<ST, IT, 128, 1, 4, 0, false, true>(p, stream) : launch_rec<ST, IT, 128, 1>(p, stream);
     case 256: return launch_rec<ST, IT, 256, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
@@ -666,12 +674,12 @@ hipError_t launch_dk(int shape, int mode, const RecurrentArgs& p, hipStream_t st
 
 }  // namespace
 
-hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, const RecurrentArgs& p,
+hipError_t launch_recurrent(Dt state, Dt io, int shape, int mode, bool nt_loads, const RecurrentArgs& p,
                             hipStream_t stream) {
-  if (state == Dt::F32 && io == Dt::F32) return launch_dk<float, float>(shape, mode, p, stream);
-  if (state == Dt::F32 && io == Dt::BF16) return launch_dk<float, bf16s>(shape, mode, p, stream);
-  if (state == Dt::BF16 && io == Dt::F32) return launch_dk<bf16s, float>(shape, mode, p, stream);
-  return launch_dk<bf16s, bf16s>(shape, mode, p, stream);
+  if (state == Dt::F32 && io == Dt::F32) return launch_dk<float, float>(shape, mode, nt_loads, p, stream);
+  if (state == Dt::F32 && io == Dt::BF16) return launch_dk<float, bf16s>(shape, mode, nt_loads, p, stream);
+  if (state == Dt::BF16 && io == Dt::F32) return launch_dk<bf16s, float>(shape, mode, nt_loads, p, stream);
+  return launch_dk<bf16s, bf16s>(shape, mode, nt_loads, p, stream);
 }
 
 hipError_t launch_commit(const CommitArgs& p, hipStream_t stream) {
