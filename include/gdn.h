@@ -46,7 +46,7 @@
  * - Host-checkable faults return an error before anything is launched; nothing is
  *   written. A failed launch returns GDN_ERR_LAUNCH.
  * - The library allocates nothing, never synchronises, keeps no global state and
- *   launches its kernels (one per call; two for gdn_prefill) on `stream` (a
+ *   launches its kernels (one per call; two to four for gdn_prefill) on `stream` (a
  *   hipStream_t; NULL is the default stream). Calls are therefore thread-safe and may
  *   be captured in a HIP graph.
  * - Supported geometry: d_k in {16, 32, 64, 128, 256}; d_v a multiple of 16 in
@@ -157,22 +157,34 @@ GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int
  * cu_seqlens[B] <= num_tokens is required (not checked: the offsets live on the device),
  * and num_tokens * Hv * d_v and num_tokens * Hk * d_k must stay below 2^30 elements
  * (GDN_ERR_UNSUPPORTED otherwise).
- * The call runs in two kernels: the first prepares, for every 16-token chunk and v-head,
- * the state-independent products in `workspace` (device memory owned by the caller,
- * 256-byte aligned, at least gdn_prefill_workspace_bytes(dims, num_tokens) bytes,
- * GDN_ERR_SHAPE if smaller); the second walks each sequence's chunks in order. The
- * workspace holds nothing between calls; calls that overlap in time need their own. */
+ * The first kernel prepares, for every 16-token chunk and v-head, the state-independent
+ * products in `workspace` (device memory owned by the caller, 256-byte aligned, at least
+ * gdn_prefill_workspace_bytes(dims, num_tokens) bytes, GDN_ERR_SHAPE if smaller). Then each
+ * sequence's chunks are walked in order, in segments (their length is chosen from the
+ * geometry, as under gdn_prefill_workspace_bytes): one more kernel when every sequence is
+ * one segment; otherwise the first segments and the maps of the middle ones, a kernel that
+ * composes the maps into each segment's starting state, and the remaining segments (up to
+ * four kernels per call). The workspace holds nothing between calls; calls that overlap in
+ * time need their own. */
 GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
                                const int32_t* state_indices, const int32_t* cu_seqlens,
                                const int32_t* fresh, int64_t num_tokens, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Workspace size of gdn_prefill: (floor(num_tokens / 16) + batch) * (num_v_heads * 5376
- * + num_k_heads * 8192) bytes. Per chunk, one record per v-head holds a 4096-byte bf16
- * chunk x d_k operand, two 512-byte 16 x 16 bf16 matrices, the per-token factors and
- * padding; one record per k-head holds the chunk's queries and transposed keys (2 * 4096
- * bytes of bf16), shared by the k-head's v-heads. Writes it to *bytes; GDN_ERR_SHAPE for a
- * negative num_tokens, the gdn_prefill geometry checks otherwise. */
+/* Workspace size of gdn_prefill, in three parts:
+ * - per 16-token chunk, (floor(num_tokens / 16) + batch) of them, one 5376-byte record per
+ *   v-head (a 4096-byte bf16 chunk x d_k operand, two 512-byte 16 x 16 bf16 matrices, the
+ *   per-token factors, padding) and one 8192-byte record per k-head (the chunk's queries
+ *   and transposed keys, shared by the k-head's v-heads);
+ * - a table of the segments of the chunk chain, 4 bytes each, padded to 256 bytes;
+ * - per segment and v-head, a slot of 128 * d_v * 4 + 128 * 128 * 2 bytes (a state and a
+ *   segment map).
+ * Segments hold 2^s tokens and number floor(num_tokens / 2^s) + batch. s is the smallest
+ * s >= 8 with 2^s > num_tokens (one segment per sequence) when 2 * batch * num_v_heads *
+ * d_v / 16 >= 512; otherwise the smallest s >= 8 with 2^s >= num_tokens * num_v_heads *
+ * (d_v / 16) * 2 / 4096 (integer division), but no more than the first. Writes the size to
+ * *bytes; GDN_ERR_SHAPE for a negative num_tokens, the gdn_prefill geometry checks
+ * otherwise. */
 GDN_API gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens, size_t* bytes);
 
 /* The gated RMS normalisation of the output, fused into verify or decode [P3] (Per-File QA

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
 
@@ -151,9 +153,33 @@ gdn::ConvArgs conv_args(const gdn_conv_dims* d) {
 // floor(cu[r] / 16) + j + r, below floor(N / 16) + B for N tokens.
 int64_t prefill_records(const gdn_dims* d, int64_t num_tokens) { return num_tokens / 16 + d->batch; }
 
+// Segment length of the chunk chain, as log2 of its tokens. The chain of one (sequence,
+// v-head, 16 value columns) is a state wave and an output wave; a chunk step keeps a SIMD
+// busy (two chains on one SIMD take twice as long per step), so splitting sequences into
+// segments, whose maps are composed afterwards, pays only when those waves leave most of
+// the chip's 1024 SIMDs idle. Then segments are sized so that about 4096 waves run; else a
+// segment is longer than any sequence (N < 2^shift: every sequence is one segment, and
+// segment ids are the row numbers, with no gaps in the grid).
+int32_t prefill_seg_shift(const gdn_dims* d, int64_t num_tokens) {
+  int32_t whole = 8;
+  while ((int64_t(1) << whole) <= num_tokens) ++whole;
+  const int64_t waves = int64_t(d->batch) * d->num_v_heads * (d->d_v / 16) * 2;
+  if (waves >= 512) return whole;
+  const int64_t target = num_tokens * d->num_v_heads * (d->d_v / 16) * 2 / 4096;  // tokens per segment
+  int32_t shift = 8;
+  while ((int64_t(1) << shift) < target) ++shift;
+  return std::min(shift, whole);
+}
+
+// Segments of the chunk chain: segment g of sequence r takes id floor(cu[r] / 2^shift) + g + r.
+int64_t prefill_segments(const gdn_dims* d, int64_t num_tokens) {
+  return (num_tokens >> prefill_seg_shift(d, num_tokens)) + d->batch;
+}
+
 size_t prefill_workspace(const gdn_dims* d, int64_t num_tokens) {
-  return size_t(prefill_records(d, num_tokens)) *
-         (size_t(d->num_v_heads) * gdn::kPrefillRecordBytes + size_t(d->num_k_heads) * gdn::kPrefillKeyRecordBytes);
+  const int64_t segs = prefill_segments(d, num_tokens);
+  return size_t(gdn::prefill_records_bytes(prefill_records(d, num_tokens), d->num_k_heads, d->num_v_heads) +
+                gdn::prefill_table_bytes(segs) + segs * d->num_v_heads * gdn::prefill_slot_bytes(d->d_v));
 }
 
 gdn_status check_prefill(const gdn_dims* d, int64_t num_tokens) {
@@ -230,6 +256,8 @@ gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool,
   p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
   p.pool = state_pool; p.idx = state_indices; p.fresh = fresh; p.cu = cu_seqlens;
   p.work = workspace; p.records = records;
+  p.segments = prefill_segments(dims, num_tokens); p.tokens = num_tokens;
+  p.seg_shift = prefill_seg_shift(dims, num_tokens);
   p.B = dims->batch; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.DV = dims->d_v;
   p.P = dims->pool_slots; p.G = dims->num_v_heads / dims->num_k_heads;
   p.scale = dims->scale; p.eps = dims->l2norm_eps;

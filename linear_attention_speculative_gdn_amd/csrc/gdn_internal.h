@@ -88,6 +88,14 @@ hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t s
 // by the k-head's v-heads). Both sizes are multiples of 256 bytes.
 constexpr int kPrefillRecordBytes = 5376;
 constexpr int kPrefillKeyRecordBytes = 8192;
+// The chunk chain runs in segments of 2^seg_shift tokens (seg_shift >= 8); after the
+// records the workspace holds a table of segment ids and, per (segment, v-head), a slot of
+// a d_k x d_v fp32 state and a d_k x d_k bf16 map.
+constexpr int64_t prefill_records_bytes(int64_t records, int Hk, int Hv) {
+  return records * (int64_t(Hv) * kPrefillRecordBytes + int64_t(Hk) * kPrefillKeyRecordBytes);
+}
+constexpr int64_t prefill_table_bytes(int64_t segments) { return (segments * 4 + 255) / 256 * 256; }
+constexpr int64_t prefill_slot_bytes(int dv) { return int64_t(dv) * 128 * 4 + 128 * 128 * 2; }
 
 // One launch of the chunked prefill (bf16 io, d_k = 128, d_v a multiple of 32).
 struct PrefillArgs {
@@ -106,6 +114,9 @@ struct PrefillArgs {
   void* work;                  // [records][Hv] records of kPrefillRecordBytes, then
                                // [records][Hk] of kPrefillKeyRecordBytes
   int64_t records;             // floor(N / 16) + B for N tokens
+  int64_t segments;            // floor(N / 2^seg_shift) + B
+  int64_t tokens;              // N
+  int32_t seg_shift;           // log2 of the tokens per segment of the chunk chain
   int32_t B, Hk, Hv, DV, P, G;
   float scale, eps;
 };

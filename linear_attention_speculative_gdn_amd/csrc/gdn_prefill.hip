@@ -107,6 +107,26 @@ __device__ __forceinline__ s16x4 ld4(const uint16_t* base, int row, int stride, 
 
 __device__ __forceinline__ int64_t record_id(int32_t cu_r, int row, int j) { return (cu_r >> 4) + j + row; }
 
+// Segments of 2^seg_shift tokens (a power of two >= 256, chosen on the host):
+// segment g of sequence r takes id floor(cu[r] / 2^seg_shift) + g + r, distinct and below
+// floor(N / 2^seg_shift) + B, like the records. An empty sequence has one.
+__device__ __forceinline__ int64_t segment_id(const PrefillArgs& p, int32_t cu_r, int row, int g) {
+  return (cu_r >> p.seg_shift) + g + row;
+}
+__device__ __forceinline__ int seg_chunks(const PrefillArgs& p) { return 1 << (p.seg_shift - 4); }
+__device__ __forceinline__ int seg_count(const PrefillArgs& p, int nchunks) {
+  return max(1, (nchunks + seg_chunks(p) - 1) >> (p.seg_shift - 4));
+}
+// after the records: the segment table ([segments] int32: (g << 16) | r, or -1), then a
+// slot per (segment, v-head)
+__device__ __forceinline__ int32_t* segment_table(const PrefillArgs& p) {
+  return reinterpret_cast<int32_t*>(static_cast<char*>(p.work) + prefill_records_bytes(p.records, p.Hk, p.Hv));
+}
+__device__ __forceinline__ char* segment_slot(const PrefillArgs& p, int64_t sid, int h) {
+  return reinterpret_cast<char*>(segment_table(p)) + prefill_table_bytes(p.segments) +
+         (sid * p.Hv + h) * prefill_slot_bytes(p.DV);
+}
+
 // record of (chunk record rid, v-head h) and of (rid, k-head kh)
 __device__ __forceinline__ char* head_record(const PrefillArgs& p, int64_t rid, int h) {
   return static_cast<char*>(p.work) + (rid * p.Hv + h) * kPrefillRecordBytes;
@@ -147,9 +167,22 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   const int h = blockIdx.y, row = blockIdx.z;
   const int l = threadIdx.x, l16 = l & 15, l4 = l >> 4;
   const int32_t slot = p.idx[row];
-  if (slot < 0 || slot >= p.P) return;  // padding rows have no chunks to prepare
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
   const int nchunks = (t1 - t0 + kC - 1) / kC;
+  if (blockIdx.x == 0 && h == 0) {
+    // the segment table entries from this sequence's first segment id up to the next
+    // sequence's (to the table's end for the last; from 0 for the first): each entry is
+    // written by exactly one wave
+    const int64_t s0 = segment_id(p, t0, row, 0);
+    const int64_t s1 = row + 1 < p.B ? segment_id(p, t1, row + 1, 0) : p.segments;
+    const int nseg = seg_count(p, nchunks);
+    int32_t* table = segment_table(p);
+    for (int64_t sidx = (row == 0 ? 0 : s0) + l; sidx < min(s1, p.segments); sidx += 64) {
+      const int64_t g = sidx - s0;
+      table[sidx] = (g >= 0 && g < nseg) ? int32_t((g << 16) | row) : -1;
+    }
+  }
+  if (slot < 0 || slot >= p.P) return;  // padding rows have no chunks to prepare
   const int kh = h / p.G;
   const bool key_writer = h == kh * p.G;  // the k-head's first v-head writes its key record
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + size_t(kh) * kDK + 4 * l4;
@@ -334,18 +367,18 @@ __device__ __forceinline__ void keep_after(T& x) {
   asm volatile("" : "+v"(x)::"memory");
 }
 
-// Runs chunks 0 .. n-1 through step(ops, j) with the operands of chunk j + 2 loading while
-// chunk j computes: pairs of chunks with no exit inside a pair (nothing sinks into the
-// next one), then an odd last chunk alone; each operand set keeps its registers (no copies
-// between them), and nothing is in flight at the loop's start (the wait counts inside
-// the loop then follow from its own loads alone).
+// Runs chunks ja .. jb-1 through step(ops, j) with the operands of chunk j + 2 loading
+// while chunk j computes: pairs of chunks with no exit inside a pair (nothing sinks into
+// the next one), then an odd last chunk alone; each operand set keeps its registers (no
+// copies between them), and nothing is in flight at the loop's start (the wait counts
+// inside the loop then follow from its own loads alone).
 template <typename Ops, typename Fetch, typename Step, typename After>
-__device__ __forceinline__ void run_chunks(int n, Fetch fetch, Step step, After after) {
-  if (n <= 0) return;
-  Ops c0 = fetch(0), c1 = fetch(1);
+__device__ __forceinline__ void run_chunks(int ja, int jb, Fetch fetch, Step step, After after) {
+  if (jb <= ja) return;
+  Ops c0 = fetch(ja), c1 = fetch(ja + 1);
   __builtin_amdgcn_s_waitcnt(0);
-  int j = 0;
-  for (; j + 1 < n; j += 2) {
+  int j = ja;
+  for (; j + 1 < jb; j += 2) {
     step(c0, j);
     after();
     c0 = fetch(j + 2);
@@ -353,171 +386,347 @@ __device__ __forceinline__ void run_chunks(int n, Fetch fetch, Step step, After 
     after();
     c1 = fetch(j + 3);
   }
-  if (j < n) step(c0, j);
+  if (j < jb) step(c0, j);
 }
 
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One workgroup of two waves per (sequence, v-head, block of 16 value columns). io is
-// bf16. Wave 0 carries the state chain: U = Tm diag(beta) V - W S_0 and the update; it
-// hands bf16 S_0 and U to wave 1, which computes the outputs (Q S_0, P U) one chunk
-// behind, so the chain never waits for them.
-// 1-D grid, XCD-aware: the column blocks of a (sequence, v-head) read the same records,
-// so they are given ids on one XCD (id % 8 equal) and share its L2. Head unit u (=
-// row * Hv + h) and column block cb take id (u % 8) + 8 (cb + nb (u / 8)).
-template <typename ST>
+// Everything a chain needs about its (sequence, v-head) and value-column block.
+struct ChainArgs {
+  int64_t rid0;  // record of chunk 0
+  int t0, t1;    // token range of the sequence
+  int h, kh;     // v-head, k-head
+  int c0;        // first value column of the block (V and o)
+};
+
+// The state chain over chunks [ja, jb) with S in MFMA accumulators (tile kt of lane l holds
+// S[16kt + 4 l4 + i][column l16 of the block]): U = Tm diag(beta) V - W S_0, then the update.
+// WITH_V: the Tm diag(beta) V term (off for a segment map, whose values are zero).
+// HANDOFF: bf16 S_0 and U go to the output wave through LDS, one barrier per chunk.
+template <bool WITH_V, bool HANDOFF>
+__device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds& L, const ChainArgs& a, f32x4 (&S)[kKT],
+                                            int ja, int jb) {
+  const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
+  const uint32_t o_l = uint32_t(l * 16);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int last = max(a.t1 - 1, 0);
+  const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(a.h) * p.DV + a.c0);
+  const uint32_t vrow_b = uint32_t(p.Hv) * uint32_t(p.DV) * 2u;
+  const uint32_t o_f = uint32_t(kRecF + 16 * l4);
+  const s16x4 eye = identity_b(l16, l4);
+  auto fetch = [&](int j) -> StateOps {
+    StateOps c;
+    const int64_t rid = min(a.rid0 + j, p.records - 1);
+    const char* rec = head_record(p, rid, a.h);
+    const char* krec = key_record(p, rid, a.kh);
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) {
+      c.w[m] = *reinterpret_cast<const s16x8*>(rec + kRecW + m * 1024 + o_l);
+      c.kt[m] = *reinterpret_cast<const s16x8*>(krec + kKeyKT + m * 1024 + o_l);
+    }
+    c.f = *reinterpret_cast<const f32x4*>(rec + o_f);
+    c.gc = *reinterpret_cast<const float*>(rec + kRecGC);
+    if constexpr (WITH_V) {
+      c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l);  // the lower half
+      const uint32_t tok = uint32_t(min(a.t0 + j * kC + l16, last));
+      c.v = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4);
+    }
+    return c;
+  };
+  auto step = [&](const StateOps& c, int j) {
+    const int buf = j & 1;
+    f32x4 tvv = zero4;
+    if constexpr (WITH_V) {
+      // Tm diag(beta) V (V transposed by the identity product). The asm pins the
+      // state-independent products to this step: hoisted to the loop's start, they would
+      // wait for loads issued just before.
+      s16x4 v = c.v, tv = c.tv;
+      asm volatile("" : "+v"(v), "+v"(tv));
+      tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+    }
+    // -W S_0 in two interleaved accumulators (half the dependent chain). The 16x16x16
+    // product above joins them through a vector add, not as an accumulator: a 16x16x32
+    // product reading the result of a 16x16x16 one needs five wait states, and the
+    // compiler does not always place them.
+    f32x4 u0 = zero4, u1 = zero4;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) {
+      const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
+      if constexpr (HANDOFF) L.s[buf][m][l] = sB;
+      if (m & 1)
+        u1 = mfma32(c.w[m], sB, u1);
+      else
+        u0 = mfma32(c.w[m], sB, u0);
+    }
+    const f32x4 u = (u0 + u1) + tvv;
+    if constexpr (HANDOFF) {
+      L.u[buf][l] = bf16x4(u);
+      barrier_lds();
+    }
+    // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
+    const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt)
+      S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
+  };
+  auto after = [&]() {
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) keep_after(S[kt]);
+  };
+  run_chunks<StateOps>(ja, jb, fetch, step, after);
+}
+
+// The outputs of chunks [ja, jb), one chunk behind the state chain that hands them over:
+// O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T) with (Q S_0)^T = S_0^T Q^T: lane (g, t)
+// holds columns 4g .. 4g+3 of token t.
+__device__ __forceinline__ void output_chain(const PrefillArgs& p, ScanLds& L, const ChainArgs& a, int ja, int jb) {
+  const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
+  const uint32_t o_l = uint32_t(l * 16);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  uint16_t* og = static_cast<uint16_t*>(p.o);
+  const uint32_t o_gq = uint32_t(kRecGQ + 4 * l16);
+  auto fetch = [&](int j) -> OutOps {
+    OutOps c;
+    const int64_t rid = min(a.rid0 + j, p.records - 1);
+    const char* rec = head_record(p, rid, a.h);
+    const char* krec = key_record(p, rid, a.kh);
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(krec + kKeyQ + m * 1024 + o_l);
+    c.pm = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l + 8);  // the upper half
+    c.gq = *reinterpret_cast<const float*>(rec + o_gq);
+    return c;
+  };
+  auto step = [&](const OutOps& c, int j) {
+    const int buf = j & 1, cs = a.t0 + j * kC, n = min(kC, a.t1 - cs);
+    barrier_lds();  // chunk j's S_0 and U are in buffer j & 1
+    // Every operand read from LDS gets its own registers and has arrived before the
+    // first product: no LDS return lands in a register a pending product still reads.
+    s16x8 sA[kKT / 2];
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) sA[m] = L.s[buf][m][l];
+    s16x4 uA = L.u[buf][l];
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA));
+    f32x4 qs = zero4;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], c.q[m], qs);
+    const f32x4 pu = mfma(uA, c.pm, zero4);
+    float ov[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
+    if (l16 < n)
+      *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + a.h) * p.DV + a.c0 + 4 * l4) =
+          uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+  };
+  // the step ends in its store, so a memory clobber keeps the next loads after it
+  auto after = [&]() { asm volatile("" ::: "memory"); };
+  run_chunks<OutOps>(ja, jb, fetch, step, after);
+}
+
+// fp32 state block cb of a segment slot, in the accumulator layout: [kt][lane][4]
+__device__ __forceinline__ f32x4* slot_block(const PrefillArgs& p, int64_t sid, int h, int cb) {
+  return reinterpret_cast<f32x4*>(segment_slot(p, sid, h)) + (cb * kKT) * 64 + (threadIdx.x & 63);
+}
+// bf16 segment map of a slot, in the A layout of 16x16x32: [row tile kt][32-column block m][lane][8]
+__device__ __forceinline__ s16x8* slot_map(const PrefillArgs& p, int64_t sid, int h) {
+  return reinterpret_cast<s16x8*>(segment_slot(p, sid, h) + size_t(p.DV) * kDK * 4);
+}
+
+// Pass 2 runs the chunk chain of each sequence in segments of 2^seg_shift tokens. With
+// F_g the map from the state at the start of segment g to the state at its end,
+// F_g(S) = M_g S + N_g: N_g is the chain from a zero state, M_g (d_k x d_k) the chain from
+// the identity with zero values. Three launches:
+// - PH 0: segment 0 from the slot's state, with outputs (its end state goes to the
+//   segment slot, or to the pool if it is the only segment); for every middle segment
+//   1 .. n-2, N_g (wave 0) and M_g (wave 1) into its slot;
+// - combine_kernel: the start states S_{g+1} = M_g S_g + N_g, in sequence, into the slot
+//   of segment g (over N_g);
+// - PH 2: every later segment again from its start state (the slot of segment g - 1),
+//   with outputs; the last one stores the final state to the pool.
+// The chain is sequential within a segment only: two segments' chunk steps and n - 2
+// small products instead of one chunk step per chunk.
+// Two waves per workgroup; 1-D grid, XCD-aware: the column blocks of a (segment, v-head)
+// read the same records, so they get ids on one XCD (id % 8 equal) and share its L2.
+// Unit u (= segment * Hv + h) and column block cb take id (u % 8) + 8 (cb + ncb (u / 8)).
+template <typename ST, int PH>
 __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   __shared__ ScanLds L;
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = p.DV / 16;
-  const int rest = int(blockIdx.x) / kXcds, cb = rest % nb;
-  const int unit = (rest / nb) * kXcds + int(blockIdx.x) % kXcds;
-  if (unit >= p.B * p.Hv) return;  // the padding of the last group of 8 head units
-  const int c0 = cb * 16, h = unit % p.Hv, row = unit / p.Hv;
+  const int ncb = PH == 0 ? max(nb, kKT) : nb;
+  const int rest = int(blockIdx.x) / kXcds, cb = rest % ncb;
+  const int64_t unit = int64_t(rest / ncb) * kXcds + int(blockIdx.x) % kXcds;
+  if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
+  const int h = int(unit % p.Hv);
+  const int64_t sid = unit / p.Hv;
+  const int32_t entry = segment_table(p)[sid];
+  if (entry < 0) return;  // no segment has this id
+  const int row = entry & 0xFFFF, g = entry >> 16;
+  if (row >= p.B) return;  // (only a table left by inconsistent cu_seqlens)
   const int32_t slot = p.idx[row];
-  const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
-  uint16_t* og = static_cast<uint16_t*>(p.o);
+  ChainArgs a;
+  a.t0 = p.cu[row];
+  a.t1 = p.cu[row + 1];
+  a.h = h;
+  a.kh = h / p.G;
+  a.c0 = cb * 16;
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
-    for (int t = t0 + wave * 32 + (l >> 1); t < t1; t += 64)
-      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + c0 + 8 * (l & 1)) = u32x4{0u, 0u, 0u, 0u};
+    if (PH == 0 && g == 0 && cb < nb) {
+      uint16_t* og = static_cast<uint16_t*>(p.o);
+      for (int t = a.t0 + wave * 32 + (l >> 1); t < a.t1; t += 64)
+        *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + a.c0 + 8 * (l & 1)) = u32x4{0u, 0u, 0u, 0u};
+    }
     return;
   }
 
-  const int nchunks = (t1 - t0 + kC - 1) / kC;
-  const int64_t rid0 = record_id(t0, row, 0);
-  const int last = max(t1 - 1, 0);
+  const int nchunks = (a.t1 - a.t0 + kC - 1) / kC;
+  const int nseg = seg_count(p, nchunks);
+  a.rid0 = record_id(a.t0, row, 0);
   // chunks with a record (all of them unless the workspace is too small for the tokens)
-  const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - rid0)));
+  const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - a.rid0)));
+  const int ja = g * seg_chunks(p), jb = min(ja + seg_chunks(p), nrun);
   // Every load is unconditional: the record index and the tokens are clamped into range
   // (a load in a branch is waited on at the branch end). Operands of tokens past the end
   // meet zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
-  // Uniform bases and 32-bit lane offsets (the host bounds the token tensors below 2^30
-  // elements) keep the lane offsets in VGPRs that do not change from chunk to chunk.
-  const int kh = h / p.G;
-  auto record = [&](int j) -> const char* { return head_record(p, min(rid0 + j, p.records - 1), h); };
-  auto krecord = [&](int j) -> const char* { return key_record(p, min(rid0 + j, p.records - 1), kh); };
-  const uint32_t o_l = uint32_t(l * 16);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  ST* const my_state =
+      static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + a.c0 + l16) * kDK + 4 * l4;
 
-  if (wave == 0) {
-    // ---- the state chain. Tile kt of lane l holds S[16kt + 4 l4 + i][c0 + l16].
-    ST* const my_state =
-        static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + c0 + l16) * kDK + 4 * l4;
-    const int32_t fresh = p.fresh ? p.fresh[row] : 0;
-    f32x4 S[kKT];
+  if constexpr (PH == 0) {
+    if (g == 0) {
+      if (cb >= nb) return;
+      if (wave == 0) {
+        const int32_t fresh = p.fresh ? p.fresh[row] : 0;
+        f32x4 S[kKT];
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
-      S[kt] = fresh ? zero4 : s;
+        for (int kt = 0; kt < kKT; ++kt) {
+          const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
+          S[kt] = fresh ? zero4 : s;
+        }
+        state_chain<true, true>(p, L, a, S, 0, jb);
+        if (nseg == 1) {  // the final state back to the slot (rounded once for a bf16 pool)
+#pragma unroll
+          for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+        } else {
+          f32x4* dst = slot_block(p, sid, h, cb);
+#pragma unroll
+          for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
+        }
+      } else {
+        output_chain(p, L, a, 0, jb);
+      }
+      return;
     }
-    const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV + c0);
-    const uint32_t vrow_b = uint32_t(p.Hv) * uint32_t(p.DV) * 2u;
-    const uint32_t o_f = uint32_t(kRecF + 16 * l4);
-    const s16x4 eye = identity_b(l16, l4);
-    auto fetch = [&](int j) -> StateOps {
-      StateOps c;
-      const char* rec = record(j);
-      const char* krec = krecord(j);
+    if (g > nseg - 2) return;  // the last segment has no map to compose
+    if (wave == 0) {
+      if (cb >= nb) return;
+      f32x4 S[kKT];  // N_g: from zero, with the values
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) {
-        c.w[m] = *reinterpret_cast<const s16x8*>(rec + kRecW + m * 1024 + o_l);
-        c.kt[m] = *reinterpret_cast<const s16x8*>(krec + kKeyKT + m * 1024 + o_l);
-      }
-      c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l);  // the lower half
-      c.f = *reinterpret_cast<const f32x4*>(rec + o_f);
-      c.gc = *reinterpret_cast<const float*>(rec + kRecGC);
-      const uint32_t tok = uint32_t(min(t0 + j * kC + l16, last));
-      c.v = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4);
-      return c;
-    };
-    auto step = [&](const StateOps& c, int j) {
-      const int buf = j & 1;
-      // U = Tm diag(beta) V - W S_0 (V transposed by the identity product). The asm pins
-      // the state-independent products to this step: hoisted to the loop's start, they
-      // would wait for loads issued just before.
-      s16x4 v = c.v, tv = c.tv;
-      asm volatile("" : "+v"(v), "+v"(tv));
-      const f32x4 tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
-      // -W S_0 in two interleaved accumulators (half the dependent chain). The 16x16x16
-      // product above joins them through a vector add, not as an accumulator: a 16x16x32
-      // product reading the result of a 16x16x16 one needs five wait states, and the
-      // compiler does not always place them.
-      f32x4 u0 = zero4, u1 = zero4;
+      for (int kt = 0; kt < kKT; ++kt) S[kt] = zero4;
+      state_chain<true, false>(p, L, a, S, ja, jb);
+      f32x4* dst = slot_block(p, sid, h, cb);
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) {
-        const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
-        L.s[buf][m][l] = sB;
-        if (m & 1)
-          u1 = mfma32(c.w[m], sB, u1);
-        else
-          u0 = mfma32(c.w[m], sB, u0);
-      }
-      const f32x4 u = (u0 + u1) + tvv;
-      L.u[buf][l] = bf16x4(u);
-      barrier_lds();
-      // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
-      const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
+      for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
+    } else {
+      if (cb >= kKT) return;
+      f32x4 S[kKT];  // columns 16 cb .. 16 cb + 15 of M_g: from the identity, no values
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
-        S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
-    };
-    auto after = [&]() {
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) keep_after(S[kt]);
-    };
-    run_chunks<StateOps>(nrun, fetch, step, after);
-    // the final state back to the slot (rounded once for a bf16 pool)
+        for (int i = 0; i < 4; ++i) S[kt][i] = (16 * kt + 4 * l4 + i == 16 * cb + l16) ? 1.f : 0.f;
+      state_chain<false, false>(p, L, a, S, ja, jb);
+      // Tile (kt, cb) read as an A operand is its transpose; the identity product turns
+      // that back into the tile itself in the A layout, exactly (bf16 in, single terms).
+      const s16x4 eye = identity_b(l16, l4);
+      char* dst = reinterpret_cast<char*>(slot_map(p, sid, h));
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+      for (int kt = 0; kt < kKT; ++kt) {
+        const s16x4 tA = bf16x4(mfma(bf16x4(S[kt]), eye, zero4));
+        *reinterpret_cast<s16x4*>(dst + ((kt * (kKT / 2) + (cb >> 1)) * 64 + l) * 16 + (cb & 1) * 8) = tA;
+      }
+    }
   } else {
-    // ---- the outputs: O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T) with
-    //      (Q S_0)^T = S_0^T Q^T: lane (g, t) holds columns 4g .. 4g+3 of token t
-    const uint32_t o_gq = uint32_t(kRecGQ + 4 * l16);
-    auto fetch = [&](int j) -> OutOps {
-      OutOps c;
-      const char* rec = record(j);
-      const char* krec = krecord(j);
+    if (g == 0 || cb >= nb) return;
+    if (wave == 0) {
+      f32x4 S[kKT];
+      const f32x4* src = slot_block(p, max<int64_t>(sid - 1, 0), h, cb);  // the start state of segment g
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(krec + kKeyQ + m * 1024 + o_l);
-      c.pm = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l + 8);  // the upper half
-      c.gq = *reinterpret_cast<const float*>(rec + o_gq);
-      return c;
-    };
-    auto step = [&](const OutOps& c, int j) {
-      const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
-      barrier_lds();  // chunk j's S_0 and U are in buffer j & 1
-      // Every operand read from LDS gets its own registers and has arrived before the
-      // first product: no LDS return lands in a register a pending product still reads.
-      s16x8 sA[kKT / 2];
+      for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
+      state_chain<true, true>(p, L, a, S, ja, jb);
+      if (g == nseg - 1) {
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) sA[m] = L.s[buf][m][l];
-      s16x4 uA = L.u[buf][l];
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA));
-      f32x4 qs = zero4;
-#pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], c.q[m], qs);
-      const f32x4 pu = mfma(uA, c.pm, zero4);
-      float ov[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
-      if (l16 < n)
-        *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + h) * p.DV + c0 + 4 * l4) =
-            uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-    };
-    // the step ends in its store, so a memory clobber keeps the next loads after it
-    auto after = [&]() { asm volatile("" ::: "memory"); };
-    run_chunks<OutOps>(nrun, fetch, step, after);
+        for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+      }
+    } else {
+      output_chain(p, L, a, ja, jb);
+    }
   }
 }
 
-template <typename ST>
+// The start states of the segments after the first: S_1 is segment 0's end state, and
+// S_{g+1} = M_g S_g + N_g for g = 1 .. n-2, stored over N_g in the slot of segment g. One
+// wave per (sequence, v-head, 16 value columns); S_g and M_g enter the products in bf16,
+// as the chain's own S_0 does. 1-D grid, XCD-aware as in scan_kernel (unit = row * Hv + h).
+__global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
+  const int nb = p.DV / 16;
+  const int rest = int(blockIdx.x) / kXcds, cb = rest % nb;
+  const int64_t unit = int64_t(rest / nb) * kXcds + int(blockIdx.x) % kXcds;
+  if (unit >= int64_t(p.B) * p.Hv) return;
+  const int h = int(unit % p.Hv), row = int(unit / p.Hv);
+  const int32_t slot = p.idx[row];
+  if (slot < 0 || slot >= p.P) return;
+  const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
+  const int nchunks = (t1 - t0 + kC - 1) / kC;
+  const int nseg = seg_count(p, nchunks);
+  if (nseg < 3) return;
+  const int l = threadIdx.x & 63;
+  const int64_t sid0 = segment_id(p, t0, row, 0);
+  f32x4 S[kKT];
+  {
+    const f32x4* src = slot_block(p, min(sid0, p.segments - 1), h, cb);
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
+  }
+  for (int g = 1; g <= nseg - 2; ++g) {
+    const int64_t sid = min(sid0 + g, p.segments - 1);
+    const s16x8* map = slot_map(p, sid, h) + l;
+    f32x4* blk = slot_block(p, sid, h, cb);
+    s16x8 sB[kKT / 2];
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) sB[m] = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+      f32x4 acc = blk[kt * 64];  // N_g
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) acc = mfma32(map[(kt * (kKT / 2) + m) * 64], sB[m], acc);
+      S[kt] = acc;
+    }
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) blk[kt * 64] = S[kt];
+  }
+}
+
+template <typename ST, int PH>
 hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
-  const int64_t units = (int64_t(p.B) * p.Hv + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid(unsigned(units * (p.DV / 16)));
-  hipLaunchKernelGGL((scan_kernel<ST>), grid, dim3(128), 0, stream, p);
+  const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
+  const int ncb = PH == 0 ? std::max(p.DV / 16, kKT) : p.DV / 16;
+  hipLaunchKernelGGL((scan_kernel<ST, PH>), dim3(unsigned(units * ncb)), dim3(128), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
+  hipError_t e = launch_scan<ST, 0>(p, stream);
+  if (e != hipSuccess) return e;
+  // a sequence has at least three segments only if it is longer than two of them
+  if (p.tokens > (int64_t(2) << p.seg_shift)) {
+    const int64_t units = (int64_t(p.B) * p.Hv + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(combine_kernel, dim3(unsigned(units * (p.DV / 16))), dim3(64), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.tokens > (int64_t(1) << p.seg_shift)) e = launch_scan<ST, 2>(p, stream);
+  return e;
 }
 
 }  // namespace
@@ -530,7 +739,7 @@ hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
   hipLaunchKernelGGL(chunk_kernel, dim3(strides, unsigned(p.Hv), unsigned(p.B)), dim3(64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return state == Dt::F32 ? launch_scan<float>(p, stream) : launch_scan<bf16s>(p, stream);
+  return state == Dt::F32 ? launch_pass2<float>(p, stream) : launch_pass2<bf16s>(p, stream);
 }
 
 }  // namespace gdn

@@ -78,7 +78,7 @@ def check(w, x, label, seed=0):
     assert torch.equal(pool.cpu()[ut], pool0.cpu()[ut]), f"{label}: an untouched slot changed"
 
 
-@pytest.mark.parametrize("wi", [1, 2, 3], ids=[workloads.PREFILL_WORKLOADS[i].name for i in (1, 2, 3)])
+@pytest.mark.parametrize("wi", [1, 2, 3, 4], ids=[workloads.PREFILL_WORKLOADS[i].name for i in (1, 2, 3, 4)])
 def test_prefill_parity(wi):
     w = workloads.PREFILL_WORKLOADS[wi]
     check(w, workloads.make_prefill_inputs(w, seed=0), w.name)
@@ -109,6 +109,20 @@ def test_prefill_slow_decay_long_memory(state):
     w = PrefillWorkload(f"slow-{state}", seqlens=(2048, 333), Hk=2, Hv=4, dk=128, dv=128, pool=4,
                         state_dtype=state, io_dtype="bf16", n_fresh=1)
     x = workloads.make_prefill_inputs(w, seed=4)
+    x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
+    check(w, x, w.name)
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+def test_prefill_segment_boundaries(state):
+    """The chunk chain runs in segments of 256 tokens whose maps are composed: lengths at
+    and around the segment boundaries (one segment, a one-token second segment, two full
+    ones, the first composed map, three maps, an empty sequence), a padding row and a fresh
+    row, d_v = 64 (map columns past the value columns), and slow decay so that the composed
+    maps carry weight."""
+    w = PrefillWorkload(f"segments-{state}", seqlens=(256, 257, 0, 512, 513, 769, 300), Hk=1, Hv=2, dk=128, dv=64,
+                        pool=8, state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1)
+    x = workloads.make_prefill_inputs(w, seed=5)
     x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
     check(w, x, w.name)
 

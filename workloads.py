@@ -375,6 +375,9 @@ PREFILL_WORKLOADS: list[PrefillWorkload] = [
     PrefillWorkload("prefill-4x4096-f32", seqlens=(4096,) * 4, Hk=16, Hv=32, dk=128, dv=128, pool=16,
                     state_dtype="f32", io_dtype="bf16", n_fresh=2,
                     description="4 sequences x 4096 tokens, Hk=16, Hv=32, d=128, fp32 state, bf16 io"),
+    PrefillWorkload("prefill-1x16384-bf16", seqlens=(16384,), Hk=4, Hv=8, dk=128, dv=128, pool=2,
+                    state_dtype="bf16", io_dtype="bf16",
+                    description="one long prompt of 16384 tokens, Hk=4, Hv=8, d=128, bf16"),
 ]
 PREFILL_HEADLINE = 2
 
