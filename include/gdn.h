@@ -182,7 +182,7 @@ GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* sta
  * Segments hold 2^s tokens and number floor(num_tokens / 2^s) + batch. s is the smallest
  * s >= 8 with 2^s > num_tokens (one segment per sequence) when 2 * batch * num_v_heads *
  * d_v / 16 >= 512; otherwise the smallest s >= 8 with 2^s >= num_tokens * num_v_heads *
- * (d_v / 16) * 2 / 4096 (integer division), but no more than the first. Writes the size to
+ * (d_v / 16) * 2 / 2048 (integer division), but no more than the first. Writes the size to
  * *bytes; GDN_ERR_SHAPE for a negative num_tokens, the gdn_prefill geometry checks
  * otherwise. */
 GDN_API gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens, size_t* bytes);

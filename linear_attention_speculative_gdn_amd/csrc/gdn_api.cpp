@@ -157,7 +157,9 @@ int64_t prefill_records(const gdn_dims* d, int64_t num_tokens) { return num_toke
 // v-head, 16 value columns) is a state wave and an output wave; a chunk step keeps a SIMD
 // busy (two chains on one SIMD take twice as long per step), so splitting sequences into
 // segments, whose maps are composed afterwards, pays only when those waves leave most of
-// the chip's 1024 SIMDs idle. Then segments are sized so that about 4096 waves run; else a
+// the chip's 1024 SIMDs idle. Then segments are sized so that about 2048 waves run (one
+// 16384-token prompt with 8 v-heads: 16 segments; 4096 waves, 32 segments, and 1024
+// waves, 8 segments, measured 8 % and 6 % slower); else a
 // segment is longer than any sequence (N < 2^shift: every sequence is one segment, and
 // segment ids are the row numbers, with no gaps in the grid).
 int32_t prefill_seg_shift(const gdn_dims* d, int64_t num_tokens) {
@@ -165,7 +167,7 @@ int32_t prefill_seg_shift(const gdn_dims* d, int64_t num_tokens) {
   while ((int64_t(1) << whole) <= num_tokens) ++whole;
   const int64_t waves = int64_t(d->batch) * d->num_v_heads * (d->d_v / 16) * 2;
   if (waves >= 512) return whole;
-  const int64_t target = num_tokens * d->num_v_heads * (d->d_v / 16) * 2 / 4096;  // tokens per segment
+  const int64_t target = num_tokens * d->num_v_heads * (d->d_v / 16) * 2 / 2048;  // tokens per segment
   int32_t shift = 8;
   while ((int64_t(1) << shift) < target) ++shift;
   return std::min(shift, whole);

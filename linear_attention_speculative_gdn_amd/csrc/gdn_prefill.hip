@@ -688,22 +688,40 @@ __global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
   }
-  for (int g = 1; g <= nseg - 2; ++g) {
-    const int64_t sid = min(sid0 + g, p.segments - 1);
+  // The maps and N do not depend on the running state: those of step g + 1 load while
+  // step g computes (the step is otherwise one load round trip long).
+  struct Ops {
+    s16x8 map[kKT * kKT / 2];
+    f32x4 n[kKT];
+  };
+  auto fetch = [&](int g) -> Ops {
+    Ops o;
+    const int64_t sid = min(sid0 + min(g, nseg - 2), p.segments - 1);
     const s16x8* map = slot_map(p, sid, h) + l;
-    f32x4* blk = slot_block(p, sid, h, cb);
+    const f32x4* blk = slot_block(p, sid, h, cb);
+#pragma unroll
+    for (int i = 0; i < kKT * kKT / 2; ++i) o.map[i] = map[i * 64];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) o.n[kt] = blk[kt * 64];
+    return o;
+  };
+  Ops cur = fetch(1);
+  for (int g = 1; g <= nseg - 2; ++g) {
+    const Ops nxt = fetch(g + 1);  // clamped to the last map: a repeat load at the end
     s16x8 sB[kKT / 2];
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) sB[m] = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
-      f32x4 acc = blk[kt * 64];  // N_g
+      f32x4 acc = cur.n[kt];
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) acc = mfma32(map[(kt * (kKT / 2) + m) * 64], sB[m], acc);
+      for (int m = 0; m < kKT / 2; ++m) acc = mfma32(cur.map[kt * (kKT / 2) + m], sB[m], acc);
       S[kt] = acc;
     }
+    f32x4* blk = slot_block(p, min(sid0 + g, p.segments - 1), h, cb);
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) blk[kt * 64] = S[kt];
+    cur = nxt;
   }
 }
 

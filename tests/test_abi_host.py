@@ -160,7 +160,7 @@ def test_prefill_workspace_size(L):
     them, 2^s tokens each), a 4-byte table entry (the table padded to 256 bytes) and per
     v-head a slot of a 128 x d_v fp32 state and a 128 x 128 bf16 map. The segment length:
     longer than N (one segment per sequence) when the chains (2 B Hv d_v/16 waves) number
-    at least 512, else the power of two >= 256 nearest above N Hv (d_v/16) 2 / 4096."""
+    at least 512, else the power of two >= 256 nearest above N Hv (d_v/16) 2 / 2048."""
     def shift(B, Hv, dv, N):
         whole = 8
         while (1 << whole) <= N:
@@ -168,7 +168,7 @@ def test_prefill_workspace_size(L):
         if B * Hv * (dv // 16) * 2 >= 512:
             return whole
         s_ = 8
-        while (1 << s_) < N * Hv * (dv // 16) * 2 // 4096:
+        while (1 << s_) < N * Hv * (dv // 16) * 2 // 2048:
             s_ += 1
         return min(s_, whole)
 
@@ -177,14 +177,14 @@ def test_prefill_workspace_size(L):
         table = (segs * 4 + 255) // 256 * 256
         return (N // 16 + B) * (Hv * 5376 + Hk * 8192) + table + segs * Hv * (128 * dv * 4 + 128 * 128 * 2)
 
-    assert shift(4, 4, 128, 64) == 8 and shift(3, 32, 64, 16399) == 15 and shift(1, 8, 128, 16384) == 9
+    assert shift(4, 4, 128, 64) == 8 and shift(3, 32, 64, 16399) == 15 and shift(1, 8, 128, 16384) == 10
     assert prefill_ws(L, dims(batch=4, num_v_heads=4), 64) == (0, size(4, 2, 4, 128, 64))
     assert prefill_ws(L, dims(batch=4, num_v_heads=4), 64)[1] == (
         (4 + 4) * (4 * 5376 + 2 * 8192) + 256 + 4 * 4 * (128 * 128 * 4 + 128 * 128 * 2))
     assert prefill_ws(L, dims(batch=3, num_v_heads=32, d_v=64), 16384 + 15) == (0, size(3, 2, 32, 64, 16399))
     assert prefill_ws(L, dims(batch=1, num_k_heads=4, num_v_heads=8), 16384) == (0, size(1, 4, 8, 128, 16384))
     assert prefill_ws(L, dims(batch=1, num_k_heads=4, num_v_heads=8), 16384)[1] == (
-        (1024 + 1) * (8 * 5376 + 4 * 8192) + 256 + 33 * 8 * (128 * 128 * 4 + 128 * 128 * 2))
+        (1024 + 1) * (8 * 5376 + 4 * 8192) + 256 + 17 * 8 * (128 * 128 * 4 + 128 * 128 * 2))
     assert prefill_ws(L, dims(batch=0), 0) == (0, 0)
     assert prefill_ws(L, dims(), -1)[0] == 2
     assert prefill_ws(L, dims(d_k=64), 16)[0] == 5
