@@ -666,6 +666,8 @@ hipError_t launch_dk(int shape, int mode, bool ntl, const RecurrentArgs& p, hipS
       if (shape == 2) return launch_rec<ST, IT, 128, 2>(p, stream);
       if (shape == 12) return launch_rec<ST, IT, 128, 1, 2>(p, stream);
       if (shape == 14) return launch_rec<ST, IT, 128, 1, 8>(p, stream);
+      if (shape == 28)
+        return ntl ? launch_rec<ST, IT, 128, 2, 8, 0, false, true>(p, stream) : launch_rec<ST, IT, 128, 2, 8>(p, stream);
       return ntl ? launch_rec<ST, IT, 128, 1, 4, 0, false, true>(p, stream) : launch_rec<ST, IT, 128, 1>(p, stream);
     case 256: return launch_rec<ST, IT, 256, 1>(p, stream);
     default: return hipErrorInvalidValue;
