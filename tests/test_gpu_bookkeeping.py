@@ -253,6 +253,8 @@ EDGE = [
     dict(dk=128, dv=80, Hk=1, Hv=2, T=4),
     dict(dk=256, dv=256, Hk=1, Hv=2, T=2),
     dict(dk=128, dv=128, Hk=2, Hv=2, T=16),
+    dict(dk=128, dv=80, Hk=1, Hv=2, T=1),     # single token: a whole head per workgroup, rows past d_v masked
+    dict(dk=128, dv=256, Hk=2, Hv=4, T=1),    # single token: two workgroups per head
 ]
 
 

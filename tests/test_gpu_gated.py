@@ -101,6 +101,8 @@ GEOM = [
              io_dtype="f32", mode="decode", n_pad=3),
     Workload("g-t16-dk128-bf16", batch=4, T=16, Hk=1, Hv=2, dk=128, dv=128, pool=6, state_dtype="bf16",
              io_dtype="bf16", mode="verify", cache_T=16),
+    Workload("g-t6-dk128-dv48-f32", batch=5, T=6, Hk=1, Hv=2, dk=128, dv=48, pool=7, state_dtype="f32",
+             io_dtype="f32", mode="verify", cache_T=6, write_final=True, n_pad=1),
 ]
 
 
