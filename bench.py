@@ -452,6 +452,7 @@ def main():
     log(f"[bench] device copy ceiling: {copy_gbps:.1f} GB/s")
 
     tokens = w.batch * w.T
+    n_valid = int(((idx >= 0) & (idx < w.pool)).sum())
     value = tokens * args.steps / t_step
     res = {
         "metric": "GDN verify tokens/s (batch x T) + achieved HBM GB/s vs peak, T=4 bf16 state",
@@ -482,6 +483,9 @@ def main():
                      "algorithmic_bytes_per_launch": v_bytes,
                      "avg_launch_us": us_ver},
         "verify_tokens_per_s": tokens / (us_ver * 1e-6),
+        # padding rows cost a launch slot but no state traffic: the rate over the rows that do work
+        "valid_rows": n_valid,
+        "verify_valid_tokens_per_s": n_valid * w.T / (us_ver * 1e-6),
         "copy_ceiling_GBps": copy_gbps,
     }
     if not args.no_cpu and not replay and not gated:
