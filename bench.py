@@ -166,6 +166,29 @@ def copy_ceiling_gbps(dev) -> float:
     return gbps
 
 
+def single_cold_launches(fn, sets, stream, dev, n: int = 21) -> dict:
+    """Cross-check of the rotating-set protocol: n single launches of ``fn``, each after a
+    1 GiB scratch fill that evicts the L2s and the 256 MB Infinity Cache, timed one by one
+    with HIP events on the launch stream (each figure also holds one launch's event and
+    dispatch overhead, so it bounds the kernel time from above)."""
+    import torch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    us = []
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(sets[i % len(sets)])
+            e1.record(stream)
+            e1.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    us.sort()
+    return {"launches": n, "median_us": us[n // 2], "min_us": us[0],
+            "protocol": "each launch alone after a 1 GiB scratch fill"}
+
+
 def conv_main(args):
     """The short causal convolution kept next to the GDN state: one gdn_conv_update per
     step (fused commit of the previous step's accepted prefix, then this step's tokens;
@@ -450,6 +473,9 @@ def main():
 
     copy_gbps = copy_ceiling_gbps(dev)
     log(f"[bench] device copy ceiling: {copy_gbps:.1f} GB/s")
+    cold = single_cold_launches(verify, sets, stream, dev)
+    log(f"[bench] verify, single launches after a 1 GiB scratch fill: median {cold['median_us']:.2f} us, "
+        f"min {cold['min_us']:.2f} us")
 
     tokens = w.batch * w.T
     n_valid = int(((idx >= 0) & (idx < w.pool)).sum())
@@ -487,6 +513,7 @@ def main():
         "valid_rows": n_valid,
         "verify_valid_tokens_per_s": n_valid * w.T / (us_ver * 1e-6),
         "copy_ceiling_GBps": copy_gbps,
+        "single_cold_launch": cold,
     }
     if not args.no_cpu and not replay and not gated:
         log("[bench] CPU oracle baseline ...")
