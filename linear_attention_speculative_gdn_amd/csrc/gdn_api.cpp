@@ -45,15 +45,15 @@ gdn_status check_dims(const gdn_dims* d, bool need_tokens) {
 // on the decode and bf16 workloads: more, smaller workgroups reach their state
 // sooner and start storing earlier. Large fp32-state grids (a 64 KiB tile, many
 // rounds of workgroups) measured faster with 2-wave workgroups (16 value rows).
-// Single-token calls (decode) measured fastest with a whole head per workgroup (two rows
-// per lane, 8 waves): 13.7 -> 11.6 us on the fp32 decode batch (B = 64, 8 v-heads), as the
-// per-workgroup work before the state arrives (q and k loads, norms, LDS staging) is then
-// done once per head instead of once per 32 value rows; with T >= 4 that shape was
-// 10-16 % slower on every workload.
+// Single-token calls (decode) measured fastest with a whole head per workgroup (four rows
+// per lane, 4 waves): 13.7 -> 11.3 us on the fp32 decode batch (B = 64, 8 v-heads; two rows
+// and 8 waves: 11.6 us), as the per-workgroup work before the state arrives (q and k loads,
+// norms, LDS staging) is then done once per head instead of once per 32 value rows; with
+// T >= 4 whole-head shapes were 10-16 % slower on every workload.
 int pick_shape(const gdn_dims* d) {
   const int64_t tiles = int64_t(d->batch) * d->num_v_heads;
   if (d->state_dtype == GDN_DTYPE_F32 && tiles >= 4096) return 12;
-  if (d->T == 1) return 28;
+  if (d->T == 1) return 44;
   return 1;
 }
 
@@ -71,7 +71,7 @@ int pick_shape(const gdn_dims* d) {
 bool pick_nt_loads(const gdn_dims* d, bool replay) {
   if (replay) return true;
   const int shape = pick_shape(d);
-  return d->T <= 4 && (shape == 1 || shape == 28);
+  return d->T <= 4 && (shape == 1 || shape == 44);
 }
 
 gdn_status run_recurrent(const gdn_dims* d, const gdn_io* io, void* pool, const int32_t* idx,

@@ -55,8 +55,8 @@ struct CommitArgs {
 };
 
 // shape: 1 = one value row per lane, 4 waves; 2 = two rows per lane, 4 waves;
-// 12 = one row per lane, 2 waves; 14 = one row per lane, 8 waves; 28 = two rows per lane,
-// 8 waves (a whole head of d_v = 128 per workgroup) (d_k = 128 only).
+// 12 = one row per lane, 2 waves; 14 = one row per lane, 8 waves; 44 = four rows per lane,
+// 4 waves (a whole head of d_v = 128 per workgroup) (d_k = 128 only).
 // mode: 0 decode / verify, 1 cached-replay verify, 2 replay commit, 3 decode / verify
 // with the gated-norm output epilogue (modes 1-3 use their own fixed shapes).
 // Mode 3 needs d_v <= 256 for d_k <= 64 and d_v <= 128 for d_k >= 128.

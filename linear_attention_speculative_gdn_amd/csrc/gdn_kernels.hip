@@ -639,9 +639,14 @@ hipError_t launch_dk(int shape, int mode, bool ntl, const RecurrentArgs& p, hipS
       case 16: return launch_rec<ST, IT, 16, 1, 4, 0, true>(p, stream);    // 256 value rows
       case 32: return launch_rec<ST, IT, 32, 1, 8, 0, true>(p, stream);    // 256
       case 64: return launch_rec<ST, IT, 64, 2, 8, 0, true>(p, stream);    // 256
-      case 128:  // 128; with more than 4 tokens one row per lane and 16 waves measured 8 %
-                 // faster (T = 8: 255 -> 235 us), with 4 or fewer 13-29 % slower
+      case 128:  // 128 value rows in every shape, chosen by T as measured: one row per
+                 // lane and 16 waves above 4 tokens (T = 8: 255 -> 241 us against two rows
+                 // and 8 waves), four rows and 4 waves for 2-4 tokens (T = 4: 18.1 ->
+                 // 17.4 us), two rows and 8 waves for one token (11.0 us; 11.7 with four)
         if (p.T > 4) return launch_rec<ST, IT, 128, 1, 16, 0, true>(p, stream);
+        if (p.T > 1)
+          return ntl ? launch_rec<ST, IT, 128, 4, 4, 0, true, true>(p, stream)
+                     : launch_rec<ST, IT, 128, 4, 4, 0, true>(p, stream);
         return ntl ? launch_rec<ST, IT, 128, 2, 8, 0, true, true>(p, stream)
                    : launch_rec<ST, IT, 128, 2, 8, 0, true>(p, stream);
       case 256: return launch_rec<ST, IT, 256, 4, 8, 0, true>(p, stream);  // 128
@@ -668,8 +673,8 @@ hipError_t launch_dk(int shape, int mode, bool ntl, const RecurrentArgs& p, hipS
       if (shape == 2) return launch_rec<ST, IT, 128, 2>(p, stream);
       if (shape == 12) return launch_rec<ST, IT, 128, 1, 2>(p, stream);
       if (shape == 14) return launch_rec<ST, IT, 128, 1, 8>(p, stream);
-      if (shape == 28)
-        return ntl ? launch_rec<ST, IT, 128, 2, 8, 0, false, true>(p, stream) : launch_rec<ST, IT, 128, 2, 8>(p, stream);
+      if (shape == 44)
+        return ntl ? launch_rec<ST, IT, 128, 4, 4, 0, false, true>(p, stream) : launch_rec<ST, IT, 128, 4, 4>(p, stream);
       return ntl ? launch_rec<ST, IT, 128, 1, 4, 0, false, true>(p, stream) : launch_rec<ST, IT, 128, 1>(p, stream);
     case 256: return launch_rec<ST, IT, 256, 1>(p, stream);
     default: return hipErrorInvalidValue;
