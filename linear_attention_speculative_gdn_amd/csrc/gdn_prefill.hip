@@ -157,6 +157,10 @@ struct __attribute__((aligned(16))) ChunkLds {
   uint16_t tv[kC * kC];    // Tm diag(beta), bf16
 };
 
+// Pass 1 is bound by vector-instruction issue (about 1200 per chunk and v-head), so the
+// gates, decay ratios and norms use the hardware's approximate exp, log, reciprocal and
+// reciprocal square root (a few ulp; every product it feeds is rounded to bf16): 1500
+// instructions and 35.7 us with the library functions on 8 x 2048 tokens, 33.9 us now.
 // grid (chunk strides, v-heads, sequences), one wave each; wave x handles chunks x,
 // x + gridDim.x, ... of its sequence. Every product takes its operands straight from
 // registers: keys and queries are loaded in the operand layout, K^T comes from the
@@ -218,8 +222,8 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     }
     const size_t tg = size_t(min(cs + l16, last)) * p.Hv + h;
     const float x = bf(ag[tg]) + dtb;
-    float G = live ? A_neg * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))) : 0.f;  // log-decay
-    const float beta = live ? 1.f / (1.f + expf(-bf(bg[tg]))) : 0.f;
+    float G = live ? A_neg * (fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))) : 0.f;  // log-decay
+    const float beta = live ? __fdividef(1.f, 1.f + __expf(-bf(bg[tg]))) : 0.f;
 #pragma unroll
     for (int d = 1; d < kC; d *= 2) {  // inclusive prefix sum over the 16 tokens (per group)
       const float y = __shfl_up(G, d, 16);
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
       }
     sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
     sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
-    const float rk = 1.f / sqrtf(sk + p.eps), rq = 1.f / sqrtf(sq + p.eps);
+    const float rk = rsqrtf(sk + p.eps), rq = rsqrtf(sq + p.eps);
     // per-token values of the lane's four accumulator rows 4g + i (from group 0's lanes)
     float Gr[4], br[4], rkr[4];
 #pragma unroll
@@ -262,9 +266,9 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * l4 + i, s_ = l16;
-        L.a[t * kC + s_] = (s_ < t) ? br[i] * rkr[i] * rk * expf(Gr[i] - G) * KK[i] : 0.f;
+        L.a[t * kC + s_] = (s_ < t) ? br[i] * rkr[i] * rk * __expf(Gr[i] - G) * KK[i] : 0.f;
         const int sp = 4 * l4 + i, tp = l16;
-        pv[i] = (sp <= tp) ? rq * rkr[i] * expf(G - Gr[i]) * KQ[i] : 0.f;
+        pv[i] = (sp <= tp) ? rq * rkr[i] * __expf(G - Gr[i]) * KQ[i] : 0.f;
       }
       pA = bf16x4(pv[0], pv[1], pv[2], pv[3]);
     }
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
       for (int s_ = 0; s_ < kC - 1; ++s_)
 #pragma unroll
         for (int t = s_ + 1; t < kC; ++t) xs[t] = fmaf(-L.a[t * kC + s_], xs[s_], xs[t]);
-      const float cw = -beta * expf(G) * rk, cv = beta;  // lane c holds token c's values
+      const float cw = -beta * __expf(G) * rk, cv = beta;  // lane c holds token c's values
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
         L.tw[t * kC + c] = to_bf(xs[t] * cw);
@@ -308,9 +312,9 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     *reinterpret_cast<s16x8*>(rec + kRecTP + l * 16) = cat8(tvA, pA);
     const float Gl = __shfl(G, kC - 1);
     if (l < kC) {
-      reinterpret_cast<float*>(rec + kRecF)[l] = rk * expf(Gl - G);
-      reinterpret_cast<float*>(rec + kRecGQ)[l] = expf(G) * rq;
-      if (l == 0) *reinterpret_cast<float*>(rec + kRecGC) = expf(Gl);
+      reinterpret_cast<float*>(rec + kRecF)[l] = rk * __expf(Gl - G);
+      reinterpret_cast<float*>(rec + kRecGQ)[l] = __expf(G) * rq;
+      if (l == 0) *reinterpret_cast<float*>(rec + kRecGC) = __expf(Gl);
     }
     lds_sync();  // LDS is reused by the next chunk
   }
