@@ -340,17 +340,20 @@ __device__ __forceinline__ void store_state(bf16s* dst, const f32x4& s) {
 // What the state wave hands to the output wave per chunk, double-buffered by chunk parity:
 // one barrier per chunk suffices, since a wave writes buffer j & 1 only after the barrier
 // of chunk j - 1, which the output wave reaches after its reads of chunk j - 2 completed.
+// NCB 16-column tiles per wave.
+template <int NCB>
 struct __attribute__((aligned(16))) ScanLds {
-  s16x8 s[2][kKT / 2][64];  // bf16 S_0 in the B layout of 16x16x32, by 32-key block
-  s16x4 u[2][64];           // bf16 U in the accumulator layout
+  s16x8 s[2][NCB][kKT / 2][64];  // bf16 S_0 in the B layout of 16x16x32, by 32-key block
+  s16x4 u[2][NCB][64];           // bf16 U in the accumulator layout
 };
 
 // Operands of one chunk, loaded two chunks ahead: the state wave's and the output wave's.
+template <int NCB>
 struct StateOps {
   s16x8 w[kKT / 2];   // -W, A layout of 16x16x32
   s16x8 kt[kKT / 2];  // K^T tiles 2m, 2m+1, A layout of 16x16x16
   s16x4 tv;           // Tm diag(beta), A layout
-  s16x4 v;            // V of token l16, columns 4 l4 .. 4 l4 + 3 (A layout; transposed in use)
+  s16x4 v[NCB];       // V of token l16, columns 16 ct + 4 l4 .. + 3 (A layout; transposed in use)
   f32x4 f;            // f of tokens 4 l4 .. 4 l4 + 3
   float gc;           // Gam_C
 };
@@ -403,13 +406,14 @@ struct ChainArgs {
   int c0;        // first value column of the block (V and o)
 };
 
-// The state chain over chunks [ja, jb) with S in MFMA accumulators (tile kt of lane l holds
-// S[16kt + 4 l4 + i][column l16 of the block]): U = Tm diag(beta) V - W S_0, then the update.
+// The state chain over chunks [ja, jb) with S in MFMA accumulators (tile kt of column tile
+// ct of lane l holds S[16kt + 4 l4 + i][column 16 ct + l16 of the block]): U = Tm diag(beta)
+// V - W S_0, then the update. The NCB column tiles share every record load.
 // WITH_V: the Tm diag(beta) V term (off for a segment map, whose values are zero).
 // HANDOFF: bf16 S_0 and U go to the output wave through LDS, one barrier per chunk.
-template <bool WITH_V, bool HANDOFF>
-__device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds& L, const ChainArgs& a, f32x4 (&S)[kKT],
-                                            int ja, int jb) {
+template <bool WITH_V, bool HANDOFF, int NCB>
+__device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds<NCB>& L, const ChainArgs& a,
+                                            f32x4 (&S)[NCB][kKT], int ja, int jb) {
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const uint32_t o_l = uint32_t(l * 16);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -418,8 +422,8 @@ __device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds& L, co
   const uint32_t vrow_b = uint32_t(p.Hv) * uint32_t(p.DV) * 2u;
   const uint32_t o_f = uint32_t(kRecF + 16 * l4);
   const s16x4 eye = identity_b(l16, l4);
-  auto fetch = [&](int j) -> StateOps {
-    StateOps c;
+  auto fetch = [&](int j) -> StateOps<NCB> {
+    StateOps<NCB> c;
     const int64_t rid = min(a.rid0 + j, p.records - 1);
     const char* rec = head_record(p, rid, a.h);
     const char* krec = key_record(p, rid, a.kh);
@@ -433,57 +437,77 @@ __device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds& L, co
     if constexpr (WITH_V) {
       c.tv = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l);  // the lower half
       const uint32_t tok = uint32_t(min(a.t0 + j * kC + l16, last));
-      c.v = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4);
+#pragma unroll
+      for (int ct = 0; ct < NCB; ++ct)
+        c.v[ct] = *reinterpret_cast<const s16x4*>(vbase + tok * vrow_b + 8u * l4 + 32u * ct);
     }
     return c;
   };
-  auto step = [&](const StateOps& c, int j) {
+  auto step = [&](const StateOps<NCB>& c, int j) {
     const int buf = j & 1;
-    f32x4 tvv = zero4;
+    f32x4 tvv[NCB];
+#pragma unroll
+    for (int ct = 0; ct < NCB; ++ct) tvv[ct] = zero4;
     if constexpr (WITH_V) {
       // Tm diag(beta) V (V transposed by the identity product). The asm pins the
       // state-independent products to this step: hoisted to the loop's start, they would
       // wait for loads issued just before.
-      s16x4 v = c.v, tv = c.tv;
-      asm volatile("" : "+v"(v), "+v"(tv));
-      tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
-    }
-    // -W S_0 in two interleaved accumulators (half the dependent chain). The 16x16x16
-    // product above joins them through a vector add, not as an accumulator: a 16x16x32
-    // product reading the result of a 16x16x16 one needs five wait states, and the
-    // compiler does not always place them.
-    f32x4 u0 = zero4, u1 = zero4;
 #pragma unroll
-    for (int m = 0; m < kKT / 2; ++m) {
-      const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
-      if constexpr (HANDOFF) L.s[buf][m][l] = sB;
-      if (m & 1)
-        u1 = mfma32(c.w[m], sB, u1);
-      else
-        u0 = mfma32(c.w[m], sB, u0);
+      for (int ct = 0; ct < NCB; ++ct) {
+        s16x4 v = c.v[ct], tv = c.tv;
+        asm volatile("" : "+v"(v), "+v"(tv));
+        tvv[ct] = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+      }
     }
-    const f32x4 u = (u0 + u1) + tvv;
-    if constexpr (HANDOFF) {
-      L.u[buf][l] = bf16x4(u);
-      barrier_lds();
+    // -W S_0 in two interleaved accumulators per column tile (half the dependent chain).
+    // The 16x16x16 product above joins them through a vector add, not as an accumulator:
+    // a 16x16x32 product reading the result of a 16x16x16 one needs five wait states, and
+    // the compiler does not always place them.
+    f32x4 u0[NCB], u1[NCB];
+#pragma unroll
+    for (int ct = 0; ct < NCB; ++ct) u0[ct] = u1[ct] = zero4;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m)
+#pragma unroll
+      for (int ct = 0; ct < NCB; ++ct) {
+        const s16x8 sB = cat8(bf16x4(S[ct][2 * m]), bf16x4(S[ct][2 * m + 1]));
+        if constexpr (HANDOFF) L.s[buf][ct][m][l] = sB;
+        if (m & 1)
+          u1[ct] = mfma32(c.w[m], sB, u1[ct]);
+        else
+          u0[ct] = mfma32(c.w[m], sB, u0[ct]);
+      }
+    f32x4 u[NCB];
+#pragma unroll
+    for (int ct = 0; ct < NCB; ++ct) {
+      u[ct] = (u0[ct] + u1[ct]) + tvv[ct];
+      if constexpr (HANDOFF) L.u[buf][ct][l] = bf16x4(u[ct]);
     }
+    if constexpr (HANDOFF) barrier_lds();
     // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
-    const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
-      S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
+    for (int ct = 0; ct < NCB; ++ct) {
+      const s16x4 uB = bf16x4(c.f[0] * u[ct][0], c.f[1] * u[ct][1], c.f[2] * u[ct][2], c.f[3] * u[ct][3]);
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt)
+        S[ct][kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[ct][kt] * c.gc);
+    }
   };
   auto after = [&]() {
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) keep_after(S[kt]);
+    for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) keep_after(S[ct][kt]);
   };
-  run_chunks<StateOps>(ja, jb, fetch, step, after);
+  run_chunks<StateOps<NCB>>(ja, jb, fetch, step, after);
 }
 
 // The outputs of chunks [ja, jb), one chunk behind the state chain that hands them over:
 // O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T) with (Q S_0)^T = S_0^T Q^T: lane (g, t)
-// holds columns 4g .. 4g+3 of token t.
-__device__ __forceinline__ void output_chain(const PrefillArgs& p, ScanLds& L, const ChainArgs& a, int ja, int jb) {
+// holds columns 4g .. 4g+3 of token t, per column tile.
+template <int NCB>
+__device__ __forceinline__ void output_chain(const PrefillArgs& p, ScanLds<NCB>& L, const ChainArgs& a, int ja,
+                                             int jb) {
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const uint32_t o_l = uint32_t(l * 16);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -503,23 +527,39 @@ __device__ __forceinline__ void output_chain(const PrefillArgs& p, ScanLds& L, c
   auto step = [&](const OutOps& c, int j) {
     const int buf = j & 1, cs = a.t0 + j * kC, n = min(kC, a.t1 - cs);
     barrier_lds();  // chunk j's S_0 and U are in buffer j & 1
-    // Every operand read from LDS gets its own registers and has arrived before the
-    // first product: no LDS return lands in a register a pending product still reads.
-    s16x8 sA[kKT / 2];
+    // Every operand read from LDS, for all column tiles, gets its own registers and has
+    // arrived before the first product: no LDS return lands in a register a pending
+    // product still reads.
+    s16x8 sA[NCB][kKT / 2];
+    s16x4 uA[NCB];
 #pragma unroll
-    for (int m = 0; m < kKT / 2; ++m) sA[m] = L.s[buf][m][l];
-    s16x4 uA = L.u[buf][l];
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA));
-    f32x4 qs = zero4;
+    for (int ct = 0; ct < NCB; ++ct) {
 #pragma unroll
-    for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], c.q[m], qs);
-    const f32x4 pu = mfma(uA, c.pm, zero4);
-    float ov[4];
+      for (int m = 0; m < kKT / 2; ++m) sA[ct][m] = L.s[buf][ct][m][l];
+      uA[ct] = L.u[buf][ct][l];
+    }
+    if constexpr (NCB == 1) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sA[0][0]), "+v"(sA[0][1]), "+v"(sA[0][2]), "+v"(sA[0][3]),
+                   "+v"(uA[0]));
+    } else {
+      static_assert(NCB == 2, "one or two column tiles per wave");
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(sA[0][0]), "+v"(sA[0][1]), "+v"(sA[0][2]), "+v"(sA[0][3]), "+v"(uA[0]),
+                     "+v"(sA[1][0]), "+v"(sA[1][1]), "+v"(sA[1][2]), "+v"(sA[1][3]), "+v"(uA[1]));
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
-    if (l16 < n)
-      *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + a.h) * p.DV + a.c0 + 4 * l4) =
-          uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+    for (int ct = 0; ct < NCB; ++ct) {
+      f32x4 qs = zero4;
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[ct][m], c.q[m], qs);
+      const f32x4 pu = mfma(uA[ct], c.pm, zero4);
+      float ov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
+      if (l16 < n)
+        *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + a.h) * p.DV + a.c0 + 16 * ct + 4 * l4) =
+            uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+    }
   };
   // the step ends in its store, so a memory clobber keeps the next loads after it
   auto after = [&]() { asm volatile("" ::: "memory"); };
@@ -551,13 +591,13 @@ __device__ __forceinline__ s16x8* slot_map(const PrefillArgs& p, int64_t sid, in
 // Two waves per workgroup; 1-D grid, XCD-aware: the column blocks of a (segment, v-head)
 // read the same records, so they get ids on one XCD (id % 8 equal) and share its L2.
 // Unit u (= segment * Hv + h) and column block cb take id (u % 8) + 8 (cb + ncb (u / 8)).
-template <typename ST, int PH>
+template <typename ST, int PH, int NCB>
 __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
-  __shared__ ScanLds L;
+  __shared__ ScanLds<NCB> L;
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nb = p.DV / 16;
-  const int ncb = PH == 0 ? max(nb, kKT) : nb;
+  const int nb = p.DV / (16 * NCB);                    // blocks of 16 NCB value columns
+  const int ncb = PH == 0 ? max(nb, kKT / NCB) : nb;   // phase 0 also covers the d_k map columns
   const int rest = int(blockIdx.x) / kXcds, cb = rest % ncb;
   const int64_t unit = int64_t(rest / ncb) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
@@ -573,13 +613,16 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   a.t1 = p.cu[row + 1];
   a.h = h;
   a.kh = h / p.G;
-  a.c0 = cb * 16;
+  a.c0 = cb * 16 * NCB;
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
     if (PH == 0 && g == 0 && cb < nb) {
       uint16_t* og = static_cast<uint16_t*>(p.o);
-      for (int t = a.t0 + wave * 32 + (l >> 1); t < a.t1; t += 64)
-        *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + a.c0 + 8 * (l & 1)) = u32x4{0u, 0u, 0u, 0u};
+      const int n16 = (a.t1 - a.t0) * 2 * NCB;  // 16-byte pieces of the block's outputs
+      for (int e = wave * 64 + l; e < n16; e += 128) {
+        const int t = a.t0 + e / (2 * NCB), c = e % (2 * NCB);
+        *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + a.c0 + 8 * c) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     return;
   }
@@ -594,6 +637,7 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   // (a load in a branch is waited on at the branch end). Operands of tokens past the end
   // meet zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // column tile ct of the block: value rows c0 + 16 ct + l16 of the slot's state
   ST* const my_state =
       static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + a.c0 + l16) * kDK + 4 * l4;
 
@@ -602,68 +646,92 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
       if (cb >= nb) return;
       if (wave == 0) {
         const int32_t fresh = p.fresh ? p.fresh[row] : 0;
-        f32x4 S[kKT];
+        f32x4 S[NCB][kKT];
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
-          const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
-          S[kt] = fresh ? zero4 : s;
-        }
-        state_chain<true, true>(p, L, a, S, 0, jb);
+        for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+          for (int kt = 0; kt < kKT; ++kt) {
+            const f32x4 s = load_state<ST>(my_state + 16 * ct * kDK + 16 * kt);  // unconditional, then masked
+            S[ct][kt] = fresh ? zero4 : s;
+          }
+        state_chain<true, true, NCB>(p, L, a, S, 0, jb);
         if (nseg == 1) {  // the final state back to the slot (rounded once for a bf16 pool)
 #pragma unroll
-          for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
-        } else {
-          f32x4* dst = slot_block(p, sid, h, cb);
+          for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
-          for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
+            for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * ct * kDK + 16 * kt, S[ct][kt]);
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < NCB; ++ct) {
+            f32x4* dst = slot_block(p, sid, h, cb * NCB + ct);
+#pragma unroll
+            for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[ct][kt];
+          }
         }
       } else {
-        output_chain(p, L, a, 0, jb);
+        output_chain<NCB>(p, L, a, 0, jb);
       }
       return;
     }
     if (g > nseg - 2) return;  // the last segment has no map to compose
     if (wave == 0) {
       if (cb >= nb) return;
-      f32x4 S[kKT];  // N_g: from zero, with the values
+      f32x4 S[NCB][kKT];  // N_g: from zero, with the values
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) S[kt] = zero4;
-      state_chain<true, false>(p, L, a, S, ja, jb);
-      f32x4* dst = slot_block(p, sid, h, cb);
+      for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
+        for (int kt = 0; kt < kKT; ++kt) S[ct][kt] = zero4;
+      state_chain<true, false, NCB>(p, L, a, S, ja, jb);
+#pragma unroll
+      for (int ct = 0; ct < NCB; ++ct) {
+        f32x4* dst = slot_block(p, sid, h, cb * NCB + ct);
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[ct][kt];
+      }
     } else {
-      if (cb >= kKT) return;
-      f32x4 S[kKT];  // columns 16 cb .. 16 cb + 15 of M_g: from the identity, no values
+      if (cb >= kKT / NCB) return;
+      f32x4 S[NCB][kKT];  // columns 16 J .. 16 J + 15 of M_g (J = cb NCB + ct): from the identity, no values
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
+      for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[kt][i] = (16 * kt + 4 * l4 + i == 16 * cb + l16) ? 1.f : 0.f;
-      state_chain<false, false>(p, L, a, S, ja, jb);
-      // Tile (kt, cb) read as an A operand is its transpose; the identity product turns
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[ct][kt][i] = (16 * kt + 4 * l4 + i == 16 * (cb * NCB + ct) + l16) ? 1.f : 0.f;
+      state_chain<false, false, NCB>(p, L, a, S, ja, jb);
+      // Tile (kt, J) read as an A operand is its transpose; the identity product turns
       // that back into the tile itself in the A layout, exactly (bf16 in, single terms).
       const s16x4 eye = identity_b(l16, l4);
       char* dst = reinterpret_cast<char*>(slot_map(p, sid, h));
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        const s16x4 tA = bf16x4(mfma(bf16x4(S[kt]), eye, zero4));
-        *reinterpret_cast<s16x4*>(dst + ((kt * (kKT / 2) + (cb >> 1)) * 64 + l) * 16 + (cb & 1) * 8) = tA;
+      for (int ct = 0; ct < NCB; ++ct) {
+        const int J = cb * NCB + ct;
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) {
+          const s16x4 tA = bf16x4(mfma(bf16x4(S[ct][kt]), eye, zero4));
+          *reinterpret_cast<s16x4*>(dst + ((kt * (kKT / 2) + (J >> 1)) * 64 + l) * 16 + (J & 1) * 8) = tA;
+        }
       }
     }
   } else {
     if (g == 0 || cb >= nb) return;
     if (wave == 0) {
-      f32x4 S[kKT];
-      const f32x4* src = slot_block(p, max<int64_t>(sid - 1, 0), h, cb);  // the start state of segment g
+      f32x4 S[NCB][kKT];
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
-      state_chain<true, true>(p, L, a, S, ja, jb);
+      for (int ct = 0; ct < NCB; ++ct) {
+        const f32x4* src = slot_block(p, max<int64_t>(sid - 1, 0), h, cb * NCB + ct);  // segment g's start
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) S[ct][kt] = src[kt * 64];
+      }
+      state_chain<true, true, NCB>(p, L, a, S, ja, jb);
       if (g == nseg - 1) {
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+        for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+          for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * ct * kDK + 16 * kt, S[ct][kt]);
       }
     } else {
-      output_chain(p, L, a, ja, jb);
+      output_chain<NCB>(p, L, a, ja, jb);
     }
   }
 }
@@ -729,17 +797,28 @@ __global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
   }
 }
 
-template <typename ST, int PH>
+template <typename ST, int PH, int NCB>
 hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
-  const int ncb = PH == 0 ? std::max(p.DV / 16, kKT) : p.DV / 16;
-  hipLaunchKernelGGL((scan_kernel<ST, PH>), dim3(unsigned(units * ncb)), dim3(128), 0, stream, p);
+  const int nb = p.DV / (16 * NCB);
+  const int ncb = PH == 0 ? std::max(nb, kKT / NCB) : nb;
+  hipLaunchKernelGGL((scan_kernel<ST, PH, NCB>), dim3(unsigned(units * ncb)), dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
-  hipError_t e = launch_scan<ST, 0>(p, stream);
+  // Every column-block wave reads its chunk's records (about 9 KB for the state wave,
+  // 4.5 KB for the output wave) through L2; where two or more chains share each SIMD that
+  // traffic, not the chain, sets the step (8 x 2048 and 4 x 4096 tokens both ran at
+  // ~9.7 TB/s of record reads). Waves of two 16-column tiles read each record once for
+  // both: 4 x 4096 tokens with 32 v-heads (2048 chain waves) 466 -> 341 us. With one
+  // chain per SIMD the halved wave count costs more than it saves (8 x 2048: 127 -> 123
+  // us, mixed lengths: 32.6 -> 37.7 us), so only grids of >= 2048 chain waves, every
+  // sequence one segment, take it.
+  const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;
+  const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
+  hipError_t e = wide ? launch_scan<ST, 0, 2>(p, stream) : launch_scan<ST, 0, 1>(p, stream);
   if (e != hipSuccess) return e;
   // a sequence has at least three segments only if it is longer than two of them
   if (p.tokens > (int64_t(2) << p.seg_shift)) {
@@ -747,7 +826,7 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
     hipLaunchKernelGGL(combine_kernel, dim3(unsigned(units * (p.DV / 16))), dim3(64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (p.tokens > (int64_t(1) << p.seg_shift)) e = launch_scan<ST, 2>(p, stream);
+  if (p.tokens > (int64_t(1) << p.seg_shift)) e = launch_scan<ST, 2, 1>(p, stream);
   return e;
 }
 

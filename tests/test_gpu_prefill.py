@@ -127,6 +127,17 @@ def test_prefill_segment_boundaries(state):
     check(w, x, w.name)
 
 
+def test_prefill_wide_column_tiles():
+    """Batches with two or more chains per SIMD (2 B Hv d_v/16 >= 2048 waves) run the chain
+    on waves of two 16-column tiles: d_v = 96 (three such blocks per head), ragged
+    lengths, a padding row and a fresh row, bf16 and fp32 pools."""
+    for state in ("bf16", "f32"):
+        w = PrefillWorkload(f"wide-dv96-{state}", seqlens=(37, 130, 0, 16, 211, 64, 5, 96), Hk=4, Hv=32, dk=128,
+                            dv=96, pool=10, state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1)
+        assert 2 * w.batch * w.Hv * (w.dv // 16) >= 2048
+        check(w, workloads.make_prefill_inputs(w, seed=7), w.name)
+
+
 def test_prefill_split_continues_from_the_pool():
     """Two calls (a chunked prefill across scheduler steps, cut off a chunk boundary)
     follow the single call to the same tolerance."""
