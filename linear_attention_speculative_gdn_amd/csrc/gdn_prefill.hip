@@ -809,10 +809,10 @@ hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   // Every column-block wave reads its chunk's records (about 9 KB for the state wave,
-  // 4.5 KB for the output wave) through L2; where two or more chains share each SIMD that
-  // traffic, not the chain, sets the step (8 x 2048 and 4 x 4096 tokens both ran at
-  // ~9.7 TB/s of record reads). Waves of two 16-column tiles read each record once for
-  // both: 4 x 4096 tokens with 32 v-heads (2048 chain waves) 466 -> 341 us. With one
+  // 4.5 KB for the output wave) through L2. Where two chains share each SIMD, waves of two
+  // 16-column tiles, which read each record once and pay the per-chunk scalar and issue
+  // overheads once for both, are faster: 4 x 4096 tokens with 32 v-heads (2048 chain
+  // waves) 466 -> 341 us. With one
   // chain per SIMD the halved wave count costs more than it saves (8 x 2048: 127 -> 123
   // us, mixed lengths: 32.6 -> 37.7 us), so only grids of >= 2048 chain waves, every
   // sequence one segment, take it.
