@@ -102,8 +102,22 @@ def _p(x: np.ndarray | None, t=_D):
     return None if x is None else x.ctypes.data_as(t)
 
 
+def host_threads() -> int:
+    """Threads the oracle uses by default: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when that is set (a machine that shares its host between GPUs grants
+    each job a share through it)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def _nthreads(n):
-    return int(n) if n else (os.cpu_count() or 1)
+    return int(n) if n else host_threads()
 
 
 def softplus(x: float) -> float:

@@ -258,14 +258,22 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("variant", ["as-drawn", "rawqk-weakdecay"])
 @pytest.mark.parametrize("geo", EDGE, ids=[f"dk{e['dk']}-dv{e['dv']}-T{e['T']}" for e in EDGE])
 @pytest.mark.parametrize("state,io", [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"), ("bf16", "f32")])
-def test_edge_geometries_against_oracle(geo, state, io):
+def test_edge_geometries_against_oracle(geo, state, io, variant):
+    """Every supported d_k, ragged d_v, 1-16 tokens and all four dtype pairs against the
+    oracle; the second variant stores q and k unnormalised (norms 0.05-20, a zero vector,
+    a vector of norm 1e-3) and draws weak decays, so the in-kernel L2 normalisation (its
+    eps and its sums over the lanes of every d_k) and the carried state are what is
+    checked."""
     w = Workload("edge", batch=5, pool=8, state_dtype=state, io_dtype=io, mode="verify", cache_T=geo["T"] + 1,
                  write_final=True, n_pad=1, **geo)
+    if variant != "as-drawn":
+        w = w.replace(qk="raw", decay="weak")
     x = workloads.make_inputs(w, seed=14)
     g = to_gpu(w, x)
-    say(f"[edge] {geo} state={state} io={io}")
+    say(f"[edge] {geo} state={state} io={io} {variant}")
     gpu_step(w, g)
     torch.cuda.synchronize()
     ref = oracle_step(w, x)

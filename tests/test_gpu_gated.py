@@ -80,9 +80,14 @@ def run_case(w, seed=0):
     assert bool(torch.all(y[torch.from_numpy(pad)] == 0))
 
 
-@pytest.mark.parametrize("w", [workloads.WORKLOADS[i] for i in (1, 2, 4)],
-                         ids=[workloads.WORKLOADS[i].name for i in (1, 2, 4)])
+GATED_WL = [workloads.WORKLOADS[i] for i in (1, 2, 4)]
+GATED_WL += [w.replace(name=w.name + "-rawqk-weakdecay", qk="raw", decay="weak") for w in GATED_WL]
+
+
+@pytest.mark.parametrize("w", GATED_WL, ids=[w.name for w in GATED_WL])
 def test_gated_parity_workloads(w):
+    """The decode, MTP T=4 and T=8 fused workloads at full size; the rawqk-weakdecay
+    copies store q and k unnormalised and draw weak decays."""
     run_case(w)
 
 
@@ -106,9 +111,10 @@ GEOM = [
 ]
 
 
+@pytest.mark.parametrize("variant", ["as-drawn", "rawqk-weakdecay"])
 @pytest.mark.parametrize("w", GEOM, ids=[w.name for w in GEOM])
-def test_gated_geometries(w):
-    run_case(w, seed=3)
+def test_gated_geometries(w, variant):
+    run_case(w if variant == "as-drawn" else w.replace(qk="raw", decay="weak"), seed=3)
 
 
 def test_gated_unsupported_wide_dv():

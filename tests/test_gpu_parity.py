@@ -1,5 +1,13 @@
 """HIP path vs the float64 oracle on every workload, element by element, at full size
-and in the launch configuration the benchmark times."""
+and in the launch configuration the benchmark times.
+
+Besides the workloads as defined (q and k drawn as unit vectors, decays with a median
+of a few 1e-3), every mode runs at full size on inputs that exercise what those leave
+unseen: q and k stored unnormalised (norms 0.05-20, one zero vector and one of norm
+1e-3 each), so the kernels' own L2 normalisation decides the result; and weak decay
+(g about 0.9-0.999), so the state carried from token to token, into the intermediate
+cache and through the fused commit dominates every step. Both state dtypes run in each
+mode (decode, verify with cache and commit, verify with fused commit)."""
 import numpy as np
 import pytest
 import torch
@@ -13,11 +21,40 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
+def _raw_weak(w, **kw):
+    kw.setdefault("name", w.name)
+    return w.replace(qk="raw", decay="weak", **kw).replace(name=kw["name"] + "-rawqk-weakdecay")
+
+
+W = workloads.WORKLOADS
+VARIANTS = [
+    _raw_weak(W[1]),                                                             # decode, fp32
+    _raw_weak(W[1], name="decode-t1-bf16", state_dtype="bf16", io_dtype="bf16"),  # decode, bf16
+    _raw_weak(W[2]),                                                             # verify + commit, bf16
+    _raw_weak(W[2], name="mtp-verify-t4-f32", state_dtype="f32", io_dtype="f32"),  # verify + commit, fp32
+    _raw_weak(W[3]),                                                             # verify + commit, fp32, B=256
+    _raw_weak(W[4]),                                                             # fused commit, bf16
+    _raw_weak(W[4], name="verify-t8-f32-fused", state_dtype="f32", io_dtype="f32", batch=64, n_pad=6),
+]
+
+
 @pytest.mark.parametrize("wi", range(len(workloads.WORKLOADS)))
 def test_workload_parity(wi):
-    w = workloads.WORKLOADS[wi]
-    say(f"[parity] workload {wi} {w.name}: generating")
+    run_parity(workloads.WORKLOADS[wi], wi)
+
+
+@pytest.mark.parametrize("w", VARIANTS, ids=[v.name for v in VARIANTS])
+def test_unnormalised_qk_weak_decay_parity(w):
     x = workloads.make_inputs(w, seed=0)
+    n = x["q"].double().norm(dim=-1)
+    assert float(n.max()) > 10 and float(n[n > 0].min()) < 1e-2 and int((n == 0).sum()) == 1
+    run_parity(w, w.name, x)
+
+
+def run_parity(w, label, x=None):
+    say(f"[parity] workload {label} {w.name}: generating")
+    if x is None:
+        x = workloads.make_inputs(w, seed=0)
     g = to_gpu(w, x)
     say(f"[parity] {w.name}: GPU {w.mode}")
     gpu_step(w, g)

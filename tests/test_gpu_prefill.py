@@ -84,6 +84,21 @@ def test_prefill_parity(wi):
     check(w, workloads.make_prefill_inputs(w, seed=0), w.name)
 
 
+@pytest.mark.parametrize("wi", [1, 2, 3, 4], ids=[workloads.PREFILL_WORKLOADS[i].name for i in (1, 2, 3, 4)])
+def test_prefill_parity_unnormalised_qk_weak_decay(wi):
+    """The prefill workloads (mixed lengths; 8 x 2048; 4 x 4096 with 32 heads on two-column-
+    tile waves; one 16384-token prompt in composed segments) with q and k stored
+    unnormalised (norms 0.05-20, a zero vector and one of norm 1e-3 each) and weak decays:
+    the norms then enter the chunked form as the diagonal factors that scale the key and
+    query products, the masks and the records, and hundreds of tokens stay in the state."""
+    w = workloads.PREFILL_WORKLOADS[wi]
+    w = w.replace(name=w.name + "-rawqk-weakdecay", qk="raw", decay="weak")
+    x = workloads.make_prefill_inputs(w, seed=0)
+    n = x["k"].double().norm(dim=-1)
+    assert float(n.max()) > 10 and int((n == 0).sum()) == 1
+    check(w, x, w.name)
+
+
 GEOM = [
     PrefillWorkload("edges-dv32-f32", seqlens=(0, 1, 15, 16, 17, 33, 48), Hk=1, Hv=2, dk=128, dv=32, pool=9,
                     state_dtype="f32", io_dtype="bf16", n_fresh=2, n_pad=1),
@@ -96,8 +111,11 @@ GEOM = [
 ]
 
 
+@pytest.mark.parametrize("variant", ["as-drawn", "rawqk-weakdecay"])
 @pytest.mark.parametrize("w", GEOM, ids=[w.name for w in GEOM])
-def test_prefill_geometries(w):
+def test_prefill_geometries(w, variant):
+    if variant != "as-drawn":
+        w = w.replace(qk="raw", decay="weak")
     check(w, workloads.make_prefill_inputs(w, seed=1), w.name)
 
 
@@ -121,7 +139,7 @@ def test_prefill_segment_boundaries(state):
     row, d_v = 64 (map columns past the value columns), and slow decay so that the composed
     maps carry weight."""
     w = PrefillWorkload(f"segments-{state}", seqlens=(256, 257, 0, 512, 513, 769, 300), Hk=1, Hv=2, dk=128, dv=64,
-                        pool=8, state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1)
+                        pool=8, state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1, qk="raw")
     x = workloads.make_prefill_inputs(w, seed=5)
     x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
     check(w, x, w.name)
@@ -136,6 +154,8 @@ def test_prefill_wide_column_tiles():
                             dv=96, pool=10, state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1)
         assert 2 * w.batch * w.Hv * (w.dv // 16) >= 2048
         check(w, workloads.make_prefill_inputs(w, seed=7), w.name)
+        wr = w.replace(name=w.name + "-rawqk-weakdecay", qk="raw", decay="weak")
+        check(wr, workloads.make_prefill_inputs(wr, seed=7), wr.name)
 
 
 def test_prefill_split_continues_from_the_pool():

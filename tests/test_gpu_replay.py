@@ -46,9 +46,15 @@ SHAPES = [
 ]
 
 
+RAW_WEAK = [s.replace(name=s.name + "-rawqk-weakdecay", qk="raw", decay="weak") for s in SHAPES]
+
+
 @pytest.mark.parametrize("commit", [True, False])
-@pytest.mark.parametrize("w", SHAPES, ids=[s.name for s in SHAPES])
+@pytest.mark.parametrize("w", SHAPES + RAW_WEAK, ids=[s.name for s in SHAPES + RAW_WEAK])
 def test_replay_parity(w, commit):
+    """Replay lengths 0..T, with and without the commit, against the oracle. The
+    rawqk-weakdecay shapes store q and k (new and replayed tokens) unnormalised and draw
+    weak decays, so the replayed state carries its full weight into the new tokens."""
     say(f"[replay] {w.name} commit={commit}")
     x_prev, g_prev = dev_step(w, 1)
     x_cur, g_cur = dev_step(w, 2, x_prev["A_log"], x_prev["dt_bias"])

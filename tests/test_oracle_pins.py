@@ -437,3 +437,28 @@ def test_oracle_matches_its_golden_fixture(orc):
     r = make_golden.compute()
     np.testing.assert_allclose(r["o"].ravel(), g["o"], rtol=0, atol=1e-15)
     np.testing.assert_allclose(r["cache"][0, 1, 1].ravel(), g["cache_0_1_1"], rtol=0, atol=1e-15)
+
+
+def test_l2norm_eps_closed_form(orc):
+    """A key of norm 1e-3 with eps = 1e-6 is scaled by 1 / sqrt(|k|^2 + eps) = 1 / sqrt(2e-6),
+    so from S0 = 0 one token stores beta k vT / sqrt(2e-6) (a normalised length of 1/sqrt 2,
+    not 1); a zero query gives o = 0 and a zero key leaves the decayed state, with no NaN."""
+    rng = np.random.default_rng(21)
+    dk, dv = 8, 3
+    kdir = unit(rng.standard_normal(dk))
+    k = (kdir * 1e-3)[None, None]
+    q = rng.standard_normal((1, 1, dk))
+    v = rng.standard_normal((1, 1, dv))
+    b = np.array([[0.2]])
+    beta = 1.0 / (1.0 + math.exp(-0.2))
+    r = run(orc, S0=np.zeros((1, dk, dv)), q=q, k=k, v=v, a=np.array([[0.1]]), b=b, A_log=np.array([0.0]),
+            dt_bias=np.array([0.0]), eps=1e-6)
+    np.testing.assert_allclose(r["cache"][0, 0], beta * np.outer(k[0, 0], v[0, 0]) / math.sqrt(2e-6),
+                               rtol=1e-13, atol=0)
+    # zero query: o = 0 exactly; zero key: S1 = g S0
+    S0 = rng.standard_normal((1, dk, dv))
+    r = run(orc, S0=S0, q=np.zeros((1, 1, dk)), k=np.zeros((1, 1, dk)), v=v, a=np.array([[0.1]]), b=b,
+            A_log=np.array([0.0]), dt_bias=np.array([0.0]), eps=1e-6)
+    g = 1.0 / (1.0 + math.exp(0.1))
+    assert np.all(r["o"] == 0.0)
+    np.testing.assert_allclose(r["cache"][0, 0], g * S0[0], rtol=1e-15, atol=0)

@@ -27,6 +27,20 @@ draws in this fixed order):
 Values are stored in the workload's io / state dtype (bf16 by round-to-nearest-even
 through torch). The stored values are the inputs; nobody re-derives them.
 
+Two variants exercise what the unit-norm, fast-decay recipe leaves unseen (both drawn
+from a second generator, ``numpy.random.default_rng([seed, 1])``, after the draws
+above, so the default workloads are unchanged):
+- ``qk="raw"``: q and k are NOT normalised before storing. Each (row, token, k-head)
+  vector keeps its N(0,1) direction and is rescaled to a norm drawn log-uniformly in
+  [0.05, 20]; then one q and one k vector are set to zero and one q and one k vector
+  to norm 1e-3 (where eps = 1e-6 in |x|^2 + eps changes the normalised length by
+  about 30 %), at random positions. The kernels' own L2 normalisation is then what
+  makes the result right.
+- ``decay="weak"``: A_log = log U[0.02, 0.05) per v-head, so g = exp(-e^A_log
+  softplus(a + dt_bias)) lies around 0.9-0.999 (median about 0.97) instead of a median
+  of a few 1e-3: the state carried across tokens dominates each step, and errors in the
+  carry, the intermediate cache or the commit show at full weight.
+
 Logical layouts (row-major): q, k [B,T,Hk,dk]; v [B,T,Hv,dv]; a, b [B,T,Hv];
 A_log, dt_bias [Hv]; pool [P,Hv,dk,dv] holding S[i][j] (i: key index, j: value
 index); cache [B,cache_T,Hv,dk,dv]. The device keeps states transposed
@@ -60,6 +74,8 @@ class Workload:
     n_pad: int = 0
     fixed_indices: tuple | None = None
     description: str = ""
+    qk: str = "unit"          # "unit": q, k normalised before storing | "raw": see the module docstring
+    decay: str = "strong"     # "strong": A_log = log U[1,16) | "weak": A_log = log U[0.02, 0.05)
 
     @property
     def scale(self) -> float:
@@ -107,6 +123,32 @@ def _unit(x: np.ndarray) -> np.ndarray:
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
 
 
+def _raw_qk(q: np.ndarray, k: np.ndarray, rng: np.random.Generator) -> tuple[np.ndarray, np.ndarray]:
+    """Unnormalised q and k: each vector along its drawn direction, with a norm drawn
+    log-uniformly in [0.05, 20]; one q and one k vector zero, one of each at norm 1e-3."""
+    out = []
+    for x in (q, k):
+        d = _unit(x)
+        lead = d.shape[:-1]
+        norms = np.exp(rng.uniform(np.log(0.05), np.log(20.0), lead))
+        y = d * norms[..., None]
+        flat = y.reshape(-1, y.shape[-1])
+        if flat.shape[0] >= 2:
+            zi, si = rng.choice(flat.shape[0], size=2, replace=False)
+            flat[zi] = 0.0
+            flat[si] = d.reshape(-1, d.shape[-1])[si] * 1e-3
+        out.append(y)
+    return out[0], out[1]
+
+
+def _weak_a_log(Hv: int, rng: np.random.Generator) -> np.ndarray:
+    return np.log(rng.uniform(0.02, 0.05, Hv))
+
+
+def _variant(seed: int) -> np.random.Generator:
+    return np.random.default_rng([seed, 1])
+
+
 def make_inputs(w: Workload, seed: int = 0) -> dict:
     """Draw one batch of inputs for workload ``w``. Returns CPU torch tensors."""
     rng = np.random.default_rng(seed)
@@ -133,6 +175,12 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     # 4. state pool
     pool = rng.standard_normal((P, Hv, dk, dv), dtype=np.float32)
     pool *= np.float32(0.1)
+    if w.qk == "raw" or w.decay == "weak":
+        vr = _variant(seed)
+        if w.qk == "raw":
+            q, k = _raw_qk(q, k, vr)
+        if w.decay == "weak":
+            A_log = _weak_a_log(Hv, vr)
     out = dict(
         idx=torch.from_numpy(idx),
         q=_store(q, w.io_dtype), k=_store(k, w.io_dtype), v=_store(v, w.io_dtype),
@@ -331,7 +379,8 @@ def make_gate_inputs(w: Workload, seed: int = 0) -> dict:
 # Recipe (one ``numpy.random.default_rng(seed)``, in this order): slot indices as for the
 # GDN workloads (n_pad rows set to -1); fresh flags: n_fresh distinct rows; q, k ~ N(0,1)
 # L2-normalised per vector; v, a, b ~ N(0,1); A_log = log U[1,16), dt_bias ~ N(0, 0.1);
-# the pool ~ N(0, 0.1) in float32.
+# the pool ~ N(0, 0.1) in float32. The "raw" q/k and "weak" decay variants are those of
+# the module docstring, drawn the same way.
 
 
 @dataclasses.dataclass(frozen=True)
@@ -348,6 +397,11 @@ class PrefillWorkload:
     n_fresh: int = 0
     n_pad: int = 0
     description: str = ""
+    qk: str = "unit"          # as for Workload: "raw" keeps q, k unnormalised
+    decay: str = "strong"     # as for Workload: "weak" draws A_log = log U[0.02, 0.05)
+
+    def replace(self, **kw) -> "PrefillWorkload":
+        return dataclasses.replace(self, **kw)
 
     @property
     def batch(self) -> int:
@@ -402,6 +456,12 @@ def make_prefill_inputs(w: PrefillWorkload, seed: int = 0) -> dict:
     A_log = np.log(rng.uniform(1.0, 16.0, Hv))
     dt_bias = rng.normal(0.0, 0.1, Hv)
     pool = rng.standard_normal((P, Hv, dk, dv), dtype=np.float32) * np.float32(0.1)
+    if w.qk == "raw" or w.decay == "weak":
+        vr = _variant(seed)
+        if w.qk == "raw":
+            q, k = _raw_qk(q, k, vr)
+        if w.decay == "weak":
+            A_log = _weak_a_log(Hv, vr)
     return dict(idx=torch.from_numpy(idx), fresh=torch.from_numpy(fresh), cu_seqlens=torch.from_numpy(cu),
                 q=_store(q, w.io_dtype), k=_store(k, w.io_dtype), v=_store(v, w.io_dtype),
                 a=_store(a, w.io_dtype), b=_store(b, w.io_dtype),
