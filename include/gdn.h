@@ -45,10 +45,10 @@
  *   the pointers are not examined then (empty tensors may have NULL data).
  * - Host-checkable faults return an error before anything is launched; nothing is
  *   written. A failed launch returns GDN_ERR_LAUNCH.
- * - The library allocates nothing, never synchronises, keeps no global state and
- *   launches its kernels (one per call; two to four for gdn_prefill) on `stream` (a
- *   hipStream_t; NULL is the default stream). Calls are therefore thread-safe and may
- *   be captured in a HIP graph.
+ * - The library allocates nothing, never synchronises, keeps no global state (but for
+ *   the per-GPU address of gdn_prefill_noalloc's fixed array) and launches its kernels
+ *   (one per call; two to four for gdn_prefill) on `stream` (a hipStream_t; NULL is the
+ *   default stream). Calls are therefore thread-safe and may be captured in a HIP graph.
  * - Supported geometry: d_k in {16, 32, 64, 128, 256}; d_v a multiple of 16 in
  *   [16, 256]; Hv a multiple of Hk; 1 <= T <= GDN_MAX_T.
  * - Alignment: q, k, v, o, state_pool and inter_cache 16-byte aligned; the others
@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 #define GDN_API __attribute__((visibility("default")))
 #define GDN_MAX_T 16
 
@@ -79,7 +79,8 @@ typedef enum {
   GDN_ERR_DTYPE = 3,       /* unknown dtype value */
   GDN_ERR_ALIGN = 4,       /* a pointer misses its alignment */
   GDN_ERR_UNSUPPORTED = 5, /* valid but outside the supported geometry */
-  GDN_ERR_LAUNCH = 6       /* the kernel launch failed */
+  GDN_ERR_LAUNCH = 6,      /* the kernel launch failed */
+  GDN_ERR_TOO_LARGE = 7    /* the call needs more than the library's fixed prefill array */
 } gdn_status;
 
 typedef struct {
@@ -170,6 +171,25 @@ GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* sta
                                const int32_t* state_indices, const int32_t* cu_seqlens,
                                const int32_t* fresh, int64_t num_tokens, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* gdn_prefill without allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * workspace is not the caller's but a fixed device array inside the library of
+ * GDN_PREFILL_NOALLOC_BYTES (128 MiB), one copy per GPU, held from the first call on that
+ * GPU until the process ends. Everything else -- arguments, layouts, results, bit for bit,
+ * and errors -- is gdn_prefill's. Calls whose workspace (gdn_prefill_workspace_bytes) would
+ * exceed the array return GDN_ERR_TOO_LARGE before anything runs (at Hk = 4, Hv = 8, d_v =
+ * 128: about 26,000 packed tokens in one sequence). The array's device address is looked up
+ * on the first call for a GPU (the GPU of `stream`, or the current one for the NULL stream), so a caller
+ * that captures graphs makes one call before capturing; a failed lookup returns
+ * GDN_ERR_LAUNCH. No call allocates, frees or synchronises. Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents (nothing in it needs to start at
+ * zero): calls that overlap in time on one GPU, on different streams or threads, race and
+ * must be ordered by the caller. */
+#define GDN_PREFILL_NOALLOC_BYTES ((size_t)128 << 20)
+GDN_API gdn_status gdn_prefill_noalloc(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                                       const int32_t* state_indices, const int32_t* cu_seqlens,
+                                       const int32_t* fresh, int64_t num_tokens, void* stream);
 
 /* Workspace size of gdn_prefill, in three parts:
  * - per 16-token chunk, (floor(num_tokens / 16) + batch) of them, one 5376-byte record per

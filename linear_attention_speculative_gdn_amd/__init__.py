@@ -22,10 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
-          5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH"}
-EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_prefill_workspace_bytes", "gdn_commit",
-            "gdn_verify_replay", "gdn_commit_replay", "gdn_conv_update", "gdn_conv_commit", "gdn_status_string",
-            "gdn_abi_version")
+          5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_TOO_LARGE"}
+EXPORTED = ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_prefill_noalloc",
+            "gdn_prefill_workspace_bytes", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay", "gdn_conv_update",
+            "gdn_conv_commit", "gdn_status_string", "gdn_abi_version")
+GDN_PREFILL_NOALLOC_BYTES = 128 << 20
 GDN_CONV_MAX_WIDTH = 8
 GDN_MAX_T = 16
 
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_commit.argtypes = [D, vp, i32, vp, vp, vp, vp]
         L.gdn_verify_gated.argtypes = [D, I, ctypes.POINTER(GdnOutGate), vp, vp, vp, i32, i32, vp, vp]
         L.gdn_prefill.argtypes = [D, I, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_size_t, vp]
+        L.gdn_prefill_noalloc.argtypes = [D, I, vp, vp, vp, vp, ctypes.c_int64, vp]
         L.gdn_prefill_workspace_bytes.argtypes = [D, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
         TK = ctypes.POINTER(GdnTokens)
         L.gdn_verify_replay.argtypes = [D, I, vp, vp, TK, vp, i32, vp]
@@ -89,8 +91,9 @@ def lib() -> ctypes.CDLL:
         CD = ctypes.POINTER(GdnConvDims)
         L.gdn_conv_update.argtypes = [CD, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp]
         L.gdn_conv_commit.argtypes = [CD, vp, vp, vp, vp, vp]
-        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_prefill_workspace_bytes",
-                  "gdn_commit", "gdn_verify_replay", "gdn_commit_replay", "gdn_conv_update", "gdn_conv_commit"):
+        for f in ("gdn_decode", "gdn_verify", "gdn_verify_gated", "gdn_prefill", "gdn_prefill_noalloc",
+                  "gdn_prefill_workspace_bytes", "gdn_commit", "gdn_verify_replay", "gdn_commit_replay",
+                  "gdn_conv_update", "gdn_conv_commit"):
             getattr(L, f).restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
@@ -385,12 +388,9 @@ def gdn_prefill_workspace_bytes(batch, num_tokens, num_k_heads, num_v_heads, d_k
     return int(out.value)
 
 
-def gdn_prefill(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh=None, *,
-                scale=None, l2norm_eps=1e-6, workspace=None, stream=None) -> None:
-    """Prefill of variable-length sequences from pooled initial states (zero where fresh[r]);
-    o for every token, the final state back to each valid slot. `workspace` is a device
-    uint8 tensor of at least gdn_prefill_workspace_bytes(...) bytes (allocated per call when
-    omitted); cu_seqlens[-1] must not exceed q.shape[0]."""
+def _prefill_args(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh, scale,
+                  l2norm_eps):
+    """Checks of the prefill tensors; returns (dims, io, N)."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a HIP device")
@@ -417,16 +417,47 @@ def gdn_prefill(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_
     if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
         raise TypeError("A_log and dt_bias must be float32")
     dims = _prefill_dims(B, N, Hk, Hv, dk, dv, state_pool.shape[0], _dt(state_pool), _dt(q), scale, l2norm_eps)
+    io = GdnIo(q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
+               dt_bias.data_ptr(), o.data_ptr())
+    return dims, io, N
+
+
+def gdn_prefill(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh=None, *,
+                scale=None, l2norm_eps=1e-6, workspace=None, stream=None) -> None:
+    """Prefill of variable-length sequences from pooled initial states (zero where fresh[r]);
+    o for every token, the final state back to each valid slot. `workspace` is a device
+    uint8 tensor of at least gdn_prefill_workspace_bytes(...) bytes; when it is omitted one
+    is allocated for the call, which a call under HIP graph capture must not do (it raises
+    then: pass a workspace, or use gdn_prefill_noalloc). cu_seqlens[-1] must not exceed
+    q.shape[0]."""
+    dims, io, N = _prefill_args(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh,
+                                scale, l2norm_eps)
+    dev = q.device
     if workspace is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("gdn_prefill: no workspace given under HIP graph capture; pass a workspace of "
+                               "gdn_prefill_workspace_bytes(...) bytes or call gdn_prefill_noalloc")
         need = ctypes.c_size_t(0)
         _raise(lib().gdn_prefill_workspace_bytes(ctypes.byref(dims), N, ctypes.byref(need)), "gdn_prefill")
         workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", 1, dev)
     if workspace.dtype != torch.uint8:
         raise TypeError("workspace must be a uint8 tensor")
-    io = GdnIo(q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), A_log.data_ptr(),
-               dt_bias.data_ptr(), o.data_ptr())
     st = lib().gdn_prefill(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
                            _ptr(cu_seqlens), _ptr(fresh), N, _ptr(workspace), workspace.numel(),
                            _stream(dev, stream))
     _raise(st, "gdn_prefill")
+
+
+def gdn_prefill_noalloc(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh=None, *,
+                        scale=None, l2norm_eps=1e-6, stream=None) -> None:
+    """gdn_prefill with its workspace in the library's fixed per-GPU device array
+    (GDN_PREFILL_NOALLOC_BYTES): nothing is allocated, so it may run under HIP graph
+    capture once one call has run on the GPU outside it. Raises GdnError with
+    GDN_ERR_TOO_LARGE when the call needs more than the array. Calls on one GPU share the
+    array: overlapping calls race."""
+    dims, io, N = _prefill_args(q, k, v, a, b, A_log, dt_bias, o, state_pool, state_indices, cu_seqlens, fresh,
+                                scale, l2norm_eps)
+    st = lib().gdn_prefill_noalloc(ctypes.byref(dims), ctypes.byref(io), _ptr(state_pool), _ptr(state_indices),
+                                   _ptr(cu_seqlens), _ptr(fresh), N, _stream(q.device, stream))
+    _raise(st, "gdn_prefill_noalloc")

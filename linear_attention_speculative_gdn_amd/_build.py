@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("gdn_kernels.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gdn_kernels.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_noalloc.hip",
+                                            "gdn_api.cpp")]
 
 # gfx950 only. Packed fp32 ops are switched off for every HIP translation unit. Matrix-core
 # results go to ordinary VGPRs (the prefill scan converts and rescales its accumulators

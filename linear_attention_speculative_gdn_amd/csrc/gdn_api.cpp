@@ -1,6 +1,7 @@
 // gdn_api.cpp -- the C ABI of include/gdn.h: argument validation, kernel choice and
-// launch. No allocation, no synchronisation, no global state; one launch per call (two
-// for the prefill).
+// launch. No allocation and no synchronisation; one launch per call (two to four for the
+// prefill). The only global state is the per-device address of the fixed prefill array
+// that gdn_prefill_noalloc uses (gdn_noalloc.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -204,6 +205,38 @@ gdn_status check_prefill(const gdn_dims* d, int64_t num_tokens) {
   return GDN_OK;
 }
 
+// Pointer and alignment checks of a prefill call (the workspace aside).
+gdn_status check_prefill_ptrs(const gdn_io* io, const void* pool, const int32_t* idx, const int32_t* cu,
+                              const int32_t* fresh) {
+  if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o || !pool ||
+      !idx || !cu)
+    return GDN_ERR_NULL;
+  if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->o, 16) ||
+      !aligned(pool, 16) || !aligned(io->a, 2) || !aligned(io->b, 2) || !aligned(io->A_log, 4) ||
+      !aligned(io->dt_bias, 4) || !aligned(idx, 4) || !aligned(cu, 4) || (fresh && !aligned(fresh, 4)))
+    return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+// Launch of a checked prefill call with a workspace of sufficient size.
+gdn_status run_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool, const int32_t* state_indices,
+                       const int32_t* cu_seqlens, const int32_t* fresh, int64_t num_tokens, void* workspace,
+                       void* stream) {
+  const int64_t records = prefill_records(dims, num_tokens);
+  gdn::PrefillArgs p;
+  p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
+  p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
+  p.pool = state_pool; p.idx = state_indices; p.fresh = fresh; p.cu = cu_seqlens;
+  p.work = workspace; p.records = records;
+  p.segments = prefill_segments(dims, num_tokens); p.tokens = num_tokens;
+  p.seg_shift = prefill_seg_shift(dims, num_tokens);
+  p.B = dims->batch; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.DV = dims->d_v;
+  p.P = dims->pool_slots; p.G = dims->num_v_heads / dims->num_k_heads;
+  p.scale = dims->scale; p.eps = dims->l2norm_eps;
+  const hipError_t e = gdn::launch_prefill(static_cast<Dt>(dims->state_dtype), p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,31 +280,31 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_dims* dims, int64_t num_tokens,
 gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* state_pool, const int32_t* state_indices,
                        const int32_t* cu_seqlens, const int32_t* fresh, int64_t num_tokens, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  const gdn_status s = check_prefill(dims, num_tokens);
+  gdn_status s = check_prefill(dims, num_tokens);
   if (s != GDN_OK) return s;
   if (dims->batch == 0) return GDN_OK;
-  const int64_t records = prefill_records(dims, num_tokens);
   if (workspace_bytes < prefill_workspace(dims, num_tokens)) return GDN_ERR_SHAPE;
-  if (!io || !io->q || !io->k || !io->v || !io->a || !io->b || !io->A_log || !io->dt_bias || !io->o ||
-      !state_pool || !state_indices || !cu_seqlens || !workspace)
-    return GDN_ERR_NULL;
-  if (!aligned(io->q, 16) || !aligned(io->k, 16) || !aligned(io->v, 16) || !aligned(io->o, 16) ||
-      !aligned(state_pool, 16) || !aligned(io->a, 2) || !aligned(io->b, 2) || !aligned(io->A_log, 4) ||
-      !aligned(io->dt_bias, 4) || !aligned(state_indices, 4) || !aligned(cu_seqlens, 4) ||
-      (fresh && !aligned(fresh, 4)) || !aligned(workspace, 256))
-    return GDN_ERR_ALIGN;
-  gdn::PrefillArgs p;
-  p.q = io->q; p.k = io->k; p.v = io->v; p.a = io->a; p.b = io->b;
-  p.A_log = io->A_log; p.dt_bias = io->dt_bias; p.o = io->o;
-  p.pool = state_pool; p.idx = state_indices; p.fresh = fresh; p.cu = cu_seqlens;
-  p.work = workspace; p.records = records;
-  p.segments = prefill_segments(dims, num_tokens); p.tokens = num_tokens;
-  p.seg_shift = prefill_seg_shift(dims, num_tokens);
-  p.B = dims->batch; p.Hk = dims->num_k_heads; p.Hv = dims->num_v_heads; p.DV = dims->d_v;
-  p.P = dims->pool_slots; p.G = dims->num_v_heads / dims->num_k_heads;
-  p.scale = dims->scale; p.eps = dims->l2norm_eps;
-  const hipError_t e = gdn::launch_prefill(static_cast<Dt>(dims->state_dtype), p, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+  if ((s = check_prefill_ptrs(io, state_pool, state_indices, cu_seqlens, fresh)) != GDN_OK) return s;
+  if (!workspace) return GDN_ERR_NULL;
+  if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+  return run_prefill(dims, io, state_pool, state_indices, cu_seqlens, fresh, num_tokens, workspace, stream);
+}
+
+gdn_status gdn_prefill_noalloc(const gdn_dims* dims, const gdn_io* io, void* state_pool,
+                               const int32_t* state_indices, const int32_t* cu_seqlens, const int32_t* fresh,
+                               int64_t num_tokens, void* stream) {
+  gdn_status s = check_prefill(dims, num_tokens);
+  if (s != GDN_OK) return s;
+  if (prefill_workspace(dims, num_tokens) > GDN_PREFILL_NOALLOC_BYTES) return GDN_ERR_TOO_LARGE;
+  if (dims->batch == 0) return GDN_OK;
+  if ((s = check_prefill_ptrs(io, state_pool, state_indices, cu_seqlens, fresh)) != GDN_OK) return s;
+  // the fixed array of the GPU the kernels run on: the stream's, or the current one
+  int device = 0;
+  const hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return GDN_ERR_LAUNCH;
+  void* work = nullptr;
+  if (gdn::noalloc_scratch(device, &work) != hipSuccess) return GDN_ERR_LAUNCH;
+  return run_prefill(dims, io, state_pool, state_indices, cu_seqlens, fresh, num_tokens, work, stream);
 }
 
 gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int32_t cache_T,
@@ -400,6 +433,8 @@ const char* gdn_status_string(gdn_status status) {
     case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not aligned as required";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: geometry outside the supported set";
     case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: kernel launch failed";
+    case GDN_ERR_TOO_LARGE:
+      return "GDN_ERR_TOO_LARGE: the call needs more than the library's fixed prefill array";
   }
   return "GDN: unknown status";
 }

@@ -124,6 +124,10 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream);
 
+// Device address of the library's fixed prefill array on `device` (gdn_noalloc.hip),
+// resolved with hipGetSymbolAddress on the first call for that device.
+hipError_t noalloc_scratch(int device, void** out);
+
 // Commit launch: 1024-thread workgroups of 4 16-byte chunks per thread (one tile of up
 // to 64 KiB per workgroup). Measured against 256 threads: verify + commit on the MTP T=4
 // bf16 batch 22.5 -> 21.9 us, on the T=4 fp32 B=256 batch 674 -> 662 us; 8 chunks per

@@ -216,6 +216,25 @@ def test_prefill_validation(L):
     assert pf(dims(), i=io(q=A16 + 8)) == 4
 
 
+def test_prefill_noalloc_validation(L):
+    """The fixed-array prefill refuses, before touching a GPU, a call whose workspace
+    exceeds the array (GDN_ERR_TOO_LARGE), and checks sizes and pointers like gdn_prefill."""
+    def pf(d, i=None, pool=A16 * 9, idx=A16 * 10, cu=A16 * 11, fresh=None, n=64):
+        i = io() if i is None else i
+        return L.gdn_prefill_noalloc(ctypes.byref(d), ctypes.byref(i), pool, idx, cu, fresh, n, None)
+    big = dims(batch=1, num_k_heads=4, num_v_heads=8)
+    fits = max(n for n in range(0, 40000, 16) if prefill_ws(L, big, n)[1] <= gdn.GDN_PREFILL_NOALLOC_BYTES)
+    assert 25000 <= fits <= 27000                             # about 26,000 tokens at Hk = 4, Hv = 8, d_v = 128
+    assert pf(big, n=fits + 16) == 7 and pf(dims(batch=0), n=1 << 19) == 7
+    assert pf(dims(batch=0)) == 0
+    assert pf(dims(io_dtype=gdn.GDN_DTYPE_F32)) == 5
+    assert pf(dims(), n=-1) == 2
+    assert pf(dims(), cu=None) == 1
+    assert pf(dims(), i=io(k=None)) == 1
+    assert pf(dims(), i=io(o=A16 + 8)) == 4
+    assert pf(dims(), fresh=A16 * 12 + 2) == 4
+
+
 def tokens(**kw):
     base = dict(k=A16 * 13, v=A16 * 14, a=A16 * 15, b=A16 * 16, T_src=4)
     base.update(kw)
