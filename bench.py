@@ -5,22 +5,28 @@ request, every intermediate state stored) followed by ``gdn_commit`` of the acce
 prefix, on the MTP verify workload (B=64, Hk=4, Hv=8, d=128, bf16 state, pool of
 256 slots; synthetic seeded inputs). Inputs are resident in HBM before timing starts.
 
-Timing: the steps run from a HIP graph (launch cost off the clock) over R rotating
-buffer sets whose combined footprint exceeds the 256 MB Infinity Cache, so every
-launch reads and writes HBM. W warm-up steps, then exactly K timed steps between two
-synchronisations; value = B*T*K / elapsed (tokens/s). The dominant kernel (verify) is
-also timed on its own the same way to give its average launch duration, from which
-the roofline fraction is computed with the algorithmic bytes of one call.
+Timing: the steps run from HIP graphs (launch cost off the clock) over R rotating
+buffer sets whose state reads together exceed the 256 MB Infinity Cache four times, so
+every launch reads and writes HBM. The sets are used in one rotation that continues
+across the warm-up, the timed steps and every later timing: at any step count each
+timed launch uses a set that the previous R-1 launches did not touch. W warm-up steps,
+then exactly K timed steps between two synchronisations (HIP events on the launch
+stream); value = B*T*K / elapsed (tokens/s). The dominant kernel (verify) is then timed
+on its own the same way; its average launch duration gives the roofline fraction with
+the algorithmic bytes of one call, and its rate is also compared with a streaming copy
+of the same read:write mix timed under the same protocol (the practical ceiling).
 
 Prints ONE JSON line on stdout; details go to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -29,22 +35,29 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published figure
+# fp32 vector FMA without packed (two-lane) instructions, which this build does not use:
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz (half the 157.3 TFLOP/s packed figure)
+VALU_F32_PEAK_TFLOPS = 78.6
 INFINITY_CACHE_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRCS = [os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "csrc", f)
-               for f in ("gdn_kernels.hip", "gdn_device.h")]
+CSRC = os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "csrc")
+KERNEL_SRCS = {
+    "recurrent": ["gdn_kernels.hip", "gdn_device.h", "gdn_internal.h", "gdn_api.cpp"],
+    "conv": ["gdn_conv.hip", "gdn_device.h", "gdn_internal.h", "gdn_api.cpp"],
+    "prefill": ["gdn_prefill.hip", "gdn_device.h", "gdn_internal.h", "gdn_api.cpp"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the recurrent kernel's sources without comments and blank lines: a
-    comment edit does not invalidate counter figures taken on the same code."""
+def kernel_source_hash(kind: str) -> str:
+    """Hash of a kernel family's sources (and the launch code) without comments and blank
+    lines: a comment edit does not invalidate counter figures taken on the same code."""
     code = []
-    for path in KERNEL_SRCS:
-        with open(path) as fh:
+    for name in KERNEL_SRCS[kind]:
+        with open(os.path.join(CSRC, name)) as fh:
             for line in fh:
                 line = line.split("//", 1)[0].strip()
                 if line:
@@ -52,79 +65,121 @@ def kernel_source_hash() -> str:
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload_name: str):
-    """HBM bytes per verify launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"gdn_verify_{workload_name}_traffic.json")
+def traffic_from_profiles(entry: str, workload_name: str, kind: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    ``profiles/<entry>_<workload>_traffic.json``, if it was taken on the current source of
+    the kernel family; else None."""
+    path = os.path.join(PROFILES, f"{entry}_{workload_name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(kind):
+        log(f"[bench] {os.path.basename(path)} was taken on other kernel sources: traffic not reported")
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, budget_s: float) -> dict:
-    """The float64 oracle, as it stands, on the same inputs: full verify + commit calls,
-    repeated until the time budget is spent (at least once)."""
-    import oracle
+    """The float64 oracle, as it stands, on the same inputs: full verify + commit calls
+    (the oracle's own C functions on prepared float64 arrays, input preparation outside
+    the clock), repeated for budget/3 seconds, three times; the median rate of the three.
+    Threads: every CPU this process may use, within OMP_NUM_THREADS (the box's share)."""
     import numpy as np
-    nthreads = min(16, os.cpu_count() or 1)
-    f = {n: x[n].double().numpy() for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "pool")}
-    idx, acc = x["idx"].numpy(), x["accept"].numpy()
+
+    import oracle
+    nthreads = oracle.host_threads()
+    f = {n: np.ascontiguousarray(x[n].double().numpy()) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    idx, acc = x["idx"].numpy().astype(np.int32), x["accept"].numpy().astype(np.int32)
     d = oracle.make_dims(w.batch, w.T, w.Hk, w.Hv, w.dk, w.dv, w.pool, w.state_dtype == "bf16", scale=w.scale)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        r = oracle.verify(d, f["q"], f["k"], f["v"], f["a"], f["b"], f["A_log"], f["dt_bias"], f["pool"], idx,
-                          cache_T=w.cache_T, write_final=w.write_final, nthreads=nthreads)
-        oracle.commit(d, r["cache"], w.cache_T, idx, acc, r["pool"], nthreads=nthreads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    del np
-    return {"value": reps * w.batch * w.T / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{reps} full verify+commit calls of the workload (B*T={w.batch * w.T} tokens each) "
-                      f"in {el:.1f} s, float64, OpenMP over (row, v-head) tiles"}
+    pool0 = np.ascontiguousarray(x["pool"].double().numpy())
+    cache = np.zeros((w.batch, w.cache_T, w.Hv, w.dk, w.dv))
+    rates, calls = [], []
+    for _ in range(3):
+        pool = pool0.copy()
+        reps, el = 0, 0.0
+        while el < budget_s / 3 or reps == 0:
+            t0 = time.perf_counter()
+            oracle.verify_commit_inplace(d, f["q"], f["k"], f["v"], f["a"], f["b"], f["A_log"], f["dt_bias"], pool,
+                                         idx, cache, w.cache_T, acc, nthreads=nthreads)
+            el += time.perf_counter() - t0
+            reps += 1
+        rates.append(reps * w.batch * w.T / el)
+        calls.append(reps)
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count() or 1
+    return {"value": statistics.median(rates), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"3 runs of about {budget_s / 3:.0f} s, each full verify + commit calls of the workload "
+                      f"(B*T={w.batch * w.T} tokens per call; {'/'.join(map(str, calls))} calls), float64, "
+                      f"OpenMP over (row, v-head) tiles; median of the 3 rates",
+            "runs_tokens_per_s": rates, "nproc": nproc, "hardware_concurrency": os.cpu_count(),
+            "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+class Rotation:
+    """Position of the next launch in the rotation over the buffer sets, shared by every
+    runner of those sets."""
+
+    def __init__(self, nsets: int):
+        self.nsets, self.pos = nsets, 0
 
 
 class Runner:
-    """n calls of ``fn`` over rotating buffer sets, replayed from HIP graphs captured
-    beforehand (``prepare(n)`` captures whatever ``run(n)`` replays), or launched eagerly."""
+    """n calls of ``fn`` over rotating buffer sets from the rotation's current position,
+    replayed from HIP graphs captured beforehand (``prepare(n)`` captures whatever
+    ``run(n)`` replays), or launched eagerly."""
 
-    def __init__(self, fn, sets, stream, eager: bool, per_replay: int):
-        self.fn, self.sets, self.stream, self.eager, self.per_replay = fn, sets, stream, eager, per_replay
-        self.graphs, self.pos = {}, 0
+    def __init__(self, fn, sets, rot: Rotation, stream, eager: bool, per_replay: int):
+        assert per_replay % len(sets) == 0
+        self.fn, self.sets, self.rot, self.stream, self.eager = fn, sets, rot, stream, eager
+        self.per_replay = per_replay
+        self.graphs = {}
 
-    def _capture(self, n):
+    def _capture(self, start, n):
         import torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=self.stream):
             for i in range(n):
-                self.fn(self.sets[i % len(self.sets)])
+                self.fn(self.sets[(start + i) % len(self.sets)])
         return g
+
+    def _pieces(self, n):
+        """(first set, calls) of the graph replays that make n calls from the current position."""
+        full, rest = divmod(n, self.per_replay)
+        start = self.rot.pos % len(self.sets)
+        out = [(start, self.per_replay)] * full        # a multiple of the set count: same start
+        if rest:
+            out.append((start, rest))
+        return out
 
     def prepare(self, n):
         if self.eager:
             return
-        full, rest = divmod(n, self.per_replay)
-        for k in ([self.per_replay] if full else []) + ([rest] if rest else []):
-            if k not in self.graphs:
-                self.graphs[k] = self._capture(k)
+        for key in self._pieces(n):
+            if key not in self.graphs:
+                self.graphs[key] = self._capture(*key)
 
     def run(self, n):
         if self.eager:
             for i in range(n):
-                self.fn(self.sets[(self.pos + i) % len(self.sets)])
-            self.pos += n
-            return
-        full, rest = divmod(n, self.per_replay)
-        for _ in range(full):
-            self.graphs[self.per_replay].replay()
-        if rest:
-            self.graphs[rest].replay()
+                self.fn(self.sets[(self.rot.pos + i) % len(self.sets)])
+        else:
+            for key in self._pieces(n):
+                self.graphs[key].replay()
+        self.rot.pos += n
 
     def warm(self, n):
         import torch
@@ -134,13 +189,19 @@ class Runner:
         torch.cuda.synchronize()
 
     def timed(self, n) -> float:
-        """Seconds for n calls, HIP events on the launch stream."""
+        """Seconds for n calls, HIP events on the launch stream. The stream is held for
+        200 us (gdn_stream_wait) before the first event, so that the event is stamped when
+        the calls behind it are queued and the host's submission latency stays off the
+        clock."""
         import torch
         self.prepare(n)
         cs = self.stream if not self.eager else torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(cs):
+            st = stream_lib().gdn_stream_wait(200000, ctypes.c_void_p(cs.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"gdn_stream_wait returned {st}")
             e0.record(cs)
             self.run(n)
             e1.record(cs)
@@ -148,22 +209,82 @@ class Runner:
         return e0.elapsed_time(e1) * 1e-3
 
 
-def copy_ceiling_gbps(dev) -> float:
-    """A plain 1 GiB device copy, same event protocol: the practical streaming ceiling."""
+def rotating_sets(read_bytes: int, set_bytes: int) -> int:
+    """Buffer sets so that the state reads of one rotation exceed the Infinity Cache four
+    times (nontemporal writes do not displace read data from it, so reads are what count),
+    within 16 GB of buffers."""
+    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / max(1, read_bytes)))
+    return min(R, 1024, max(2, int(16e9 // max(1, set_bytes))))
+
+
+def per_replay_of(R: int) -> int:
+    return R * max(1, 200 // R)
+
+
+_stream_lib = None
+
+
+def stream_lib():
+    global _stream_lib
+    if _stream_lib is None:
+        path = os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "libgdn_stream.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        L.gdn_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
+            ctypes.c_void_p]
+        L.gdn_stream_copy.restype = ctypes.c_int32
+        L.gdn_stream_wait.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+        L.gdn_stream_wait.restype = ctypes.c_int32
+        _stream_lib = L
+    return _stream_lib
+
+
+# (threads per workgroup, 16-byte chunks per thread, flags: 1 nontemporal loads, 2
+# nontemporal stores, 4 copy-major) of the streaming-copy variants timed for the ceiling:
+# the fastest of a sweep over 64/256/1024 threads, 1-8 chunks and the flags, at the read:write
+# mixes of decode (1:1), the MTP T=4 verify (1:4) and the T=8 verify (1:9)
+COPY_VARIANTS = ((64, 8, 7), (64, 1, 3), (64, 1, 4), (256, 2, 3), (256, 2, 7))
+
+
+def copy_ceiling(dev, read_bytes: int, writes: int, launches: int, eager: bool) -> dict:
+    """The streaming copy of libgdn_stream.so moving the state bytes of one call
+    (`read_bytes` in, `writes` x out) over rotating cold buffer sets, replayed from graphs
+    like the kernel it is compared with, for each variant of COPY_VARIANTS: the best rate is
+    the practical HBM ceiling for that mix."""
     import torch
-    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    gbps = 10 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
-    return gbps
+    L = stream_lib()
+    unit = 64 * 8 * 16                                # a multiple of every variant's block
+    rd = max(1, read_bytes // unit) * unit
+    R = rotating_sets(rd, rd * (1 + writes))
+    sets = [{"src": torch.empty(rd, dtype=torch.uint8, device=dev).fill_(i & 0xFF),
+             "dst": torch.empty(rd * writes, dtype=torch.uint8, device=dev)} for i in range(R)]
+    stream = torch.cuda.Stream()
+    moved = rd * (1 + writes)
+    n = max(launches, 2 * R)
+    results = []
+    for th, ch, fl in COPY_VARIANTS:
+        def call(s, th=th, ch=ch, fl=fl):
+            st = L.gdn_stream_copy(ctypes.c_void_p(s["src"].data_ptr()), ctypes.c_void_p(s["dst"].data_ptr()), rd,
+                                   writes, th, ch, fl, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"gdn_stream_copy returned {st}")
+        with torch.cuda.stream(stream):
+            call(sets[0])
+        torch.cuda.synchronize()
+        run = Runner(call, sets, Rotation(R), stream, eager, per_replay_of(R))
+        run.warm(R)
+        us = run.timed(n) / n * 1e6
+        results.append({"threads": th, "chunks": ch, "nontemporal_loads": bool(fl & 1),
+                        "nontemporal_stores": bool(fl & 2), "order": "copy-major" if fl & 4 else "block-major",
+                        "us_per_launch": us, "GBps": moved / (us * 1e-6) / 1e9})
+        del run
+    del sets
+    torch.cuda.empty_cache()
+    best = max(results, key=lambda r: r["GBps"])
+    return {"GBps": best["GBps"], "us_per_launch": best["us_per_launch"], "bytes_per_launch": moved,
+            "mix": f"1 read : {writes} write{'s' if writes > 1 else ''}", "rotating_buffer_sets": R,
+            "launches": n, "kernel": "gdn_stream_copy (libgdn_stream.so)", "best": best, "variants": results}
 
 
 def single_cold_launches(fn, sets, stream, dev, n: int = 21) -> dict:
@@ -189,11 +310,23 @@ def single_cold_launches(fn, sets, stream, dev, n: int = 21) -> dict:
             "protocol": "each launch alone after a 1 GiB scratch fill"}
 
 
+def calibration_copy(dev):
+    """256 MiB read + 256 MiB written, launched alone: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 pass to bytes."""
+    import torch
+    a_ = torch.ones(1 << 27, dtype=torch.bfloat16, device=dev)
+    b_ = torch.empty_like(a_)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b_.copy_(a_)
+        torch.cuda.synchronize()
+    del a_, b_
+
+
 def conv_main(args):
     """The short causal convolution kept next to the GDN state: one gdn_conv_update per
     step (fused commit of the previous step's accepted prefix, then this step's tokens;
     write-back for the decode workload), same cold protocol as the GDN path."""
-    import numpy as np
     import torch
 
     import linear_attention_speculative_gdn_amd as gdn
@@ -211,8 +344,7 @@ def conv_main(args):
     esz = x["x"].element_size()
     state_read = int(((idx >= 0) & (idx < w.pool)).sum()) * (w.width - 1) * w.channels * esz
     set_bytes = sum(x[n].numel() * x[n].element_size() for n in ("x", "prev_x", "pool")) + x["x"].numel() * esz
-    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / max(1, state_read)))
-    R = min(R, 1024, max(2, int(16e9 // set_bytes)))
+    R = rotating_sets(state_read, set_bytes)
     shared = {n: x[n].to(dev) for n in ("idx", "prev_len", "w", "bias")}
     sets = []
     for _ in range(R):
@@ -230,7 +362,9 @@ def conv_main(args):
 
     call(sets[0])
     torch.cuda.synchronize()
-    run = Runner(call, sets, torch.cuda.Stream(), args.eager, R * max(1, 200 // R))
+    if args.calibrate_copy:
+        calibration_copy(dev)
+    run = Runner(call, sets, Rotation(R), torch.cuda.Stream(), args.eager, per_replay_of(R))
     run.warm(args.warmup)
     t = run.timed(args.steps)
     us = t / args.steps * 1e6
@@ -240,17 +374,18 @@ def conv_main(args):
         "metric": "GDN short-conv update tokens/s (batch x T) + achieved HBM GB/s vs peak",
         "value": w.batch * w.T / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "storage_dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "T": w.T, "channels": w.channels, "width": w.width,
                    "pool_slots": w.pool, "dtype": w.dtype, "activation": w.activation,
                    "step": "conv update" + (" with fused commit" if fused else "") + (" + write-back" if wb else ""),
                    "rotating_buffer_sets": R, "launch": "eager" if args.eager else "hip_graph",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "gdn_conv_update (conv_kernel)",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profiles("gdn_conv_update", w.name, "conv"),
+                     "kernel": "gdn_conv_update (conv_kernel)",
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": us},
     }
-    del np
     print(json.dumps(res), flush=True)
 
 
@@ -290,7 +425,9 @@ def prefill_main(args):
 
     call(sets[0])
     torch.cuda.synchronize()
-    run = Runner(call, sets, torch.cuda.Stream(), args.eager, 2)
+    if args.calibrate_copy:
+        calibration_copy(dev)
+    run = Runner(call, sets, Rotation(R), torch.cuda.Stream(), args.eager, 2)
     run.warm(args.warmup)
     t = run.timed(args.steps)
     us = t / args.steps * 1e6
@@ -303,7 +440,8 @@ def prefill_main(args):
             if hbm_bound else
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": tflops / MFMA_BF16_PEAK_TFLOPS})
-    roof.update({"traffic": None, "kernel": "gdn_prefill (chunk_kernel + scan_kernel)",
+    roof.update({"traffic": traffic_from_profiles("gdn_prefill", w.name, "prefill"),
+                 "kernel": "gdn_prefill (chunk_kernel + scan_kernel)",
                  "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
                  "avg_launch_us": us, "mfma_TFLOPs": tflops,
                  "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS})
@@ -311,7 +449,7 @@ def prefill_main(args):
         "metric": "GDN chunked prefill tokens/s + achieved HBM GB/s or MFMA TFLOP/s vs the binding peak",
         "value": w.tokens / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "storage_dtype": w.state_dtype, "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.batch, "tokens": w.tokens, "num_k_heads": w.Hk,
                    "num_v_heads": w.Hv, "d_k": w.dk, "d_v": w.dv, "state_dtype": w.state_dtype,
                    "io_dtype": w.io_dtype, "chunk": 16, "launch": "eager" if args.eager else "hip_graph",
@@ -319,6 +457,17 @@ def prefill_main(args):
         "roofline": roof,
     }
     print(json.dumps(res), flush=True)
+
+
+def replay_flops(w, idx, rlen) -> int:
+    """Flops of one cached-replay call, each multiply-add counted as 2: per state element,
+    a new token takes S^T k, S^T q and the rank-1 update (3 multiply-adds, plus the decay
+    scaling: 7 flop), a replayed token S^T k and the update (5 flop); valid rows only."""
+    import numpy as np
+    valid = (idx >= 0) & (idx < w.pool)
+    n = np.where(valid & (rlen >= 0) & (rlen <= w.T), rlen, 0)
+    elems = w.Hv * w.dk * w.dv
+    return int(valid.sum()) * w.T * 7 * elems + int(n.sum()) * 5 * elems
 
 
 def main():
@@ -338,6 +487,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the copy ceiling and the single cold launches (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (known bytes) for counter calibration")
     args = ap.parse_args()
@@ -366,6 +517,7 @@ def main():
     idx = x["idx"].numpy()
     replay = args.mode == "replay"
     gated = args.mode == "gated"
+    rlen = None
     if replay:
         if w.mode == "decode":
             sys.exit("bench.py: replay mode needs a verify workload")
@@ -382,16 +534,14 @@ def main():
         nvalid = int(((idx >= 0) & (idx < w.pool)).sum())
         v_bytes += nvalid * w.T * w.Hv * w.dv * xg["z"].element_size() + w.dv * 4
 
-    # Rotating buffer sets, so that every launch reads its state from HBM: the pool
-    # reads of all sets together exceed the 256 MB Infinity Cache four times over
-    # (nontemporal cache writes do not displace them, so only the reads are counted).
-    # Slot indices and accept lengths are shared by all sets, as every GDN layer of a
-    # serving step uses the same ones; everything else is per set.
+    # Rotating buffer sets, so that every launch reads its state from HBM. Slot indices and
+    # accept lengths are shared by all sets, as every GDN layer of a serving step uses the
+    # same ones; everything else is per set.
     touched = v_bytes + c_bytes
+    state_read = workloads.state_read_bytes(w, idx)
     set_bytes = (x["pool"].numel() * x["pool"].element_size() * (1 + (w.cache_T / w.pool * w.batch if w.cache_T else 0))
                  + sum(x[n].numel() * x[n].element_size() for n in ("q", "k", "v", "a", "b")))
-    R = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / max(1, workloads.state_read_bytes(w, idx))))
-    R = min(R, 1024, max(2, int(16e9 // set_bytes)))   # tiny workloads: latency-bound anyway
+    R = rotating_sets(state_read, set_bytes)
     shared = {n: x[n].to(dev) for n in ("idx", "accept", "prev_accept") if n in x}
     base = {n: x[n].to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
     if gated:
@@ -444,42 +594,63 @@ def main():
     stream = torch.cuda.Stream()
     step(sets[0])  # first launches load the code objects, outside any capture
     torch.cuda.synchronize()
-    per_replay = R * max(1, 200 // R)
-    run_step = Runner(step, sets, stream, args.eager, per_replay)
-    run_verify = Runner(verify, sets, stream, args.eager, per_replay)
+    if args.calibrate_copy:
+        calibration_copy(dev)
+    rot = Rotation(R)
+    run_step = Runner(step, sets, rot, stream, args.eager, per_replay_of(R))
+    run_verify = Runner(verify, sets, rot, stream, args.eager, per_replay_of(R))
 
     run_step.warm(args.warmup)
     t_step = run_step.timed(args.steps)
     log(f"[bench] {args.steps} steps in {t_step * 1e3:.3f} ms -> {t_step / args.steps * 1e6:.2f} us/step")
 
-    # the dominant kernel on its own, same protocol
+    # the dominant kernel on its own, same protocol, continuing the rotation: five windows of
+    # at least 200 launches each (one window of 20 launches of 15 us varies by several
+    # percent from run to run); the median window's average launch duration
+    n_ver = max(args.steps, 200)
     run_verify.warm(args.warmup)
-    t_ver = run_verify.timed(args.steps)
-    us_ver = t_ver / args.steps * 1e6
+    windows_us = [run_verify.timed(n_ver) / n_ver * 1e6 for _ in range(5)]
+    us_ver = statistics.median(windows_us)
+    log(f"[bench] verify windows of {n_ver} launches: " + " ".join(f"{u:.2f}" for u in windows_us) + " us")
     achieved = v_bytes / (us_ver * 1e-6) / 1e9
     log(f"[bench] verify alone: {us_ver:.2f} us/launch, {achieved:.1f} GB/s algorithmic "
         f"({v_bytes / 1e6:.2f} MB), {achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s")
 
-    if args.calibrate_copy:
-        # 256 MiB read + 256 MiB written, launched alone: the reference for scaling
-        # FETCH_SIZE / WRITE_SIZE counters to bytes
-        a_ = torch.ones(1 << 27, dtype=torch.bfloat16, device=dev)
-        b_ = torch.empty_like(a_)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b_.copy_(a_)
-            torch.cuda.synchronize()
-        del a_, b_
-
-    copy_gbps = copy_ceiling_gbps(dev)
-    log(f"[bench] device copy ceiling: {copy_gbps:.1f} GB/s")
-    cold = single_cold_launches(verify, sets, stream, dev)
-    log(f"[bench] verify, single launches after a 1 GiB scratch fill: median {cold['median_us']:.2f} us, "
-        f"min {cold['min_us']:.2f} us")
+    extras = {}
+    if not args.no_extras:
+        # practical ceiling: a streaming copy of the call's state traffic (read once, written
+        # once per stored state) under the same protocol
+        writes = 1 if (replay or w.mode == "decode" or not w.cache_T) else w.T + (1 if w.mode == "verify_fused" else 0)
+        ceil = copy_ceiling(dev, state_read, writes, args.steps, args.eager)
+        log(f"[bench] streaming copy ceiling ({ceil['mix']}, {ceil['bytes_per_launch'] / 1e6:.1f} MB): "
+            f"{ceil['us_per_launch']:.2f} us, {ceil['GBps']:.1f} GB/s")
+        extras["copy_ceiling"] = ceil
+        extras["single_cold_launch"] = single_cold_launches(verify, sets, stream, dev)
+        log(f"[bench] verify, single launches after a 1 GiB scratch fill: median "
+            f"{extras['single_cold_launch']['median_us']:.2f} us, min {extras['single_cold_launch']['min_us']:.2f} us")
 
     tokens = w.batch * w.T
     n_valid = int(((idx >= 0) & (idx < w.pool)).sum())
     value = tokens * args.steps / t_step
+    entry = "gdn_verify_replay" if replay else "gdn_verify_gated" if gated else (
+        "gdn_decode" if w.mode == "decode" else "gdn_verify")
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_profiles(entry, w.name, "recurrent"),
+            "kernel": entry + " (recurrent_kernel)", "algorithmic_bytes_per_launch": v_bytes,
+            "avg_launch_us": us_ver, "timed_launches_per_window": n_ver,
+            "window_avg_launch_us": windows_us}
+    if "copy_ceiling" in extras:
+        roof["copy_ceiling_GBps"] = extras["copy_ceiling"]["GBps"]
+        roof["frac_of_copy_ceiling"] = achieved / extras["copy_ceiling"]["GBps"]
+    if replay:
+        # cached replay re-runs the accepted tokens instead of storing their states: its
+        # bound is the fp32 vector ALU (flops below at the non-packed FMA rate); the HBM
+        # figures stay beside it
+        fl = replay_flops(w, idx, rlen)
+        tf = fl / (us_ver * 1e-6) / 1e12
+        hbm = {k_: roof[k_] for k_ in ("achieved", "peak", "unit", "frac")}
+        roof.update({"bound": "alu", "achieved": tf, "peak": VALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / VALU_F32_PEAK_TFLOPS, "algorithmic_flops_per_launch": fl, "hbm": hbm})
     res = {
         "metric": "GDN verify tokens/s (batch x T) + achieved HBM GB/s vs peak, T=4 bf16 state",
         "value": value,
@@ -491,7 +662,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # every product and sum is fp32; the state and the io are stored in the workload's dtypes
         "dtype": "f32",
+        "storage_dtype": w.state_dtype if w.state_dtype == w.io_dtype else f"{w.state_dtype} state, {w.io_dtype} io",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "T": w.T, "num_k_heads": w.Hk, "num_v_heads": w.Hv,
                    "d_k": w.dk, "d_v": w.dv, "pool_slots": w.pool, "state_dtype": w.state_dtype,
@@ -501,24 +674,19 @@ def main():
                             + (" + commit" if w.commit else "")),
                    "rotating_buffer_sets": R,
                    "launch": "eager" if args.eager else "hip_graph", "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None if (replay or gated) else traffic_from_profiles(w.name),
-                     "kernel": ("gdn_verify_replay" if replay else "gdn_verify_gated" if gated else "gdn_verify")
-                     + " (recurrent_kernel)",
-                     "algorithmic_bytes_per_launch": v_bytes,
-                     "avg_launch_us": us_ver},
+        "roofline": roof,
         "verify_tokens_per_s": tokens / (us_ver * 1e-6),
         # padding rows cost a launch slot but no state traffic: the rate over the rows that do work
         "valid_rows": n_valid,
         "verify_valid_tokens_per_s": n_valid * w.T / (us_ver * 1e-6),
-        "copy_ceiling_GBps": copy_gbps,
-        "single_cold_launch": cold,
     }
-    if not args.no_cpu and not replay and not gated:
+    res.update(extras)
+    if not args.no_cpu and not replay and not gated and w.commit:
         log("[bench] CPU oracle baseline ...")
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
-        log(f"[bench] CPU oracle: {res['cpu_baseline']['value']:.1f} tokens/s on {res['cpu_baseline']['cores']} threads")
+        cb = res["cpu_baseline"]
+        log(f"[bench] CPU oracle: {cb['value']:.1f} tokens/s on {cb['cores']} threads "
+            f"({cb['nproc']} CPUs available, {cb['hardware_concurrency']} on the host, {cb['cpu_model']})")
     print(json.dumps(res), flush=True)
 
 

@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
+# the measurement library (include/gdn_stream.h): a streaming copy that bench.py times
+STREAM_LIB = os.path.join(PKG, "libgdn_stream.so")
+STREAM_SOURCES = [os.path.join(CSRC, "gdn_stream.hip")]
 SOURCES = [os.path.join(CSRC, f) for f in ("gdn_kernels.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_noalloc.hip",
                                             "gdn_api.cpp")]
 
@@ -32,15 +35,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
-def build(extra_flags: list[str] | None = None, out: str = LIB, quiet: bool = True) -> str:
+def _hipcc(sources: list[str], out: str, extra_flags: list[str] | None, quiet: bool) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-o", tmp, *sources]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if not quiet:
         print(res.stderr)
     os.replace(tmp, out)
+    return out
+
+
+def build(extra_flags: list[str] | None = None, out: str = LIB, quiet: bool = True) -> str:
+    """Builds libgdn.so (to `out`) and, for the default output, the measurement library."""
+    _hipcc(SOURCES, out, extra_flags, quiet)
+    if out == LIB:
+        _hipcc(STREAM_SOURCES, STREAM_LIB, None, quiet)
     return out
 
 

@@ -293,3 +293,23 @@ def conv_commit(dims: ConvDims, x, pool, idx, accept) -> np.ndarray:
     if rc:
         raise ValueError("oracle_conv_commit: invalid dimensions")
     return pool
+
+
+def verify_commit_inplace(dims: Dims, q, k, v, a, b, A_log, dt_bias, pool, idx, cache, cache_T: int, accept, *,
+                          nthreads: int | None = None) -> None:
+    """One verify (every intermediate into ``cache``) then the commit of ``accept``, on
+    float64 arrays prepared by the caller and updated in place: the same two oracle
+    functions as ``verify`` and ``commit``, without their input conversions and copies, so
+    that a timing of this call covers the oracle's own arithmetic only (the CPU baseline)."""
+    for x in (q, k, v, a, b, A_log, dt_bias, pool, cache):
+        assert x.dtype == np.float64 and x.flags.c_contiguous
+    assert idx.dtype == np.int32 and accept.dtype == np.int32
+    B, T, Hv, dv = dims.batch, dims.T, dims.num_v_heads, dims.d_v
+    o = np.empty((B, T, Hv, dv), dtype=np.float64)
+    n = _nthreads(nthreads)
+    rc = lib().oracle_verify(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log), _p(dt_bias),
+                             _p(pool), _p(idx, _I), _p(cache), int(cache_T), 0, None, _p(o), n)
+    rc = rc or lib().oracle_commit(ctypes.byref(dims), _p(cache), int(cache_T), _p(idx, _I), _p(accept, _I),
+                                   _p(pool), n)
+    if rc:
+        raise ValueError("oracle verify/commit: invalid dimensions")

@@ -322,6 +322,43 @@ def test_conv_commit_validation(L):
     assert cc(cdims(width=9)) == 5
 
 
+STREAM_HEADER = os.path.join(ROOT, "include", "gdn_stream.h")
+STREAM_LIB = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_stream.so")
+
+
+def test_stream_library_exports_and_validates():
+    """The measurement library (a streaming copy bench.py times as the practical HBM
+    ceiling) loads, exports what its header declares, and refuses bad arguments before any
+    launch."""
+    import subprocess
+    if not os.path.exists(STREAM_LIB):
+        pytest.fail("libgdn_stream.so is not built (run __graft_entry__.build())")
+    declared = set(re.findall(r'visibility\("default"\)\)\)\s+[\w\s\*]+?\b(gdn_\w+)\s*\(',
+                              open(STREAM_HEADER).read()))
+    assert declared == {"gdn_stream_copy", "gdn_stream_wait"}
+    out = subprocess.run(["nm", "-D", "--defined-only", STREAM_LIB], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert {s for s in syms if not s.startswith("_")} == declared
+    S = ctypes.CDLL(STREAM_LIB)
+    S.gdn_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
+        ctypes.c_void_p]
+    S.gdn_stream_copy.restype = ctypes.c_int32
+    S.gdn_stream_wait.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    S.gdn_stream_wait.restype = ctypes.c_int32
+    blk = 256 * 2 * 16
+    assert S.gdn_stream_copy(A16, A16 * 2, 0, 4, 256, 2, 7, None) == 0        # nothing to do
+    assert S.gdn_stream_copy(A16, A16 * 2, -blk, 4, 256, 2, 7, None) == 2
+    assert S.gdn_stream_copy(A16, A16 * 2, blk + 16, 4, 256, 2, 7, None) == 2  # not whole blocks
+    assert S.gdn_stream_copy(A16, A16 * 2, blk, 0, 256, 2, 7, None) == 2
+    assert S.gdn_stream_copy(A16, A16 * 2, blk, 17, 256, 2, 7, None) == 2
+    assert S.gdn_stream_copy(A16, A16 * 2, blk, 4, 128, 2, 7, None) == 2      # threads 64 or 256
+    assert S.gdn_stream_copy(A16, A16 * 2, blk, 4, 256, 4, 7, None) == 2      # chunks 1, 2 or 8
+    assert S.gdn_stream_copy(A16, A16 * 2, blk, 4, 256, 2, 8, None) == 2
+    assert S.gdn_stream_copy(None, A16 * 2, blk, 4, 256, 2, 7, None) == 1
+    assert S.gdn_stream_copy(A16 + 4, A16 * 2, blk, 4, 256, 2, 7, None) == 4
+    assert S.gdn_stream_wait(-1, None) == 2 and S.gdn_stream_wait(10 ** 8, None) == 2
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 1, 16)
