@@ -156,19 +156,21 @@ class Runner:
                 self.fn(self.sets[(start + i) % len(self.sets)])
         return g
 
-    def _pieces(self, n):
-        """(first set, calls) of the graph replays that make n calls from the current position."""
+    def _pieces(self, n, ahead=0):
+        """(first set, calls) of the graph replays that make n calls from the current position
+        (plus `ahead` calls)."""
         full, rest = divmod(n, self.per_replay)
-        start = self.rot.pos % len(self.sets)
+        start = (self.rot.pos + ahead) % len(self.sets)
         out = [(start, self.per_replay)] * full        # a multiple of the set count: same start
         if rest:
             out.append((start, rest))
         return out
 
-    def prepare(self, n):
+    def prepare(self, n, ahead=0):
+        """Captures the graphs that n calls starting `ahead` calls from now will replay."""
         if self.eager:
             return
-        for key in self._pieces(n):
+        for key in self._pieces(n, ahead):
             if key not in self.graphs:
                 self.graphs[key] = self._capture(*key)
 
@@ -600,6 +602,9 @@ def main():
     run_step = Runner(step, sets, rot, stream, args.eager, per_replay_of(R))
     run_verify = Runner(verify, sets, rot, stream, args.eager, per_replay_of(R))
 
+    # graphs are captured before the warm-up, so that no capture (an idle GPU) sits between
+    # the warm-up and the timed launches
+    run_step.prepare(args.steps, ahead=args.warmup)
     run_step.warm(args.warmup)
     t_step = run_step.timed(args.steps)
     log(f"[bench] {args.steps} steps in {t_step * 1e3:.3f} ms -> {t_step / args.steps * 1e6:.2f} us/step")
@@ -608,6 +613,8 @@ def main():
     # at least 200 launches each (one window of 20 launches of 15 us varies by several
     # percent from run to run); the median window's average launch duration
     n_ver = max(args.steps, 200)
+    for k_ in range(5):
+        run_verify.prepare(n_ver, ahead=args.warmup + k_ * n_ver)
     run_verify.warm(args.warmup)
     windows_us = [run_verify.timed(n_ver) / n_ver * 1e6 for _ in range(5)]
     us_ver = statistics.median(windows_us)

@@ -340,6 +340,7 @@ __device__ __forceinline__ void store_state(bf16s* dst, const f32x4& s) {
 // What the state wave hands to the output wave per chunk, double-buffered by chunk parity:
 // one barrier per chunk suffices, since a wave writes buffer j & 1 only after the barrier
 // of chunk j - 1, which the output wave reaches after its reads of chunk j - 2 completed.
+// (Meeting every second chunk, with four buffers, measured the same.)
 // NCB 16-column tiles per wave.
 template <int NCB>
 struct __attribute__((aligned(16))) ScanLds {
@@ -347,7 +348,7 @@ struct __attribute__((aligned(16))) ScanLds {
   s16x4 u[2][NCB][64];           // bf16 U in the accumulator layout
 };
 
-// Operands of one chunk, loaded two chunks ahead: the state wave's and the output wave's.
+// Operands of one chunk, loaded kDepth chunks ahead: the state wave's and the output wave's.
 template <int NCB>
 struct StateOps {
   s16x8 w[kKT / 2];   // -W, A layout of 16x16x32
@@ -374,26 +375,34 @@ __device__ __forceinline__ void keep_after(T& x) {
   asm volatile("" : "+v"(x)::"memory");
 }
 
-// Runs chunks ja .. jb-1 through step(ops, j) with the operands of chunk j + 2 loading
-// while chunk j computes: pairs of chunks with no exit inside a pair (nothing sinks into
-// the next one), then an odd last chunk alone; each operand set keeps its registers (no
-// copies between them), and nothing is in flight at the loop's start (the wait counts
-// inside the loop then follow from its own loads alone).
-template <typename Ops, typename Fetch, typename Step, typename After>
+// Runs chunks ja .. jb-1 through step(ops, j) with the operands of chunk j + D loading
+// while chunk j computes: D operand sets, each keeping its registers (no copies between
+// them: the loop is unrolled D times), D chunks per trip with no exit inside (nothing sinks
+// into the next trip), then the last chunks alone; nothing is in flight at the loop's start
+// (the wait counts inside the loop then follow from its own loads alone). With two chunks
+// in flight a chain waited for its records (8 x 2048 tokens: 117.5 us per call); three
+// measured 109.5 us, four 110.7 us.
+constexpr int kDepth = 3;  // chunks of operands in flight in the chain
+
+template <int D, typename Ops, typename Fetch, typename Step, typename After>
 __device__ __forceinline__ void run_chunks(int ja, int jb, Fetch fetch, Step step, After after) {
   if (jb <= ja) return;
-  Ops c0 = fetch(ja), c1 = fetch(ja + 1);
+  Ops c[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) c[i] = fetch(ja + i);
   __builtin_amdgcn_s_waitcnt(0);
   int j = ja;
-  for (; j + 1 < jb; j += 2) {
-    step(c0, j);
-    after();
-    c0 = fetch(j + 2);
-    step(c1, j + 1);
-    after();
-    c1 = fetch(j + 3);
+  for (; j + D - 1 < jb; j += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      step(c[i], j + i);
+      after();
+      c[i] = fetch(j + i + D);
+    }
   }
-  if (j < jb) step(c0, j);
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i)
+    if (j + i < jb) step(c[i], j + i);
 }
 
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -499,7 +508,7 @@ __device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds<NCB>& 
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) keep_after(S[ct][kt]);
   };
-  run_chunks<StateOps<NCB>>(ja, jb, fetch, step, after);
+  run_chunks<kDepth, StateOps<NCB>>(ja, jb, fetch, step, after);
 }
 
 // The outputs of chunks [ja, jb), one chunk behind the state chain that hands them over:
@@ -563,7 +572,7 @@ __device__ __forceinline__ void output_chain(const PrefillArgs& p, ScanLds<NCB>&
   };
   // the step ends in its store, so a memory clobber keeps the next loads after it
   auto after = [&]() { asm volatile("" ::: "memory"); };
-  run_chunks<OutOps>(ja, jb, fetch, step, after);
+  run_chunks<kDepth, OutOps>(ja, jb, fetch, step, after);
 }
 
 // fp32 state block cb of a segment slot, in the accumulator layout: [kt][lane][4]
@@ -588,18 +597,31 @@ __device__ __forceinline__ s16x8* slot_map(const PrefillArgs& p, int64_t sid, in
 //   with outputs; the last one stores the final state to the pool.
 // The chain is sequential within a segment only: two segments' chunk steps and n - 2
 // small products instead of one chunk step per chunk.
-// Two waves per workgroup; 1-D grid, XCD-aware: the column blocks of a (segment, v-head)
-// read the same records, so they get ids on one XCD (id % 8 equal) and share its L2.
-// Unit u (= segment * Hv + h) and column block cb take id (u % 8) + 8 (cb + ncb (u / 8)).
-template <typename ST, int PH, int NCB>
-__global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
-  __shared__ ScanLds<NCB> L;
+// Two waves per column block (a state wave and an output wave); 1-D grid, XCD-aware: the
+// column blocks of a (segment, v-head) read the same records, so they get ids on one XCD
+// (id % 8 equal) and share its L2. Unit u (= segment * Hv + h) and column block cb take id
+// (u % 8) + 8 (cb + ncb (u / 8)).
+// PAIR: a workgroup of four waves holds the chains of two neighbouring column blocks of one
+// unit (waves 0 and 1 their state waves, 2 and 3 their output waves). The four waves of a
+// workgroup go to the four SIMDs of a CU, so every SIMD carries one wave: with two-wave
+// workgroups, two per CU, the hardware puts both waves of one workgroup and one of the other
+// on three SIMDs and leaves the fourth idle on most CUs. The two chains walk the same chunks,
+// so the workgroup barrier that hands each chunk from the state to the output waves is
+// reached the same number of times by all four.
+template <typename ST, int PH, int NCB, bool PAIR = false>
+__global__ __launch_bounds__(PAIR ? 256 : 128) void scan_kernel(const PrefillArgs p) {
+  __shared__ ScanLds<NCB> Ls[PAIR ? 2 : 1];
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int chain = PAIR ? (wid & 1) : 0;
+  const int wave = PAIR ? (wid >> 1) : wid;            // 0: the state wave, 1: the output wave
+  ScanLds<NCB>& L = Ls[chain];
   const int nb = p.DV / (16 * NCB);                    // blocks of 16 NCB value columns
   const int ncb = PH == 0 ? max(nb, kKT / NCB) : nb;   // phase 0 also covers the d_k map columns
-  const int rest = int(blockIdx.x) / kXcds, cb = rest % ncb;
-  const int64_t unit = int64_t(rest / ncb) * kXcds + int(blockIdx.x) % kXcds;
+  const int per = PAIR ? ncb / 2 : ncb;                // workgroups per unit
+  const int rest = int(blockIdx.x) / kXcds, cbw = rest % per;
+  const int cb = PAIR ? 2 * cbw + chain : cbw;
+  const int64_t unit = int64_t(rest / per) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
   const int h = int(unit % p.Hv);
   const int64_t sid = unit / p.Hv;
@@ -797,12 +819,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
   }
 }
 
-template <typename ST, int PH, int NCB>
+template <typename ST, int PH, int NCB, bool PAIR = false>
 hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
   const int nb = p.DV / (16 * NCB);
   const int ncb = PH == 0 ? std::max(nb, kKT / NCB) : nb;
-  hipLaunchKernelGGL((scan_kernel<ST, PH, NCB>), dim3(unsigned(units * ncb)), dim3(128), 0, stream, p);
+  if (PAIR && ncb % 2 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((scan_kernel<ST, PH, NCB, PAIR>), dim3(unsigned(units * (PAIR ? ncb / 2 : ncb))),
+                     dim3(PAIR ? 256 : 128), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -818,7 +842,10 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   // sequence one segment, take it.
   const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;
   const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
-  hipError_t e = wide ? launch_scan<ST, 0, 2>(p, stream) : launch_scan<ST, 0, 1>(p, stream);
+  // one segment per sequence, one column tile per wave: two chains per workgroup (d_v is a
+  // multiple of 32, so the column blocks pair up)
+  hipError_t e = wide ? launch_scan<ST, 0, 2>(p, stream)
+                      : whole ? launch_scan<ST, 0, 1, true>(p, stream) : launch_scan<ST, 0, 1>(p, stream);
   if (e != hipSuccess) return e;
   // a sequence has at least three segments only if it is longer than two of them
   if (p.tokens > (int64_t(2) << p.seg_shift)) {
