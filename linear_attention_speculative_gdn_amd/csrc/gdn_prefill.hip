@@ -152,7 +152,7 @@ __device__ __forceinline__ s16x4 hi4(const s16x8& x) { return __builtin_shufflev
 
 // ============================================================ pass 1: chunk records
 struct __attribute__((aligned(16))) ChunkLds {
-  float a[kC * kC];        // A (fp32) for the triangular solve
+  float a[kC * kC];        // A (fp32) for the triangular solve, by column: a[s * kC + t] = A_ts
   uint16_t tw[kC * kC];    // -Tm diag(beta Gam rk), bf16
   uint16_t tv[kC * kC];    // Tm diag(beta), bf16
 };
@@ -266,24 +266,52 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * l4 + i, s_ = l16;
-        L.a[t * kC + s_] = (s_ < t) ? br[i] * rkr[i] * rk * __expf(Gr[i] - G) * KK[i] : 0.f;
+        L.a[s_ * kC + t] = (s_ < t) ? br[i] * rkr[i] * rk * __expf(Gr[i] - G) * KK[i] : 0.f;
         const int sp = 4 * l4 + i, tp = l16;
         pv[i] = (sp <= tp) ? rq * rkr[i] * __expf(G - Gr[i]) * KQ[i] : 0.f;
       }
       pA = bf16x4(pv[0], pv[1], pv[2], pv[3]);
     }
+    // ---- 5a. K^T tiles by the identity product (lane (g, key 16kt + l16): tokens 4g ..),
+    //          and the k-head's record of K^T and Q, before the solve: the keys and queries
+    //          then need no registers across it
+    s16x4 ktA[kKT];
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) {
+      ktA[2 * m] = bf16x4(mfma(lo4(kA[m]), eye, zero4));
+      ktA[2 * m + 1] = bf16x4(mfma(hi4(kA[m]), eye, zero4));
+      if (key_writer) {
+        *reinterpret_cast<s16x8*>(krec + kKeyKT + m * 1024 + l * 16) = cat8(ktA[2 * m], ktA[2 * m + 1]);
+        *reinterpret_cast<s16x8*>(krec + kKeyQ + m * 1024 + l * 16) = qA[m];  // zero past the end
+      }
+    }
     lds_sync();
     // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16),
-    //         column-oriented: once x[s] is final it updates every later row at once
+    //         column-oriented: once x[s] is final it updates every later row at once. Column
+    //         s + 1 of A (a broadcast LDS read) loads while step s computes, and no column
+    //         earlier: read all ahead, A took registers that limited pass 1 to three waves
+    //         per SIMD (161 VGPRs; 93 now).
     if (l < kC) {
       const int c = l;
       float xs[kC];
 #pragma unroll
       for (int t = 0; t < kC; ++t) xs[t] = (t == c) ? 1.f : 0.f;
+      f32x4 cur[kC / 4], nxt[kC / 4];
 #pragma unroll
-      for (int s_ = 0; s_ < kC - 1; ++s_)
+      for (int q4 = 0; q4 < kC / 4; ++q4) cur[q4] = reinterpret_cast<const f32x4*>(L.a)[q4];
 #pragma unroll
-        for (int t = s_ + 1; t < kC; ++t) xs[t] = fmaf(-L.a[t * kC + s_], xs[s_], xs[t]);
+      for (int s_ = 0; s_ < kC - 1; ++s_) {
+        if (s_ + 1 < kC - 1) {
+#pragma unroll
+          for (int q4 = (s_ + 2) / 4; q4 < kC / 4; ++q4)
+            nxt[q4] = reinterpret_cast<const f32x4*>(L.a + (s_ + 1) * kC)[q4];
+        }
+#pragma unroll
+        for (int t = s_ + 1; t < kC; ++t) xs[t] = fmaf(-cur[t / 4][t % 4], xs[s_], xs[t]);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q4 = 0; q4 < kC / 4; ++q4) cur[q4] = nxt[q4];
+      }
       const float cw = -beta * __expf(G) * rk, cv = beta;  // lane c holds token c's values
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
@@ -293,19 +321,12 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     }
     lds_sync();
     const s16x4 twA = ld4(L.tw, l16, kC, 4 * l4), tvA = ld4(L.tv, l16, kC, 4 * l4);
-    // ---- 5. K^T tiles by the identity product (lane (g, key 16kt + l16): tokens 4g ..),
-    //         stored; -W^T = K^T (-TW)^T gives -W in the A layout (lane (t, g): keys
-    //         16kt + 4g ..), stored by 32-key blocks
+    // ---- 5b. -W^T = K^T (-TW)^T gives -W in the A layout (lane (t, g): keys 16kt + 4g ..),
+    //          stored by 32-key blocks
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) {
-      const s16x4 kt0 = bf16x4(mfma(lo4(kA[m]), eye, zero4));
-      const s16x4 kt1 = bf16x4(mfma(hi4(kA[m]), eye, zero4));
-      if (key_writer) {
-        *reinterpret_cast<s16x8*>(krec + kKeyKT + m * 1024 + l * 16) = cat8(kt0, kt1);
-        *reinterpret_cast<s16x8*>(krec + kKeyQ + m * 1024 + l * 16) = qA[m];  // zero past the end
-      }
-      const s16x4 w0 = bf16x4(mfma(kt0, twA, zero4));
-      const s16x4 w1 = bf16x4(mfma(kt1, twA, zero4));
+      const s16x4 w0 = bf16x4(mfma(ktA[2 * m], twA, zero4));
+      const s16x4 w1 = bf16x4(mfma(ktA[2 * m + 1], twA, zero4));
       *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
     }
     // ---- 6. Tm diag(beta) and P, the per-token factors
