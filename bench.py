@@ -65,19 +65,24 @@ def kernel_source_hash(kind: str) -> str:
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(entry: str, workload_name: str, kind: str):
-    """HBM bytes per call from the committed rocprofv3 counter summary
-    ``profiles/<entry>_<workload>_traffic.json``, if it was taken on the current source of
-    the kernel family; else None."""
+def profile_record(entry: str, workload_name: str, kind: str):
+    """The committed rocprofv3 counter summary ``profiles/<entry>_<workload>_traffic.json``,
+    if it was taken on the current source of the kernel family; else None."""
     path = os.path.join(PROFILES, f"{entry}_{workload_name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("kernel_source_sha256_16") != kernel_source_hash(kind):
-        log(f"[bench] {os.path.basename(path)} was taken on other kernel sources: traffic not reported")
+        log(f"[bench] {os.path.basename(path)} was taken on other kernel sources: counters not reported")
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def traffic_from_profiles(entry: str, workload_name: str, kind: str):
+    """HBM bytes per call (FETCH_SIZE + WRITE_SIZE, calibrated) from the committed summary."""
+    rec = profile_record(entry, workload_name, kind)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
 def cpu_model() -> str:
@@ -658,6 +663,12 @@ def main():
         hbm = {k_: roof[k_] for k_ in ("achieved", "peak", "unit", "frac")}
         roof.update({"bound": "alu", "achieved": tf, "peak": VALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / VALU_F32_PEAK_TFLOPS, "algorithmic_flops_per_launch": fl, "hbm": hbm})
+        rec = profile_record(entry, w.name, "recurrent")
+        if rec and rec.get("valu_wave_instructions_per_launch"):
+            # share of the call during which a SIMD issues vector instructions: SQ_INSTS_VALU of one
+            # call (counter pass) x 4 clocks per wave64 instruction on a 16-lane SIMD, over 1024
+            # SIMDs and the live launch duration at 2.4 GHz
+            roof["valu_busy_frac"] = rec["valu_wave_instructions_per_launch"] * 4 / 1024 / (us_ver * 1e-6 * 2.4e9)
     res = {
         "metric": "GDN verify tokens/s (batch x T) + achieved HBM GB/s vs peak, T=4 bf16 state",
         "value": value,

@@ -154,6 +154,17 @@ GDN_API gdn_status gdn_commit(const gdn_dims* dims, const void* inter_cache, int
  * state access. The chunked form runs on the bf16 matrix cores: io must be bf16, d_k 128,
  * d_v a multiple of 32 (GDN_ERR_UNSUPPORTED otherwise). Valid slots must be distinct.
  *
+ * Precision, whatever the pool dtype: every product takes bf16 operands with fp32
+ * accumulation -- the stored keys, queries and values exactly, and the state at each chunk
+ * start, the chunk's triangular inverse and derived matrices, and U rounded to bf16 (2^-9
+ * relative each). o and the final state come out within a few bf16 roundings of the
+ * token-by-token result relative to their magnitude (tested to 2^-5 of each head's largest
+ * |o| and |S|; measured 0.2-1.1 %), not to fp32 precision: an fp32 pool keeps its state in
+ * fp32 between calls, but a prefill call is bf16-grade. For an fp32-grade prefill of an fp32
+ * pool, run the tokens through gdn_verify with write_final = 1 in calls of up to GDN_MAX_T
+ * tokens: it is the same update, token by token in fp32 (tested against this call's float64
+ * definition to 1e-4), at the cost of one call per GDN_MAX_T tokens.
+ *
  * num_tokens is the length of the packed token axis of q, k, v, a, b and o;
  * cu_seqlens[B] <= num_tokens is required (not checked: the offsets live on the device),
  * and num_tokens * Hv * d_v and num_tokens * Hk * d_k must stay below 2^30 elements

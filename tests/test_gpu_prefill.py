@@ -245,3 +245,33 @@ def test_prefill_caller_workspace_reused_and_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_ref) and torch.equal(pool_g, pool_ref), rep
+
+
+def test_fp32_grade_prefill_through_verify():
+    """The route to an fp32-grade prefill of an fp32 pool: the tokens through gdn_verify with
+    write-back, GDN_MAX_T at a time, match the float64 prefill to the recurrent path's fp32
+    tolerance (1e-4 absolute on o and the state), where gdn_prefill itself is held to bf16
+    grade. Unnormalised q and k, weak decay, sequence lengths across several calls."""
+    w = PrefillWorkload("fp32-grade", seqlens=(40, 17, 100), Hk=2, Hv=4, dk=128, dv=128, pool=5,
+                        state_dtype="f32", io_dtype="f32", qk="raw", decay="weak")
+    x = workloads.make_prefill_inputs(w, seed=11)
+    ref = run_oracle(w, x)
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx")}
+    pool = to_device_state(x["pool"]).to(DEV)
+    o = torch.full((w.tokens, w.Hv, w.dv), float("nan"), dtype=torch.float32, device=DEV)
+    cu = x["cu_seqlens"].numpy()
+    for r in range(w.batch):
+        for t0 in range(int(cu[r]), int(cu[r + 1]), gdn.GDN_MAX_T):
+            t1 = min(t0 + gdn.GDN_MAX_T, int(cu[r + 1]))
+            sl = slice(t0, t1)
+            ot = torch.empty((1, t1 - t0, w.Hv, w.dv), dtype=torch.float32, device=DEV)
+            gdn.gdn_verify(g["q"][sl][None].contiguous(), g["k"][sl][None].contiguous(), g["v"][sl][None].contiguous(),
+                           g["a"][sl][None].contiguous(), g["b"][sl][None].contiguous(), g["A_log"], g["dt_bias"], ot,
+                           pool, g["idx"][r:r + 1].contiguous(), None, True, None, scale=w.scale)
+            o[sl] = ot[0]
+    torch.cuda.synchronize()
+    o_err = float(np.abs(f64(o) - ref["o"]).max())
+    idx = x["idx"].numpy()
+    s_err = float(np.abs(from_device_state(pool.cpu()).double().numpy()[idx] - ref["pool"][idx]).max())
+    say(f"[prefill] fp32 through verify: o err {o_err:.2e}, state err {s_err:.2e} (absolute)")
+    assert o_err <= 1e-4 and s_err <= 1e-4

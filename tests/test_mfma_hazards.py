@@ -1,13 +1,19 @@
 """The prefill kernels never feed one matrix-core product into a product of another shape
-through its accumulator (srcC) without five wait states between them.
+through its accumulator operand (srcC).
 
-Measured on gfx950 with a one-wave probe: a v_mfma_f32_16x16x32_bf16 reading, as srcC, the
-result of a v_mfma_f32_16x16x16_bf16 issued 0 to 4 wait states earlier reads a stale
-accumulator; 5 or more give the right result. The compiler of this toolchain places fewer
-in some schedules (it did in the chunk chain, where the outputs of chunked prefill then
-lost a term). The kernels therefore combine products of different shapes through vector
-adds; this test compiles the prefill source to gfx950 assembly with the library's flags
-and checks every such dependency in straight-line order.
+AMD's CDNA3 and CDNA4 instruction-set references (the MFMA dependency-resolution rules:
+required independent instructions between dependent matrix-core instructions) leave the
+ordering of such dependencies to software: the hardware forwards an accumulator from one
+product to the next only for chains of the same instruction, and a product of another
+shape or opcode that reads it as srcC needs independent instructions in between, more the
+more passes the first product takes. A build of the chunk chain in which the compiler had
+scheduled a v_mfma_f32_16x16x32_bf16 reading the accumulator of a
+v_mfma_f32_16x16x16_bf16 a few instructions earlier gave wrong prefill outputs (a term of U
+lost for some chunk counts). The kernels therefore combine products of different shapes
+through vector adds only, and this test compiles the prefill source to gfx950 assembly with
+the library's flags (and with accumulation registers) and requires that no such dependency
+exists at all, whatever the number of instructions in between: no threshold from the
+tables is needed.
 """
 import os
 import re
@@ -17,7 +23,6 @@ import pytest
 
 from linear_attention_speculative_gdn_amd import _build
 
-MIN_WAIT = 5
 SRC = os.path.join(_build.CSRC, "gdn_prefill.hip")
 
 
@@ -81,7 +86,7 @@ _Zk:
 
 
 @pytest.mark.parametrize("form", ["vgpr", "agpr"])
-def test_prefill_has_no_short_cross_shape_chain(tmp_path, form):
+def test_prefill_has_no_cross_shape_srcc_dependency(tmp_path, form):
     flags = [f for f in _build.HIPCC_FLAGS if f not in ("-shared",)]
     if form == "agpr":
         flags = [f for f in flags if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
@@ -91,5 +96,5 @@ def test_prefill_has_no_short_cross_shape_chain(tmp_path, form):
     assert res.returncode == 0, res.stderr[-2000:]
     asm = out.read_text()
     assert "v_mfma_f32_16x16x32_bf16" in asm and "v_mfma_f32_16x16x16_bf16" in asm
-    short = [f for f in cross_shape_srcc(asm) if f[0] < MIN_WAIT]
-    assert not short, "\n".join(f"{w} wait states after {op}: {ln}" for w, op, ln in short)
+    found = cross_shape_srcc(asm)
+    assert not found, "\n".join(f"{w} wait states after {op}: {ln}" for w, op, ln in found)
