@@ -343,9 +343,10 @@ def make_conv_inputs(w: ConvWorkload, seed: int = 0) -> dict:
 
 def conv_bytes(w: ConvWorkload, idx: np.ndarray, prev_len: np.ndarray | None = None) -> int:
     """Bytes one convolution update must move: x of valid rows, y of all rows, taps and
-    bias, the K-1 state rows of each valid row read once, written once when the row
-    commits (fused commit with 1 <= prev_len <= T, or write-back), plus the previous
-    step's inputs that the commit selects (at most K-1 per row)."""
+    bias, the K-1 history rows of each valid row read once (a fused commit of n tokens
+    takes min(n, K-1) of them from the previous step's inputs and the rest from the
+    state), the state written once when the row commits (fused commit with
+    1 <= prev_len <= T, or write-back), and the slot indices and commit lengths."""
     esz = 4 if w.dtype == "f32" else 2
     B, T, D, H = w.batch, w.T, w.channels, w.width - 1
     valid = (idx >= 0) & (idx < w.pool)
@@ -355,7 +356,7 @@ def conv_bytes(w: ConvWorkload, idx: np.ndarray, prev_len: np.ndarray | None = N
         total += nv * H * D * esz
     elif w.mode == "fused" and prev_len is not None:
         n = np.where(valid & (prev_len >= 1) & (prev_len <= T), prev_len, 0)
-        total += int(np.sum(n >= 1)) * H * D * esz + int(np.minimum(n, H).sum()) * D * esz + B * 4
+        total += int(np.sum(n >= 1)) * H * D * esz + B * 4
     return total
 
 
