@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published figure
-# fp32 vector FMA without packed (two-lane) instructions, which this build does not use:
+# fp32 vector FMA without packed (two-lane) instructions, which the library is compiled without:
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz (half the 157.3 TFLOP/s packed figure)
 VALU_F32_PEAK_TFLOPS = 78.6
 INFINITY_CACHE_BYTES = 256 << 20
