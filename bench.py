@@ -39,6 +39,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD publis
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz (half the 157.3 TFLOP/s packed figure)
 VALU_F32_PEAK_TFLOPS = 78.6
 INFINITY_CACHE_BYTES = 256 << 20
+# launches of the dominant kernel before and in each roofline window (about 30 ms of verify
+# calls): enough for the chip's clocks to settle whatever K and W are
+SETTLE_LAUNCHES = 2000
+SETTLE_SECONDS = 0.02  # untimed calls before the warm-up in the single-kernel modes
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_speculative_gdn_amd", "csrc")
 KERNEL_SRCS = {
@@ -216,6 +220,19 @@ class Runner:
         return e0.elapsed_time(e1) * 1e-3
 
 
+def settled_timing(run: Runner, warmup: int, steps: int, est_us: float) -> float:
+    """Seconds for exactly `steps` calls after exactly `warmup` warm-up calls, preceded by
+    untimed calls worth about SETTLE_SECONDS (at `est_us` per call) so that the chip's clocks
+    have settled whatever the step counts; all graphs captured before any of them runs."""
+    n_settle = max(1, int(SETTLE_SECONDS / (est_us * 1e-6)))
+    run.prepare(n_settle)
+    run.prepare(warmup, ahead=n_settle)
+    run.prepare(steps, ahead=n_settle + warmup)
+    run.warm(n_settle)
+    run.warm(warmup)
+    return run.timed(steps)
+
+
 def rotating_sets(read_bytes: int, set_bytes: int) -> int:
     """Buffer sets so that the state reads of one rotation exceed the Infinity Cache four
     times (nontemporal writes do not displace read data from it, so reads are what count),
@@ -372,8 +389,7 @@ def conv_main(args):
     if args.calibrate_copy:
         calibration_copy(dev)
     run = Runner(call, sets, Rotation(R), torch.cuda.Stream(), args.eager, per_replay_of(R))
-    run.warm(args.warmup)
-    t = run.timed(args.steps)
+    t = settled_timing(run, args.warmup, args.steps, est_us=6.0)
     us = t / args.steps * 1e6
     achieved = nbytes / (us * 1e-6) / 1e9
     log(f"[bench] conv: {us:.2f} us/launch, {achieved:.1f} GB/s algorithmic, {achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s")
@@ -435,8 +451,7 @@ def prefill_main(args):
     if args.calibrate_copy:
         calibration_copy(dev)
     run = Runner(call, sets, Rotation(R), torch.cuda.Stream(), args.eager, 2)
-    run.warm(args.warmup)
-    t = run.timed(args.steps)
+    t = settled_timing(run, args.warmup, args.steps, est_us=100.0)
     us = t / args.steps * 1e6
     tflops = flops / (us * 1e-6) / 1e12
     log(f"[bench] prefill: {us:.1f} us/launch, {w.tokens / (us * 1e-6) / 1e6:.1f} M tokens/s, {tflops:.1f} TFLOP/s "
@@ -607,23 +622,30 @@ def main():
     run_step = Runner(step, sets, rot, stream, args.eager, per_replay_of(R))
     run_verify = Runner(verify, sets, rot, stream, args.eager, per_replay_of(R))
 
-    # graphs are captured before the warm-up, so that no capture (an idle GPU) sits between
-    # the warm-up and the timed launches
-    run_step.prepare(args.steps, ahead=args.warmup)
-    run_step.warm(args.warmup)
-    t_step = run_step.timed(args.steps)
-    log(f"[bench] {args.steps} steps in {t_step * 1e3:.3f} ms -> {t_step / args.steps * 1e6:.2f} us/step")
-
-    # the dominant kernel on its own, same protocol, continuing the rotation: five windows of
-    # at least 200 launches each (one window of 20 launches of 15 us varies by several
-    # percent from run to run); the median window's average launch duration
-    n_ver = max(args.steps, 200)
+    # Every graph is captured first, so that no capture (an idle GPU) sits between the
+    # phases, and one rotation over the buffer sets runs through all of them. The dominant
+    # kernel is timed on its own first, independently of K and W: a warm-up of at least
+    # SETTLE_LAUNCHES launches (the chip's clocks settle within milliseconds of load; after a
+    # 5-launch warm-up, 200-launch windows ran up to 20 % slow), then five windows of at
+    # least SETTLE_LAUNCHES launches; the median window's average launch duration prices the
+    # roofline. The step timing follows on the warm chip: exactly W warm-up steps, then
+    # exactly K timed steps.
+    n_vwarm = max(args.warmup, SETTLE_LAUNCHES)
+    n_ver = max(args.steps, SETTLE_LAUNCHES)
+    run_verify.prepare(n_vwarm)
     for k_ in range(5):
-        run_verify.prepare(n_ver, ahead=args.warmup + k_ * n_ver)
-    run_verify.warm(args.warmup)
+        run_verify.prepare(n_ver, ahead=n_vwarm + k_ * n_ver)
+    off = n_vwarm + 5 * n_ver
+    run_step.prepare(args.warmup, ahead=off)
+    run_step.prepare(args.steps, ahead=off + args.warmup)
+    run_verify.warm(n_vwarm)
     windows_us = [run_verify.timed(n_ver) / n_ver * 1e6 for _ in range(5)]
     us_ver = statistics.median(windows_us)
     log(f"[bench] verify windows of {n_ver} launches: " + " ".join(f"{u:.2f}" for u in windows_us) + " us")
+
+    run_step.warm(args.warmup)
+    t_step = run_step.timed(args.steps)
+    log(f"[bench] {args.steps} steps in {t_step * 1e3:.3f} ms -> {t_step / args.steps * 1e6:.2f} us/step")
     achieved = v_bytes / (us_ver * 1e-6) / 1e9
     log(f"[bench] verify alone: {us_ver:.2f} us/launch, {achieved:.1f} GB/s algorithmic "
         f"({v_bytes / 1e6:.2f} MB), {achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s")

@@ -37,33 +37,56 @@ def graph_runner(sets, rot, per_replay, log):
 
 @pytest.mark.parametrize("nsets,warmup,steps", [(7, 5, 20), (64, 5, 20), (64, 800, 8000), (3, 0, 1), (5, 4, 14)])
 def test_rotation_continues_across_warmup_and_timings(nsets, warmup, steps):
-    """Graph replays of the step runner (warm-up, then the timed steps) and then of the
-    verify runner (warm-up and five windows) use the sets in one unbroken rotation, as the
-    bench drives them: graphs prepared before the warm-up, then run."""
+    """Graph replays of the verify runner (its warm-up and five windows) and then of the
+    step runner (W warm-up steps, then the K timed steps) use the sets in one unbroken
+    rotation, as the bench drives them: every graph prepared first, then run."""
     sets = list(range(nsets))
     rot = bench.Rotation(nsets)
     per = bench.per_replay_of(nsets)
     assert per % nsets == 0
     log = []
     step = graph_runner(sets, rot, per, log)
-    step.prepare(steps, ahead=warmup)
-    step.prepare(warmup)
-    step.run(warmup)
-    step.run(steps)
     verify = graph_runner(sets, rot, per, log)
-    n_ver = max(steps, 200)
+    n_vwarm = max(warmup, bench.SETTLE_LAUNCHES)
+    n_ver = max(steps, bench.SETTLE_LAUNCHES)
+    verify.prepare(n_vwarm)
     for k in range(5):
-        verify.prepare(n_ver, ahead=warmup + k * n_ver)
-    verify.prepare(warmup)
-    verify.run(warmup)
+        verify.prepare(n_ver, ahead=n_vwarm + k * n_ver)
+    off = n_vwarm + 5 * n_ver
+    step.prepare(warmup, ahead=off)
+    step.prepare(steps, ahead=off + warmup)
+    captured = (len(verify.graphs), len(step.graphs))
+    verify.run(n_vwarm)
     for _ in range(5):
         verify.run(n_ver)
-    total = warmup + steps + warmup + 5 * n_ver
+    step.run(warmup)
+    step.run(steps)
+    assert (len(verify.graphs), len(step.graphs)) == captured  # nothing captured between phases
+    total = n_vwarm + 5 * n_ver + warmup + steps
     assert log == [i % nsets for i in range(total)]
     # every launch uses a set the previous nsets - 1 launches did not touch
     for i in range(1, len(log)):
         window = log[max(0, i - nsets + 1):i]
         assert log[i] not in window
+
+
+def test_settled_timing_runs_exactly_w_then_k(monkeypatch):
+    """The single-kernel modes: untimed settling calls, then exactly W warm-up calls, then
+    exactly K timed calls, in one rotation, all graphs captured before the first runs."""
+    sets = list(range(5))
+    log, timed = [], []
+    r = graph_runner(sets, bench.Rotation(5), 5, log)
+    monkeypatch.setattr(r, "warm", lambda n: r.run(n))
+
+    def fake_timed(n):
+        timed.append((len(log), n))
+        r.run(n)
+        return 1.0
+    monkeypatch.setattr(r, "timed", fake_timed)
+    n_settle = int(bench.SETTLE_SECONDS / 100e-6)
+    bench.settled_timing(r, warmup=3, steps=7, est_us=100.0)
+    assert timed == [(n_settle + 3, 7)]
+    assert log == [i % 5 for i in range(n_settle + 3 + 7)]
 
 
 def test_eager_rotation_matches_graph_rotation():
