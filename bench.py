@@ -224,7 +224,7 @@ def settled_timing(run: Runner, warmup: int, steps: int, est_us: float) -> float
     """Seconds for exactly `steps` calls after exactly `warmup` warm-up calls, preceded by
     untimed calls worth about SETTLE_SECONDS (at `est_us` per call) so that the chip's clocks
     have settled whatever the step counts; all graphs captured before any of them runs."""
-    n_settle = max(1, int(SETTLE_SECONDS / (est_us * 1e-6)))
+    n_settle = 0 if run.eager else max(1, int(SETTLE_SECONDS / (est_us * 1e-6)))
     run.prepare(n_settle)
     run.prepare(warmup, ahead=n_settle)
     run.prepare(steps, ahead=n_settle + warmup)
@@ -630,8 +630,9 @@ def main():
     # least SETTLE_LAUNCHES launches; the median window's average launch duration prices the
     # roofline. The step timing follows on the warm chip: exactly W warm-up steps, then
     # exactly K timed steps.
-    n_vwarm = max(args.warmup, SETTLE_LAUNCHES)
-    n_ver = max(args.steps, SETTLE_LAUNCHES)
+    # (eager launches serve counter collection, one row per dispatch: W and K as given there)
+    n_vwarm = args.warmup if args.eager else max(args.warmup, SETTLE_LAUNCHES)
+    n_ver = args.steps if args.eager else max(args.steps, SETTLE_LAUNCHES)
     run_verify.prepare(n_vwarm)
     for k_ in range(5):
         run_verify.prepare(n_ver, ahead=n_vwarm + k_ * n_ver)

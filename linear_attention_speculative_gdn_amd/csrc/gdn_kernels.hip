@@ -585,8 +585,12 @@ __global__ __launch_bounds__(NW * 64) void recurrent_kernel(const RecurrentArgs 
 template <int CPT>
 __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs p) {
   const int blk = blockIdx.x, h = blockIdx.y, row = blockIdx.z;  // grid (blocks, Hv, B)
+  // both per-row scalars in flight together: with the tests short-circuited the accept
+  // length was read only after the slot had arrived (one more round trip; 21.85 -> 21.66 us
+  // per verify + commit step on the MTP T=4 batch)
   const int32_t slot = p.idx[row], n = p.accept[row];
-  if (slot < 0 || slot >= p.P || n < 1 || n > p.cache_T) return;
+  asm volatile("" ::: "memory");
+  if ((slot < 0) | (slot >= p.P) | (n < 1) | (n > p.cache_T)) return;
   const char* src = static_cast<const char*>(p.cache) + ((size_t(row) * p.cache_T + (n - 1)) * p.Hv + h) * p.tile_bytes;
   char* dst = static_cast<char*>(p.pool) + (size_t(slot) * p.Hv + h) * p.tile_bytes;
   const int64_t nchunks = p.tile_bytes / 16;
