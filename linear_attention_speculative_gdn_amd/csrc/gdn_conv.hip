@@ -52,6 +52,9 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const ConvArgs p) {
   const int ch = blockIdx.x * kConvThreads + tid;
   const int32_t slot = p.idx[row];
   const int32_t n_raw = p.prev_len ? p.prev_len[row] : 0;
+  // the two per-row scalars are issued before the input loads below, which the compiler
+  // otherwise places first, delaying the slot -> state chain (MTP T=4 batch: 5.47 -> 5.40 us)
+  asm volatile("" ::: "memory");
   if (ch >= p.D / VE) return;
   const int K = p.K, T = COMMIT_ONLY ? 0 : p.T;
   const size_t D = size_t(p.D), c0 = size_t(ch) * VE;
