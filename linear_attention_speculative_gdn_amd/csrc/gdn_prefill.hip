@@ -622,27 +622,15 @@ __device__ __forceinline__ s16x8* slot_map(const PrefillArgs& p, int64_t sid, in
 // column blocks of a (segment, v-head) read the same records, so they get ids on one XCD
 // (id % 8 equal) and share its L2. Unit u (= segment * Hv + h) and column block cb take id
 // (u % 8) + 8 (cb + ncb (u / 8)).
-// PAIR: a workgroup of four waves holds the chains of two neighbouring column blocks of one
-// unit (waves 0 and 1 their state waves, 2 and 3 their output waves). The four waves of a
-// workgroup go to the four SIMDs of a CU, so every SIMD carries one wave: with two-wave
-// workgroups, two per CU, the hardware puts both waves of one workgroup and one of the other
-// on three SIMDs and leaves the fourth idle on most CUs. The two chains walk the same chunks,
-// so the workgroup barrier that hands each chunk from the state to the output waves is
-// reached the same number of times by all four.
-template <typename ST, int PH, int NCB, bool PAIR = false>
-__global__ __launch_bounds__(PAIR ? 256 : 128) void scan_kernel(const PrefillArgs p) {
-  __shared__ ScanLds<NCB> Ls[PAIR ? 2 : 1];
+template <typename ST, int PH, int NCB>
+__global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
+  __shared__ ScanLds<NCB> L;
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int chain = PAIR ? (wid & 1) : 0;
-  const int wave = PAIR ? (wid >> 1) : wid;            // 0: the state wave, 1: the output wave
-  ScanLds<NCB>& L = Ls[chain];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: the state wave, 1: the output wave
   const int nb = p.DV / (16 * NCB);                    // blocks of 16 NCB value columns
   const int ncb = PH == 0 ? max(nb, kKT / NCB) : nb;   // phase 0 also covers the d_k map columns
-  const int per = PAIR ? ncb / 2 : ncb;                // workgroups per unit
-  const int rest = int(blockIdx.x) / kXcds, cbw = rest % per;
-  const int cb = PAIR ? 2 * cbw + chain : cbw;
-  const int64_t unit = int64_t(rest / per) * kXcds + int(blockIdx.x) % kXcds;
+  const int rest = int(blockIdx.x) / kXcds, cb = rest % ncb;
+  const int64_t unit = int64_t(rest / ncb) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
   const int h = int(unit % p.Hv);
   const int64_t sid = unit / p.Hv;
@@ -779,6 +767,261 @@ __global__ __launch_bounds__(PAIR ? 256 : 128) void scan_kernel(const PrefillArg
   }
 }
 
+// ============================================================ pass 2, one segment per sequence:
+// two chains per workgroup with their records staged in LDS
+//
+// A workgroup of five waves runs the chains of two neighbouring 16-column blocks of one
+// (sequence, v-head): waves 0 and 1 are their state waves, 2 and 3 their output waves, and
+// wave 4 copies each chunk's records and the pair's 32 value columns from the workspace
+// into a ring of LDS slots with direct-to-LDS loads (global_load_lds_dwordx4), once for
+// both chains. The chains read their operands out of LDS, so each record byte crosses the
+// CU's vector-memory path once, not once per wave that uses it (the two state waves read
+// the same -W, K^T and Tm diag(beta), the two output waves the same Q and P): that path,
+// with its texture units busy four fifths of the time, bound the chain step when every
+// wave loaded its own operands. Only the copying wave issues direct-to-LDS loads, so the
+// other waves' LDS reads need no wait on vector memory; it waits for its own loads with
+// explicit vmcnt counts before the barrier that publishes them.
+//
+// Schedule, with B(j) the barrier of chunk j that all five waves reach once per chunk
+// (B(-1) before the first chunk):
+// - state waves: the operands of chunk j are read after B(j-1); U of chunk j; S_0 and U to
+//   the output wave's buffer j & 1; B(j); the operands of chunk j+1 are read; the update.
+// - output waves: after B(j), the outputs of chunk j from buffer j & 1 and slot j.
+// - copying wave: after B(j), chunk j + kRing - 1 into the slot of chunk j - 1, which the
+//   state waves finished reading before B(j - 1) and the output waves before B(j); then a
+//   wait until chunk j + 2 has landed (the three later chunks may still be in flight), so
+//   that B(j + 1) publishes it for the state waves.
+constexpr int kStW = 0;          // -W: 4 x 1 KiB, as in the v-head record
+constexpr int kStKT = 4096;      // K^T: 4 x 1 KiB, as in the k-head record
+constexpr int kStQ = 8192;       // Q: 4 x 1 KiB, as in the k-head record
+constexpr int kStTP = 12288;     // Tm diag(beta) and P: 1 KiB
+constexpr int kStSmall = 13312;  // record bytes kRecF .. kRecF + 255: f, Gam rq, Gam_C
+constexpr int kStV = 13568;      // V of the pair's 32 columns, token t at byte 64 t
+constexpr int kStBytes = 14592;
+constexpr int kRing = 6;         // slots: chunks j - 1 .. j + 4 around chunk j
+constexpr int kStLoads = 15;     // direct-to-LDS loads per chunk
+// the copying wave's loads newer than chunk j + 2's when it waits: three chunks'. Its
+// counter of vector-memory operations in flight holds at most 63, so it never has more
+// than four chunks' loads in flight.
+constexpr int kStNewer = (kRing - 3) * kStLoads;
+static_assert(kStNewer + kStLoads <= 63, "vmcnt range");
+static_assert(kRecF + 256 <= kPrefillRecordBytes && kRecGQ - kRecF == 64 && kRecGC - kRecF == 128, "small fields");
+
+struct __attribute__((aligned(16))) PairLds {
+  char ring[kRing][kStBytes];
+  ScanLds<1> hand[2];
+};
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+template <typename T>
+__device__ __forceinline__ T lds_ld(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
+}
+// lane l's 16 (4) bytes at g land at LDS bytes dst + 16 l (dst + 4 l); dst is wave-uniform
+__device__ __forceinline__ void to_lds16(const void* g, lds_char* dst) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void to_lds4(const void* g, lds_char* dst) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N), the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// The state wave's operands of one chunk, read from its slot.
+struct StOps {
+  s16x8 w[kKT / 2];   // -W, A layout of 16x16x32
+  s16x8 kt[kKT / 2];  // K^T tiles 2m, 2m+1, A layout of 16x16x16
+  s16x4 tv;           // Tm diag(beta), A layout
+  s16x4 v;            // V of token l16, columns 4 l4 .. + 3 of the chain's block
+  f32x4 f;            // f of tokens 4 l4 .. 4 l4 + 3
+  float gc;           // Gam_C
+};
+__device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, int l, int l16, int l4) {
+  StOps c;
+#pragma unroll
+  for (int m = 0; m < kKT / 2; ++m) {
+    c.w[m] = lds_ld<s16x8>(s + kStW + m * 1024 + 16 * l);
+    c.kt[m] = lds_ld<s16x8>(s + kStKT + m * 1024 + 16 * l);
+  }
+  c.tv = lds_ld<s16x4>(s + kStTP + 16 * l);  // the lower half
+  c.v = lds_ld<s16x4>(s + kStV + 64 * l16 + 32 * chain + 8 * l4);
+  c.f = lds_ld<f32x4>(s + kStSmall + 16 * l4);
+  c.gc = lds_ld<float>(s + kStSmall + (kRecGC - kRecF));
+  return c;
+}
+
+template <typename ST>
+__global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
+  __shared__ PairLds L;
+  const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int chain = wid & 1;
+  const int per = p.DV / 32;  // pairs of column blocks per (sequence, v-head)
+  const int rest = int(blockIdx.x) / kXcds, pair = rest % per;
+  const int64_t unit = int64_t(rest / per) * kXcds + int(blockIdx.x) % kXcds;
+  if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
+  const int h = int(unit % p.Hv), kh = h / p.G;
+  const int32_t entry = segment_table(p)[unit / p.Hv];
+  if (entry < 0 || (entry >> 16) != 0) return;  // no segment has this id (one per sequence here)
+  const int row = entry & 0xFFFF;
+  if (row >= p.B) return;  // (only a table left by inconsistent cu_seqlens)
+  const int32_t slot = p.idx[row];
+  const int t0 = p.cu[row], t1 = p.cu[row + 1];
+  const int c0 = (2 * pair + chain) * 16;  // the chain's first value column
+
+  if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
+    uint16_t* og = static_cast<uint16_t*>(p.o);
+    for (int e = int(threadIdx.x); e < (t1 - t0) * 4; e += 320) {
+      const int t = t0 + e / 4;
+      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + 32 * pair + 8 * (e % 4)) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  const int nchunks = (t1 - t0 + kC - 1) / kC;
+  const int64_t rid0 = record_id(t0, row, 0);
+  // chunks with a record (all of them unless the workspace is too small for the tokens)
+  const int jb = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - rid0)));
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  auto slot_of = [&](int j) -> lds_char* { return (lds_char*)&L.ring[j % kRing][0]; };
+
+  if (wid < 2) {  // ---- the state waves
+    ST* const my_state = static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + c0 + l16) * kDK + 4 * l4;
+    const int32_t fresh = p.fresh ? p.fresh[row] : 0;
+    f32x4 S[kKT];
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+      const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
+      S[kt] = fresh ? zero4 : s;
+    }
+    if (jb > 0) {
+      ScanLds<1>& H = L.hand[chain];
+      const s16x4 eye = identity_b(l16, l4);
+      // U of chunk j, the handover, B(j), the next chunk's operands, the update
+      auto step = [&](const StOps& c, StOps& next, int j) {
+        const int buf = j & 1;
+        // Tm diag(beta) V (V transposed by the identity product); the asm keeps the
+        // state-independent products in this step
+        s16x4 v = c.v, tv = c.tv;
+        asm volatile("" : "+v"(v), "+v"(tv));
+        const f32x4 tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+        // -W S_0 in two interleaved accumulators (half the dependent chain); the
+        // 16x16x16 product above joins them through a vector add
+        f32x4 u0 = zero4, u1 = zero4;
+#pragma unroll
+        for (int m = 0; m < kKT / 2; ++m) {
+          const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
+          H.s[buf][0][m][l] = sB;
+          if (m & 1)
+            u1 = mfma32(c.w[m], sB, u1);
+          else
+            u0 = mfma32(c.w[m], sB, u0);
+        }
+        const f32x4 u = (u0 + u1) + tvv;
+        H.u[buf][0][l] = bf16x4(u);
+        barrier_lds();  // B(j)
+        next = read_state_ops(slot_of(j + 1), chain, l, l16, l4);
+        // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
+        const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+          S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
+      };
+      barrier_lds();  // B(-1)
+      StOps ca = read_state_ops(slot_of(0), chain, l, l16, l4), cb;
+      for (int j = 0; j < jb; j += 2) {
+        step(ca, cb, j);
+        if (j + 1 >= jb) break;
+        step(cb, ca, j + 1);
+      }
+    }
+    // the final state back to the slot (rounded once for a bf16 pool)
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+    return;
+  }
+  if (jb == 0) return;
+
+  if (wid < 4) {  // ---- the output waves: O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T)
+    ScanLds<1>& H = L.hand[chain];
+    uint16_t* og = static_cast<uint16_t*>(p.o);
+    barrier_lds();  // B(-1)
+    for (int j = 0; j < jb; ++j) {
+      const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
+      barrier_lds();  // B(j): chunk j's S_0 and U are in buffer j & 1
+      const lds_char* s = slot_of(j);
+      s16x8 sA[kKT / 2], q[kKT / 2];
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) {
+        sA[m] = H.s[buf][0][m][l];
+        q[m] = lds_ld<s16x8>(s + kStQ + m * 1024 + 16 * l);
+      }
+      s16x4 uA = H.u[buf][0][l];
+      s16x4 pm = lds_ld<s16x4>(s + kStTP + 16 * l + 8);  // the upper half
+      float gq = lds_ld<float>(s + kStSmall + (kRecGQ - kRecF) + 4 * l16);
+      // every operand has arrived before the first product
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA), "+v"(q[0]), "+v"(q[1]),
+                     "+v"(q[2]), "+v"(q[3]), "+v"(pm), "+v"(gq));
+      f32x4 qs = zero4;
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], q[m], qs);
+      const f32x4 pu = mfma(uA, pm, zero4);
+      float ov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(gq, qs[i], pu[i]);
+      if (l16 < n)
+        *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + h) * p.DV + c0 + 4 * l4) =
+            uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+    }
+    return;
+  }
+
+  // ---- the copying wave
+  const int last = t1 - 1;
+  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV + 32 * pair) +
+                   16 * (l & 3);
+  const size_t vrow_b = size_t(p.Hv) * p.DV * 2;
+  // chunk c (records clamped into the workspace, tokens to the sequence: the chunks past
+  // the end that the ring reaches are loaded but never used)
+  auto issue = [&](int c) {
+    lds_char* s = slot_of(c);
+    const int64_t rid = min(rid0 + c, p.records - 1);
+    const char* rec = head_record(p, rid, h);
+    const char* krec = key_record(p, rid, kh) + 16 * l;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) {
+      to_lds16(rec + kRecW + m * 1024 + 16 * l, s + kStW + m * 1024);
+      to_lds16(krec + kKeyKT + m * 1024, s + kStKT + m * 1024);
+      to_lds16(krec + kKeyQ + m * 1024, s + kStQ + m * 1024);
+    }
+    to_lds16(rec + kRecTP + 16 * l, s + kStTP);
+    to_lds4(rec + kRecF + 4 * l, s + kStSmall);
+    const int tok = min(t0 + c * kC + (l >> 2), last);
+    to_lds16(vg + size_t(tok) * vrow_b, s + kStV);
+  };
+  // chunks 0 .. kRing - 2, never more than four chunks' loads in flight
+#pragma unroll
+  for (int c = 0; c < kRing - 2; ++c) issue(c);
+  wait_vm<kStNewer>();  // chunk 0 has landed
+  issue(kRing - 2);
+  wait_vm<kStNewer>();  // chunk 1 has landed
+  barrier_lds();        // B(-1)
+  for (int j = 0; j < jb; ++j) {
+    barrier_lds();  // B(j)
+    issue(j + kRing - 1);
+    wait_vm<kStNewer>();  // chunk j + 2 has landed
+  }
+  wait_vm<0>();  // nothing lands in LDS after the workgroup ends
+}
+
 // The start states of the segments after the first: S_1 is segment 0's end state, and
 // S_{g+1} = M_g S_g + N_g for g = 1 .. n-2, stored over N_g in the slot of segment g. One
 // wave per (sequence, v-head, 16 value columns); S_g and M_g enter the products in bf16,
@@ -840,14 +1083,12 @@ __global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
   }
 }
 
-template <typename ST, int PH, int NCB, bool PAIR = false>
+template <typename ST, int PH, int NCB>
 hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
   const int nb = p.DV / (16 * NCB);
   const int ncb = PH == 0 ? std::max(nb, kKT / NCB) : nb;
-  if (PAIR && ncb % 2 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((scan_kernel<ST, PH, NCB, PAIR>), dim3(unsigned(units * (PAIR ? ncb / 2 : ncb))),
-                     dim3(PAIR ? 256 : 128), 0, stream, p);
+  hipLaunchKernelGGL((scan_kernel<ST, PH, NCB>), dim3(unsigned(units * ncb)), dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -865,8 +1106,16 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
   // one segment per sequence, one column tile per wave: two chains per workgroup (d_v is a
   // multiple of 32, so the column blocks pair up)
-  hipError_t e = wide ? launch_scan<ST, 0, 2>(p, stream)
-                      : whole ? launch_scan<ST, 0, 1, true>(p, stream) : launch_scan<ST, 0, 1>(p, stream);
+  hipError_t e;
+  if (wide) {
+    e = launch_scan<ST, 0, 2>(p, stream);
+  } else if (whole) {
+    const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(pair_chain_kernel<ST>, dim3(unsigned(units * (p.DV / 32))), dim3(320), 0, stream, p);
+    e = hipGetLastError();
+  } else {
+    e = launch_scan<ST, 0, 1>(p, stream);
+  }
   if (e != hipSuccess) return e;
   // a sequence has at least three segments only if it is longer than two of them
   if (p.tokens > (int64_t(2) << p.seg_shift)) {
