@@ -157,23 +157,27 @@ struct __attribute__((aligned(16))) ChunkLds {
   uint16_t tv[kC * kC];    // Tm diag(beta), bf16
 };
 
-// Pass 1 is bound by vector-instruction issue (about 1200 per chunk and v-head), so the
-// gates, decay ratios and norms use the hardware's approximate exp, log, reciprocal and
-// reciprocal square root (a few ulp; every product it feeds is rounded to bf16): 1500
-// instructions and 35.7 us with the library functions on 8 x 2048 tokens, 33.9 us now.
-// grid (chunk strides, v-heads, sequences), one wave each; wave x handles chunks x,
-// x + gridDim.x, ... of its sequence. Every product takes its operands straight from
-// registers: keys and queries are loaded in the operand layout, K^T comes from the
-// identity product, and W^T = K^T TW^T and (Q K^T)^T = K Q^T come out of the matrix core
-// already in the layout their A operands need. LDS holds only the 16 x 16 solve.
+// Pass 1 is bound by vector-instruction issue and memory latency (about 1200 instructions
+// per chunk and v-head), so the gates, decay ratios and norms use the hardware's approximate
+// exp, log, reciprocal and reciprocal square root (a few ulp; every product it feeds is
+// rounded to bf16): 1500 instructions and 35.7 us with the library functions on 8 x 2048
+// tokens, 33.9 us then.
+// grid (chunk strides, groups of VH v-heads, sequences), one wave each; wave x handles chunks
+// x, x + gridDim.x, ... of its sequence for VH v-heads of one k-head. Every product takes its
+// operands straight from registers: keys and queries are loaded in the operand layout, K^T
+// comes from the identity product, and W^T = K^T TW^T and (Q K^T)^T = K Q^T come out of the
+// matrix core already in the layout their A operands need. LDS holds only the 16 x 16 solves.
+// With VH = 2 the keys, queries, their norms, K K^T, K Q^T and K^T serve both v-heads, and
+// the two triangular solves run side by side, one per 16 lanes.
+template <int VH>
 __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
-  __shared__ ChunkLds L;
-  const int h = blockIdx.y, row = blockIdx.z;
+  __shared__ ChunkLds L[VH];
+  const int h0 = blockIdx.y * VH, row = blockIdx.z;
   const int l = threadIdx.x, l16 = l & 15, l4 = l >> 4;
   const int32_t slot = p.idx[row];
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
   const int nchunks = (t1 - t0 + kC - 1) / kC;
-  if (blockIdx.x == 0 && h == 0) {
+  if (blockIdx.x == 0 && h0 == 0) {
     // the segment table entries from this sequence's first segment id up to the next
     // sequence's (to the table's end for the last; from 0 for the first): each entry is
     // written by exactly one wave
@@ -187,20 +191,26 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     }
   }
   if (slot < 0 || slot >= p.P) return;  // padding rows have no chunks to prepare
-  const int kh = h / p.G;
-  const bool key_writer = h == kh * p.G;  // the k-head's first v-head writes its key record
+  const int kh = h0 / p.G;              // VH divides G: the group shares its k-head
+  const bool key_writer = h0 == kh * p.G;  // the k-head's first v-head writes its key record
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + size_t(kh) * kDK + 4 * l4;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + size_t(kh) * kDK + 4 * l4;
   const uint16_t* ag = static_cast<const uint16_t*>(p.a);
   const uint16_t* bg = static_cast<const uint16_t*>(p.b);
-  const float A_neg = -expf(p.A_log[h]), dtb = p.dt_bias[h];
+  float A_neg[VH], dtb[VH];
+#pragma unroll
+  for (int vh = 0; vh < VH; ++vh) {
+    A_neg[vh] = -expf(p.A_log[h0 + vh]);
+    dtb[vh] = p.dt_bias[h0 + vh];
+  }
   const s16x4 eye = identity_b(l16, l4);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // the solving lanes: 16 per v-head, lane 16 vh + c solves column c of v-head vh
+  const int sv = VH == 2 ? (l >> 4) & 1 : 0;
 
   for (int j = blockIdx.x; j < nchunks; j += gridDim.x) {
     const int64_t rid = record_id(t0, row, j);
     if (rid >= p.records) return;  // workspace too small for the tokens: write nothing
-    char* rec = head_record(p, rid, h);
     char* krec = key_record(p, rid, kh);
     const int cs = t0 + j * kC, n = min(kC, t1 - cs), last = t1 - 1;
     const bool live = l16 < n;  // token t = l16 of the chunk exists
@@ -220,14 +230,21 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
         qA[m] = live ? cat8(q0, q1) : z8;
       }
     }
-    const size_t tg = size_t(min(cs + l16, last)) * p.Hv + h;
-    const float x = bf(ag[tg]) + dtb;
-    float G = live ? A_neg * (fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))) : 0.f;  // log-decay
-    const float beta = live ? __fdividef(1.f, 1.f + __expf(-bf(bg[tg]))) : 0.f;
+    float G[VH], beta[VH];
 #pragma unroll
-    for (int d = 1; d < kC; d *= 2) {  // inclusive prefix sum over the 16 tokens (per group)
-      const float y = __shfl_up(G, d, 16);
-      if (l16 >= d) G += y;
+    for (int vh = 0; vh < VH; ++vh) {
+      const size_t tg = size_t(min(cs + l16, last)) * p.Hv + h0 + vh;
+      const float x = bf(ag[tg]) + dtb[vh];
+      G[vh] = live ? A_neg[vh] * (fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)))) : 0.f;  // log-decay
+      beta[vh] = live ? __fdividef(1.f, 1.f + __expf(-bf(bg[tg]))) : 0.f;
+    }
+#pragma unroll
+    for (int d = 1; d < kC; d *= 2) {  // inclusive prefix sums over the 16 tokens (per group)
+#pragma unroll
+      for (int vh = 0; vh < VH; ++vh) {
+        const float y = __shfl_up(G[vh], d, 16);
+        if (l16 >= d) G[vh] += y;
+      }
     }
     // ---- 2. inverse L2 norms of token l16: each group holds 32 of its 128 keys
     float sk = 0.f, sq = 0.f;
@@ -243,11 +260,14 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
     const float rk = rsqrtf(sk + p.eps), rq = rsqrtf(sq + p.eps);
     // per-token values of the lane's four accumulator rows 4g + i (from group 0's lanes)
-    float Gr[4], br[4], rkr[4];
+    float Gr[VH][4], br[VH][4], rkr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      Gr[i] = __shfl(G, 4 * l4 + i);
-      br[i] = __shfl(beta, 4 * l4 + i);
+#pragma unroll
+      for (int vh = 0; vh < VH; ++vh) {
+        Gr[vh][i] = __shfl(G[vh], 4 * l4 + i);
+        br[vh][i] = __shfl(beta[vh], 4 * l4 + i);
+      }
       rkr[i] = __shfl(rk, 4 * l4 + i);
     }
     // ---- 3. K K^T (rows t = 4g + i, column s = l16) and K Q^T = (Q K^T)^T (rows s,
@@ -260,17 +280,18 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
     }
     // A_ts = beta_t (Gam_t / Gam_s) rk_t rk_s k_t.k_s (s < t) -> LDS for the solve;
     // P_ts = (Gam_t / Gam_s) rq_t rk_s q_t.k_s (s <= t) in its A layout (t = l16, s = 4g + i)
-    s16x4 pA;
-    {
+    s16x4 pA[VH];
+#pragma unroll
+    for (int vh = 0; vh < VH; ++vh) {
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * l4 + i, s_ = l16;
-        L.a[s_ * kC + t] = (s_ < t) ? br[i] * rkr[i] * rk * __expf(Gr[i] - G) * KK[i] : 0.f;
+        L[vh].a[s_ * kC + t] = (s_ < t) ? br[vh][i] * rkr[i] * rk * __expf(Gr[vh][i] - G[vh]) * KK[i] : 0.f;
         const int sp = 4 * l4 + i, tp = l16;
-        pv[i] = (sp <= tp) ? rq * rkr[i] * __expf(G - Gr[i]) * KQ[i] : 0.f;
+        pv[i] = (sp <= tp) ? rq * rkr[i] * __expf(G[vh] - Gr[vh][i]) * KQ[i] : 0.f;
       }
-      pA = bf16x4(pv[0], pv[1], pv[2], pv[3]);
+      pA[vh] = bf16x4(pv[0], pv[1], pv[2], pv[3]);
     }
     // ---- 5a. K^T tiles by the identity product (lane (g, key 16kt + l16): tokens 4g ..),
     //          and the k-head's record of K^T and Q, before the solve: the keys and queries
@@ -286,25 +307,26 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
       }
     }
     lds_sync();
-    // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16),
+    // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16 VH),
     //         column-oriented: once x[s] is final it updates every later row at once. Column
-    //         s + 1 of A (a broadcast LDS read) loads while step s computes, and no column
-    //         earlier: read all ahead, A took registers that limited pass 1 to three waves
-    //         per SIMD (161 VGPRs; 93 now).
-    if (l < kC) {
-      const int c = l;
+    //         s + 1 of A (a broadcast LDS read per v-head) loads while step s computes, and
+    //         no column earlier: read all ahead, A took registers that limited pass 1 to
+    //         three waves per SIMD.
+    if (l < kC * VH) {
+      const int c = l16;
+      const float* a_v = L[sv].a;
       float xs[kC];
 #pragma unroll
       for (int t = 0; t < kC; ++t) xs[t] = (t == c) ? 1.f : 0.f;
       f32x4 cur[kC / 4], nxt[kC / 4];
 #pragma unroll
-      for (int q4 = 0; q4 < kC / 4; ++q4) cur[q4] = reinterpret_cast<const f32x4*>(L.a)[q4];
+      for (int q4 = 0; q4 < kC / 4; ++q4) cur[q4] = reinterpret_cast<const f32x4*>(a_v)[q4];
 #pragma unroll
       for (int s_ = 0; s_ < kC - 1; ++s_) {
         if (s_ + 1 < kC - 1) {
 #pragma unroll
           for (int q4 = (s_ + 2) / 4; q4 < kC / 4; ++q4)
-            nxt[q4] = reinterpret_cast<const f32x4*>(L.a + (s_ + 1) * kC)[q4];
+            nxt[q4] = reinterpret_cast<const f32x4*>(a_v + (s_ + 1) * kC)[q4];
         }
 #pragma unroll
         for (int t = s_ + 1; t < kC; ++t) xs[t] = fmaf(-cur[t / 4][t % 4], xs[s_], xs[t]);
@@ -312,30 +334,40 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
 #pragma unroll
         for (int q4 = 0; q4 < kC / 4; ++q4) cur[q4] = nxt[q4];
       }
-      const float cw = -beta * __expf(G) * rk, cv = beta;  // lane c holds token c's values
+      // lane 16 vh + c holds token c's values of v-head vh
+      const float bs = (VH == 2 && sv) ? beta[VH - 1] : beta[0];
+      const float Gs = (VH == 2 && sv) ? G[VH - 1] : G[0];
+      const float cw = -bs * __expf(Gs) * rk, cv = bs;
+      uint16_t* tw = L[sv].tw;
+      uint16_t* tvp = L[sv].tv;
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
-        L.tw[t * kC + c] = to_bf(xs[t] * cw);
-        L.tv[t * kC + c] = to_bf(xs[t] * cv);
+        tw[t * kC + c] = to_bf(xs[t] * cw);
+        tvp[t * kC + c] = to_bf(xs[t] * cv);
       }
     }
     lds_sync();
-    const s16x4 twA = ld4(L.tw, l16, kC, 4 * l4), tvA = ld4(L.tv, l16, kC, 4 * l4);
-    // ---- 5b. -W^T = K^T (-TW)^T gives -W in the A layout (lane (t, g): keys 16kt + 4g ..),
-    //          stored by 32-key blocks
+    const float Gl0 = __shfl(G[0], kC - 1);
 #pragma unroll
-    for (int m = 0; m < kKT / 2; ++m) {
-      const s16x4 w0 = bf16x4(mfma(ktA[2 * m], twA, zero4));
-      const s16x4 w1 = bf16x4(mfma(ktA[2 * m + 1], twA, zero4));
-      *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
-    }
-    // ---- 6. Tm diag(beta) and P, the per-token factors
-    *reinterpret_cast<s16x8*>(rec + kRecTP + l * 16) = cat8(tvA, pA);
-    const float Gl = __shfl(G, kC - 1);
-    if (l < kC) {
-      reinterpret_cast<float*>(rec + kRecF)[l] = rk * __expf(Gl - G);
-      reinterpret_cast<float*>(rec + kRecGQ)[l] = __expf(G) * rq;
-      if (l == 0) *reinterpret_cast<float*>(rec + kRecGC) = __expf(Gl);
+    for (int vh = 0; vh < VH; ++vh) {
+      char* rec = head_record(p, rid, h0 + vh);
+      const s16x4 twA = ld4(L[vh].tw, l16, kC, 4 * l4), tvA = ld4(L[vh].tv, l16, kC, 4 * l4);
+      // ---- 5b. -W^T = K^T (-TW)^T gives -W in the A layout (lane (t, g): keys 16kt + 4g ..),
+      //          stored by 32-key blocks
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) {
+        const s16x4 w0 = bf16x4(mfma(ktA[2 * m], twA, zero4));
+        const s16x4 w1 = bf16x4(mfma(ktA[2 * m + 1], twA, zero4));
+        *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
+      }
+      // ---- 6. Tm diag(beta) and P, the per-token factors
+      *reinterpret_cast<s16x8*>(rec + kRecTP + l * 16) = cat8(tvA, pA[vh]);
+      const float Gl = vh == 0 ? Gl0 : __shfl(G[vh], kC - 1);
+      if (l < kC) {
+        reinterpret_cast<float*>(rec + kRecF)[l] = rk * __expf(Gl - G[vh]);
+        reinterpret_cast<float*>(rec + kRecGQ)[l] = __expf(G[vh]) * rq;
+        if (l == 0) *reinterpret_cast<float*>(rec + kRecGC) = __expf(Gl);
+      }
     }
     lds_sync();  // LDS is reused by the next chunk
   }
@@ -1132,9 +1164,17 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
 // Pass 1 gets enough waves to fill the chip whatever the batch: each (sequence, v-head)
 // gets `strides` waves that share its chunks.
 hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
+  // Two v-heads per wave share their k-head's work and run their solves side by side, but
+  // halve the waves: worth it once one wave per (chunk, v-head) exceeds the four per SIMD
+  // that the chip holds at once (8 x 2048 tokens: pass 1 30.5 -> 23.3 us; the mixed batch,
+  // about 1000 waves, loses 0.8 us).
+  const int vh = (p.G % 2 == 0 && p.records * p.Hv > 4096) ? 2 : 1;  // v-heads per wave
   const int64_t heads = int64_t(p.B) * p.Hv;
   const unsigned strides = unsigned(std::min<int64_t>(1024, std::max<int64_t>(1, (8192 + heads - 1) / heads)));
-  hipLaunchKernelGGL(chunk_kernel, dim3(strides, unsigned(p.Hv), unsigned(p.B)), dim3(64), 0, stream, p);
+  if (vh == 2)
+    hipLaunchKernelGGL(chunk_kernel<2>, dim3(strides, unsigned(p.Hv / 2), unsigned(p.B)), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(chunk_kernel<1>, dim3(strides, unsigned(p.Hv), unsigned(p.B)), dim3(64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return state == Dt::F32 ? launch_pass2<float>(p, stream) : launch_pass2<bf16s>(p, stream);
