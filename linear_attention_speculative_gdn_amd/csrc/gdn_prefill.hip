@@ -815,14 +815,17 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
 // explicit vmcnt counts before the barrier that publishes them.
 //
 // Schedule, with B(j) the barrier of chunk j that all five waves reach once per chunk
-// (B(-1) before the first chunk):
-// - state waves: the operands of chunk j are read after B(j-1); U of chunk j; S_0 and U to
-//   the output wave's buffer j & 1; B(j); the operands of chunk j+1 are read; the update.
-// - output waves: after B(j), the outputs of chunk j from buffer j & 1 and slot j.
-// - copying wave: after B(j), chunk j + kRing - 1 into the slot of chunk j - 1, which the
-//   state waves finished reading before B(j - 1) and the output waves before B(j); then a
-//   wait until chunk j + 2 has landed (the three later chunks may still be in flight), so
-//   that B(j + 1) publishes it for the state waves.
+// (B(-1) before the first chunk). Chunk c is published at B(c - 2), so that every wave reads
+// its operands of a chunk one step ahead, off the chain's dependent path:
+// - state waves, step j (between B(j-1) and B(j)): the operands of chunk j + 1 are read
+//   while U of chunk j is computed from those read in step j - 1; S_0 and U go to the
+//   output wave's buffer j & 1; B(j); the update.
+// - output waves, after B(j): the outputs of chunk j from buffer j & 1 and the Q, P and
+//   factors read in the previous step; then those of chunk j + 1 are read.
+// - copying wave, after B(j): chunk j + kRing into the slot of chunk j, which the state
+//   waves finished reading before B(j - 1) and the output waves before B(j); then a wait
+//   until chunk j + 3 has landed (the two later chunks may still be in flight), so that
+//   B(j + 1) publishes it.
 constexpr int kStW = 0;          // -W: 4 x 1 KiB, as in the v-head record
 constexpr int kStKT = 4096;      // K^T: 4 x 1 KiB, as in the k-head record
 constexpr int kStQ = 8192;       // Q: 4 x 1 KiB, as in the k-head record
@@ -830,9 +833,9 @@ constexpr int kStTP = 12288;     // Tm diag(beta) and P: 1 KiB
 constexpr int kStSmall = 13312;  // record bytes kRecF .. kRecF + 255: f, Gam rq, Gam_C
 constexpr int kStV = 13568;      // V of the pair's 32 columns, token t at byte 64 t
 constexpr int kStBytes = 14592;
-constexpr int kRing = 6;         // slots: chunks j - 1 .. j + 4 around chunk j
+constexpr int kRing = 6;         // slots: chunks j .. j + 5 around chunk j
 constexpr int kStLoads = 15;     // direct-to-LDS loads per chunk
-// the copying wave's loads newer than chunk j + 2's when it waits: three chunks'. Its
+// the copying wave's loads newer than chunk j + 3's when it waits: three chunks'. Its
 // counter of vector-memory operations in flight holds at most 63, so it never has more
 // than four chunks' loads in flight.
 constexpr int kStNewer = (kRing - 3) * kStLoads;
@@ -856,6 +859,15 @@ __device__ __forceinline__ void to_lds16(const void* g, lds_char* dst) {
 }
 __device__ __forceinline__ void to_lds4(const void* g, lds_char* dst) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 4, 0, 0);
+}
+// The workgroup barrier of the staged chain, as builtins rather than asm: the compiler then
+// knows that every LDS access of the wave has completed (lgkmcnt(0)) and does not wait again
+// for loads issued before it when their values are used after loads issued since.
+__device__ __forceinline__ void barrier_known() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 // s_waitcnt vmcnt(N), the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -936,9 +948,11 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
     if (jb > 0) {
       ScanLds<1>& H = L.hand[chain];
       const s16x4 eye = identity_b(l16, l4);
-      // U of chunk j, the handover, B(j), the next chunk's operands, the update
+      // the next chunk's operands, U of chunk j, the handover, B(j), the update
       auto step = [&](const StOps& c, StOps& next, int j) {
         const int buf = j & 1;
+        next = read_state_ops(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
+        __builtin_amdgcn_sched_barrier(0);  // they go out first
         // Tm diag(beta) V (V transposed by the identity product); the asm keeps the
         // state-independent products in this step
         s16x4 v = c.v, tv = c.tv;
@@ -958,15 +972,14 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
         }
         const f32x4 u = (u0 + u1) + tvv;
         H.u[buf][0][l] = bf16x4(u);
-        barrier_lds();  // B(j)
-        next = read_state_ops(slot_of(j + 1), chain, l, l16, l4);
+        barrier_known();  // B(j)
         // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
         const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt)
           S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
       };
-      barrier_lds();  // B(-1)
+      barrier_known();  // B(-1)
       StOps ca = read_state_ops(slot_of(0), chain, l, l16, l4), cb;
       for (int j = 0; j < jb; j += 2) {
         step(ca, cb, j);
@@ -984,34 +997,44 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
   if (wid < 4) {  // ---- the output waves: O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T)
     ScanLds<1>& H = L.hand[chain];
     uint16_t* og = static_cast<uint16_t*>(p.o);
-    barrier_lds();  // B(-1)
+    struct OutSt {
+      s16x8 q[kKT / 2];  // Q (stored values), A layout of 16x16x32
+      s16x4 pm;          // P, A layout
+      float gq;          // Gam_t rq_t of token l16
+    };
+    auto read_out = [&](int j) {
+      const lds_char* s = slot_of(j);
+      OutSt c;
+#pragma unroll
+      for (int m = 0; m < kKT / 2; ++m) c.q[m] = lds_ld<s16x8>(s + kStQ + m * 1024 + 16 * l);
+      c.pm = lds_ld<s16x4>(s + kStTP + 16 * l + 8);  // the upper half
+      c.gq = lds_ld<float>(s + kStSmall + (kRecGQ - kRecF) + 4 * l16);
+      return c;
+    };
+    barrier_known();  // B(-1)
+    OutSt c = read_out(0);
     for (int j = 0; j < jb; ++j) {
       const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
-      barrier_lds();  // B(j): chunk j's S_0 and U are in buffer j & 1
-      const lds_char* s = slot_of(j);
-      s16x8 sA[kKT / 2], q[kKT / 2];
+      barrier_known();  // B(j): chunk j's S_0 and U are in buffer j & 1
+      s16x8 sA[kKT / 2];
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) {
-        sA[m] = H.s[buf][0][m][l];
-        q[m] = lds_ld<s16x8>(s + kStQ + m * 1024 + 16 * l);
-      }
+      for (int m = 0; m < kKT / 2; ++m) sA[m] = H.s[buf][0][m][l];
       s16x4 uA = H.u[buf][0][l];
-      s16x4 pm = lds_ld<s16x4>(s + kStTP + 16 * l + 8);  // the upper half
-      float gq = lds_ld<float>(s + kStSmall + (kRecGQ - kRecF) + 4 * l16);
       // every operand has arrived before the first product
       asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA), "+v"(q[0]), "+v"(q[1]),
-                     "+v"(q[2]), "+v"(q[3]), "+v"(pm), "+v"(gq));
+                   : "+v"(sA[0]), "+v"(sA[1]), "+v"(sA[2]), "+v"(sA[3]), "+v"(uA), "+v"(c.q[0]), "+v"(c.q[1]),
+                     "+v"(c.q[2]), "+v"(c.q[3]), "+v"(c.pm), "+v"(c.gq));
       f32x4 qs = zero4;
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], q[m], qs);
-      const f32x4 pu = mfma(uA, pm, zero4);
+      for (int m = 0; m < kKT / 2; ++m) qs = mfma32(sA[m], c.q[m], qs);
+      const f32x4 pu = mfma(uA, c.pm, zero4);
       float ov[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(gq, qs[i], pu[i]);
+      for (int i = 0; i < 4; ++i) ov[i] = p.scale * fmaf(c.gq, qs[i], pu[i]);
       if (l16 < n)
         *reinterpret_cast<uint2*>(og + (size_t(cs + l16) * p.Hv + h) * p.DV + c0 + 4 * l4) =
             uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+      c = read_out(j + 1);  // published at B(j - 1)
     }
     return;
   }
@@ -1039,17 +1062,19 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
     const int tok = min(t0 + c * kC + (l >> 2), last);
     to_lds16(vg + size_t(tok) * vrow_b, s + kStV);
   };
-  // chunks 0 .. kRing - 2, never more than four chunks' loads in flight
+  // chunks 0 .. kRing - 1, never more than four chunks' loads in flight
 #pragma unroll
   for (int c = 0; c < kRing - 2; ++c) issue(c);
   wait_vm<kStNewer>();  // chunk 0 has landed
   issue(kRing - 2);
   wait_vm<kStNewer>();  // chunk 1 has landed
-  barrier_lds();        // B(-1)
+  barrier_known();        // B(-1)
+  issue(kRing - 1);
+  wait_vm<kStNewer>();  // chunk 2 has landed
   for (int j = 0; j < jb; ++j) {
-    barrier_lds();  // B(j)
-    issue(j + kRing - 1);
-    wait_vm<kStNewer>();  // chunk j + 2 has landed
+    barrier_known();  // B(j)
+    issue(j + kRing);
+    wait_vm<kStNewer>();  // chunk j + 3 has landed
   }
   wait_vm<0>();  // nothing lands in LDS after the workgroup ends
 }
