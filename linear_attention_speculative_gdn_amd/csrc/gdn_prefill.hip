@@ -458,7 +458,15 @@ __device__ __forceinline__ void run_chunks(int ja, int jb, Fetch fetch, Step ste
     if (j + i < jb) step(c[i], j + i);
 }
 
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The workgroup barrier of the chains, as builtins rather than asm: the compiler then knows
+// that every LDS access of the wave has completed (lgkmcnt(0)) and does not wait again for
+// loads issued before it when their values are used after loads issued since.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Everything a chain needs about its (sequence, v-head) and value-column block.
 struct ChainArgs {
@@ -860,15 +868,6 @@ __device__ __forceinline__ void to_lds16(const void* g, lds_char* dst) {
 __device__ __forceinline__ void to_lds4(const void* g, lds_char* dst) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 4, 0, 0);
 }
-// The workgroup barrier of the staged chain, as builtins rather than asm: the compiler then
-// knows that every LDS access of the wave has completed (lgkmcnt(0)) and does not wait again
-// for loads issued before it when their values are used after loads issued since.
-__device__ __forceinline__ void barrier_known() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 // s_waitcnt vmcnt(N), the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8)
 template <int N>
@@ -972,14 +971,14 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
         }
         const f32x4 u = (u0 + u1) + tvv;
         H.u[buf][0][l] = bf16x4(u);
-        barrier_known();  // B(j)
+        barrier_lds();  // B(j)
         // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
         const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt)
           S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
       };
-      barrier_known();  // B(-1)
+      barrier_lds();  // B(-1)
       StOps ca = read_state_ops(slot_of(0), chain, l, l16, l4), cb;
       for (int j = 0; j < jb; j += 2) {
         step(ca, cb, j);
@@ -1011,11 +1010,11 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
       c.gq = lds_ld<float>(s + kStSmall + (kRecGQ - kRecF) + 4 * l16);
       return c;
     };
-    barrier_known();  // B(-1)
+    barrier_lds();  // B(-1)
     OutSt c = read_out(0);
     for (int j = 0; j < jb; ++j) {
       const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
-      barrier_known();  // B(j): chunk j's S_0 and U are in buffer j & 1
+      barrier_lds();  // B(j): chunk j's S_0 and U are in buffer j & 1
       s16x8 sA[kKT / 2];
 #pragma unroll
       for (int m = 0; m < kKT / 2; ++m) sA[m] = H.s[buf][0][m][l];
@@ -1068,11 +1067,11 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
   wait_vm<kStNewer>();  // chunk 0 has landed
   issue(kRing - 2);
   wait_vm<kStNewer>();  // chunk 1 has landed
-  barrier_known();        // B(-1)
+  barrier_lds();        // B(-1)
   issue(kRing - 1);
   wait_vm<kStNewer>();  // chunk 2 has landed
   for (int j = 0; j < jb; ++j) {
-    barrier_known();  // B(j)
+    barrier_lds();  // B(j)
     issue(j + kRing);
     wait_vm<kStNewer>();  // chunk j + 3 has landed
   }
