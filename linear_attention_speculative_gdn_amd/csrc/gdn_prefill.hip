@@ -23,9 +23,10 @@
 //   chunk's instructions, and none of it is sequential. Queries and K^T do not depend on
 //   the gates: they go to one record per k-head, written by its first v-head, which the
 //   other v-heads of the group read too.
-// - Pass 2 (scan_kernel) walks each sequence's chunks in order with the state in MFMA
-//   accumulators: U~ = Tm diag(beta) V, W S_0, Q S_0, P U and the state update only. The
-//   next chunk's record and queries are loaded while the current chunk computes.
+// - Pass 2 (pair_chain_kernel, or scan_kernel for the segmented and wide forms) walks each
+//   sequence's chunks in order with the state in MFMA accumulators: U~ = Tm diag(beta) V,
+//   W S_0, Q S_0, P U and the state update only. Later chunks' records are loaded while the
+//   current chunk computes (in pair_chain_kernel, copied into LDS once for two chains).
 // - One pass-2 wave per (sequence, v-head, block of NB value columns): columns are
 //   independent given the record. A 16 x 16 accumulator tile holds, per lane, four
 //   consecutive rows of one column -- the B-operand layout -- so S_0 feeds W S_0 and
