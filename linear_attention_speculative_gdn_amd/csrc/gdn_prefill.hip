@@ -23,10 +23,10 @@
 //   chunk's instructions, and none of it is sequential. Queries and K^T do not depend on
 //   the gates: they go to one record per k-head, written by its first v-head, which the
 //   other v-heads of the group read too.
-// - Pass 2 (pair_chain_kernel, or scan_kernel for the segmented and wide forms) walks each
+// - Pass 2 (group_chain_kernel, or scan_kernel for the segmented form) walks each
 //   sequence's chunks in order with the state in MFMA accumulators: U~ = Tm diag(beta) V,
 //   W S_0, Q S_0, P U and the state update only. Later chunks' records are loaded while the
-//   current chunk computes (in pair_chain_kernel, copied into LDS once for two chains).
+//   current chunk computes (in group_chain_kernel, copied into LDS once for its chains).
 // - One pass-2 wave per (sequence, v-head, block of NB value columns): columns are
 //   independent given the record. A 16 x 16 accumulator tile holds, per lane, four
 //   consecutive rows of one column -- the B-operand layout -- so S_0 feeds W S_0 and
@@ -809,21 +809,26 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
 }
 
 // ============================================================ pass 2, one segment per sequence:
-// two chains per workgroup with their records staged in LDS
+// two or four chains per workgroup with their records staged in LDS
 //
-// A workgroup of five waves runs the chains of two neighbouring 16-column blocks of one
-// (sequence, v-head): waves 0 and 1 are their state waves, 2 and 3 their output waves, and
-// wave 4 copies each chunk's records and the pair's 32 value columns from the workspace
-// into a ring of LDS slots with direct-to-LDS loads (global_load_lds_dwordx4), once for
-// both chains. The chains read their operands out of LDS, so each record byte crosses the
-// CU's vector-memory path once, not once per wave that uses it (the two state waves read
-// the same -W, K^T and Tm diag(beta), the two output waves the same Q and P): that path,
+// A workgroup of 2 CH + 1 waves runs the chains of CH neighbouring 16-column blocks of one
+// (sequence, v-head): waves 0 .. CH-1 are their state waves, CH .. 2CH-1 their output
+// waves, and wave 2CH copies each chunk's records and the group's 16 CH value columns from
+// the workspace into a ring of LDS slots with direct-to-LDS loads (global_load_lds_dwordx4),
+// once for all the chains. The chains read their operands out of LDS, so each record byte
+// crosses the CU's vector-memory path once, not once per wave that uses it (the state waves
+// read the same -W, K^T and Tm diag(beta), the output waves the same Q and P): that path,
 // with its texture units busy four fifths of the time, bound the chain step when every
 // wave loaded its own operands. Only the copying wave issues direct-to-LDS loads, so the
 // other waves' LDS reads need no wait on vector memory; it waits for its own loads with
 // explicit vmcnt counts before the barrier that publishes them.
+// CH = 2 (one chain wave per SIMD) when the chains are fewer than two per SIMD; CH = 4 (two
+// per SIMD, four chains sharing each record read) when there are more: 4 x 4096 tokens
+// with 32 v-heads, pass 2 231 -> 177 us against waves of two column tiles loading their own
+// records; two-chain workgroups there, one per CU at a time, took 232 us, and two per CU
+// (a ring of four slots to fit LDS) 274 us.
 //
-// Schedule, with B(j) the barrier of chunk j that all five waves reach once per chunk
+// Schedule, with B(j) the barrier of chunk j that all the waves reach once per chunk
 // (B(-1) before the first chunk). Chunk c is published at B(c - 2), so that every wave reads
 // its operands of a chunk one step ahead, off the chain's dependent path:
 // - state waves, step j (between B(j-1) and B(j)): the operands of chunk j + 1 are read
@@ -831,7 +836,7 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
 //   output wave's buffer j & 1; B(j); the update.
 // - output waves, after B(j): the outputs of chunk j from buffer j & 1 and the Q, P and
 //   factors read in the previous step; then those of chunk j + 1 are read.
-// - copying wave, after B(j): chunk j + kRing into the slot of chunk j, which the state
+// - copying wave, after B(j): chunk j + RING into the slot of chunk j, which the state
 //   waves finished reading before B(j - 1) and the output waves before B(j); then a wait
 //   until chunk j + 3 has landed (the two later chunks may still be in flight), so that
 //   B(j + 1) publishes it.
@@ -840,20 +845,17 @@ constexpr int kStKT = 4096;      // K^T: 4 x 1 KiB, as in the k-head record
 constexpr int kStQ = 8192;       // Q: 4 x 1 KiB, as in the k-head record
 constexpr int kStTP = 12288;     // Tm diag(beta) and P: 1 KiB
 constexpr int kStSmall = 13312;  // record bytes kRecF .. kRecF + 255: f, Gam rq, Gam_C
-constexpr int kStV = 13568;      // V of the pair's 32 columns, token t at byte 64 t
-constexpr int kStBytes = 14592;
-constexpr int kRing = 6;         // slots: chunks j .. j + 5 around chunk j
-constexpr int kStLoads = 15;     // direct-to-LDS loads per chunk
-// the copying wave's loads newer than chunk j + 3's when it waits: three chunks'. Its
-// counter of vector-memory operations in flight holds at most 63, so it never has more
-// than four chunks' loads in flight.
-constexpr int kStNewer = (kRing - 3) * kStLoads;
-static_assert(kStNewer + kStLoads <= 63, "vmcnt range");
+constexpr int kStV = 13568;      // V of the group's 16 CH columns, token t at byte 32 CH t
 static_assert(kRecF + 256 <= kPrefillRecordBytes && kRecGQ - kRecF == 64 && kRecGC - kRecF == 128, "small fields");
+// bytes of a slot and direct-to-LDS loads per chunk for CH chains
+constexpr int st_bytes(int CH) { return kStV + 512 * CH; }
+constexpr int st_loads(int CH) { return 14 + CH / 2; }
 
-struct __attribute__((aligned(16))) PairLds {
-  char ring[kRing][kStBytes];
-  ScanLds<1> hand[2];
+// RING slots: chunks j .. j + RING - 1 around chunk j
+template <int CH, int RING>
+struct __attribute__((aligned(16))) GroupLds {
+  char ring[RING][st_bytes(CH)];
+  ScanLds<1> hand[CH];
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -888,6 +890,7 @@ struct StOps {
   f32x4 f;            // f of tokens 4 l4 .. 4 l4 + 3
   float gc;           // Gam_C
 };
+template <int CH>
 __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, int l, int l16, int l4) {
   StOps c;
 #pragma unroll
@@ -896,20 +899,27 @@ __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, in
     c.kt[m] = lds_ld<s16x8>(s + kStKT + m * 1024 + 16 * l);
   }
   c.tv = lds_ld<s16x4>(s + kStTP + 16 * l);  // the lower half
-  c.v = lds_ld<s16x4>(s + kStV + 64 * l16 + 32 * chain + 8 * l4);
+  c.v = lds_ld<s16x4>(s + kStV + 32 * CH * l16 + 32 * chain + 8 * l4);
   c.f = lds_ld<f32x4>(s + kStSmall + 16 * l4);
   c.gc = lds_ld<float>(s + kStSmall + (kRecGC - kRecF));
   return c;
 }
 
-template <typename ST>
-__global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
-  __shared__ PairLds L;
+template <typename ST, int CH, int RING>
+__global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const PrefillArgs p) {
+  constexpr int kStBytes = st_bytes(CH), kStLoads = st_loads(CH);
+  // the copying wave's loads newer than chunk j + 3's when it waits: RING - 3 chunks'. Its
+  // counter of vector-memory operations in flight holds at most 63, so it never has more
+  // than RING - 2 chunks' loads in flight.
+  constexpr int kStNewer = (RING - 3) * kStLoads;
+  static_assert((CH == 2 || CH == 4) && RING >= 4 && kStNewer + kStLoads <= 63, "two or four chains, ring of 4 to 6");
+  constexpr int kThreads = 64 * (2 * CH + 1);
+  __shared__ GroupLds<CH, RING> L;
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int chain = wid & 1;
-  const int per = p.DV / 32;  // pairs of column blocks per (sequence, v-head)
-  const int rest = int(blockIdx.x) / kXcds, pair = rest % per;
+  const int chain = wid % CH;
+  const int per = p.DV / (16 * CH);  // groups of column blocks per (sequence, v-head)
+  const int rest = int(blockIdx.x) / kXcds, grp = rest % per;
   const int64_t unit = int64_t(rest / per) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
   const int h = int(unit % p.Hv), kh = h / p.G;
@@ -919,13 +929,14 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
   if (row >= p.B) return;  // (only a table left by inconsistent cu_seqlens)
   const int32_t slot = p.idx[row];
   const int t0 = p.cu[row], t1 = p.cu[row + 1];
-  const int c0 = (2 * pair + chain) * 16;  // the chain's first value column
+  const int c0 = (CH * grp + chain) * 16;  // the chain's first value column
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
     uint16_t* og = static_cast<uint16_t*>(p.o);
-    for (int e = int(threadIdx.x); e < (t1 - t0) * 4; e += 320) {
-      const int t = t0 + e / 4;
-      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + 32 * pair + 8 * (e % 4)) = u32x4{0u, 0u, 0u, 0u};
+    for (int e = int(threadIdx.x); e < (t1 - t0) * 2 * CH; e += kThreads) {
+      const int t = t0 + e / (2 * CH);
+      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + 16 * CH * grp + 8 * (e % (2 * CH))) =
+          u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
@@ -934,9 +945,9 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
   // chunks with a record (all of them unless the workspace is too small for the tokens)
   const int jb = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - rid0)));
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  auto slot_of = [&](int j) -> lds_char* { return (lds_char*)&L.ring[j % kRing][0]; };
+  auto slot_of = [&](int j) -> lds_char* { return (lds_char*)&L.ring[j % RING][0]; };
 
-  if (wid < 2) {  // ---- the state waves
+  if (wid < CH) {  // ---- the state waves
     ST* const my_state = static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + c0 + l16) * kDK + 4 * l4;
     const int32_t fresh = p.fresh ? p.fresh[row] : 0;
     f32x4 S[kKT];
@@ -951,7 +962,7 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
       // the next chunk's operands, U of chunk j, the handover, B(j), the update
       auto step = [&](const StOps& c, StOps& next, int j) {
         const int buf = j & 1;
-        next = read_state_ops(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
+        next = read_state_ops<CH>(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
         __builtin_amdgcn_sched_barrier(0);  // they go out first
         // Tm diag(beta) V (V transposed by the identity product); the asm keeps the
         // state-independent products in this step
@@ -980,7 +991,7 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
           S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
       };
       barrier_lds();  // B(-1)
-      StOps ca = read_state_ops(slot_of(0), chain, l, l16, l4), cb;
+      StOps ca = read_state_ops<CH>(slot_of(0), chain, l, l16, l4), cb;
       for (int j = 0; j < jb; j += 2) {
         step(ca, cb, j);
         if (j + 1 >= jb) break;
@@ -994,7 +1005,7 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
   }
   if (jb == 0) return;
 
-  if (wid < 4) {  // ---- the output waves: O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T)
+  if (wid < 2 * CH) {  // ---- the output waves: O^T = scale ((Q S_0)^T diag(Gam rq) + U^T P^T)
     ScanLds<1>& H = L.hand[chain];
     uint16_t* og = static_cast<uint16_t*>(p.o);
     struct OutSt {
@@ -1041,8 +1052,9 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
 
   // ---- the copying wave
   const int last = t1 - 1;
-  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV + 32 * pair) +
-                   16 * (l & 3);
+  // value columns: lane l loads 16 bytes (piece l % 2CH) of token l / 2CH of each 1 KiB block
+  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV + 16 * CH * grp) +
+                   16 * (l % (2 * CH));
   const size_t vrow_b = size_t(p.Hv) * p.DV * 2;
   // chunk c (records clamped into the workspace, tokens to the sequence: the chunks past
   // the end that the ring reaches are loaded but never used)
@@ -1059,21 +1071,24 @@ __global__ __launch_bounds__(320) void pair_chain_kernel(const PrefillArgs p) {
     }
     to_lds16(rec + kRecTP + 16 * l, s + kStTP);
     to_lds4(rec + kRecF + 4 * l, s + kStSmall);
-    const int tok = min(t0 + c * kC + (l >> 2), last);
-    to_lds16(vg + size_t(tok) * vrow_b, s + kStV);
-  };
-  // chunks 0 .. kRing - 1, never more than four chunks' loads in flight
 #pragma unroll
-  for (int c = 0; c < kRing - 2; ++c) issue(c);
+    for (int vo = 0; vo < CH / 2; ++vo) {
+      const int tok = min(t0 + c * kC + vo * (32 / CH) + l / (2 * CH), last);
+      to_lds16(vg + size_t(tok) * vrow_b, s + kStV + 1024 * vo);
+    }
+  };
+  // chunks 0 .. RING - 1, never more than four chunks' loads in flight
+#pragma unroll
+  for (int c = 0; c < RING - 2; ++c) issue(c);
   wait_vm<kStNewer>();  // chunk 0 has landed
-  issue(kRing - 2);
+  issue(RING - 2);
   wait_vm<kStNewer>();  // chunk 1 has landed
   barrier_lds();        // B(-1)
-  issue(kRing - 1);
+  issue(RING - 1);
   wait_vm<kStNewer>();  // chunk 2 has landed
   for (int j = 0; j < jb; ++j) {
     barrier_lds();  // B(j)
-    issue(j + kRing);
+    issue(j + RING);
     wait_vm<kStNewer>();  // chunk j + 3 has landed
   }
   wait_vm<0>();  // nothing lands in LDS after the workgroup ends
@@ -1151,24 +1166,22 @@ hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
 
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
-  // Every column-block wave reads its chunk's records (about 9 KB for the state wave,
-  // 4.5 KB for the output wave) through L2. Where two chains share each SIMD, waves of two
-  // 16-column tiles, which read each record once and pay the per-chunk scalar and issue
-  // overheads once for both, are faster: 4 x 4096 tokens with 32 v-heads (2048 chain
-  // waves) 466 -> 341 us. With one
-  // chain per SIMD the halved wave count costs more than it saves (8 x 2048: 127 -> 123
-  // us, mixed lengths: 32.6 -> 37.7 us), so only grids of >= 2048 chain waves, every
-  // sequence one segment, take it.
+  // Every sequence one segment: the chains stage their records in LDS, four per workgroup
+  // when they number at least two per SIMD (>= 2048 chain waves), else two. Chain waves of
+  // two 16-column tiles that load their own records remain for a d_v that is not a multiple
+  // of 64 in the wide case; the segmented chain runs one chain per two-wave workgroup.
   const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;
   const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
-  // one segment per sequence, one column tile per wave: two chains per workgroup (d_v is a
-  // multiple of 32, so the column blocks pair up)
   hipError_t e;
-  if (wide) {
+  if (wide && p.DV % 64 == 0) {  // four chains per workgroup, one workgroup per CU at a time
+    const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((group_chain_kernel<ST, 4, 5>), dim3(unsigned(units * (p.DV / 64))), dim3(576), 0, stream, p);
+    e = hipGetLastError();
+  } else if (wide) {
     e = launch_scan<ST, 0, 2>(p, stream);
   } else if (whole) {
     const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(pair_chain_kernel<ST>, dim3(unsigned(units * (p.DV / 32))), dim3(320), 0, stream, p);
+    hipLaunchKernelGGL((group_chain_kernel<ST, 2, 6>), dim3(unsigned(units * (p.DV / 32))), dim3(320), 0, stream, p);
     e = hipGetLastError();
   } else {
     e = launch_scan<ST, 0, 1>(p, stream);

@@ -146,8 +146,8 @@ def test_prefill_segment_boundaries(state):
 
 
 def test_prefill_wide_column_tiles():
-    """Batches with two or more chains per SIMD (2 B Hv d_v/16 >= 2048 waves) run the chain
-    on waves of two 16-column tiles: d_v = 96 (three such blocks per head), ragged
+    """Batches with two or more chains per SIMD (2 B Hv d_v/16 >= 2048 waves) and a d_v that
+    is not a multiple of 64 run the chain on waves of two 16-column tiles: d_v = 96 (three such blocks per head), ragged
     lengths, a padding row and a fresh row, bf16 and fp32 pools."""
     for state in ("bf16", "f32"):
         w = PrefillWorkload(f"wide-dv96-{state}", seqlens=(37, 130, 0, 16, 211, 64, 5, 96), Hk=4, Hv=32, dk=128,
@@ -156,6 +156,21 @@ def test_prefill_wide_column_tiles():
         check(w, workloads.make_prefill_inputs(w, seed=7), w.name)
         wr = w.replace(name=w.name + "-rawqk-weakdecay", qk="raw", decay="weak")
         check(wr, workloads.make_prefill_inputs(wr, seed=7), wr.name)
+
+
+@pytest.mark.parametrize("dv,Hv", [(64, 32), (128, 16)])
+def test_prefill_four_chain_groups(dv, Hv):
+    """Batches with two or more chains per SIMD and d_v a multiple of 64 run four chains per
+    workgroup on records staged once in LDS: ragged lengths (an empty sequence, chunk-sized,
+    one-token and long ones), a padding row and a fresh row, bf16 and fp32 pools, and the
+    unnormalised-q/k, weak-decay variant."""
+    for state in ("bf16", "f32"):
+        w = PrefillWorkload(f"quad-dv{dv}-{state}", seqlens=(37, 130, 0, 16, 211, 64, 1, 96), Hk=4, Hv=Hv, dk=128,
+                            dv=dv, pool=10, state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1)
+        assert 2 * w.batch * w.Hv * (w.dv // 16) >= 2048 and w.dv % 64 == 0
+        check(w, workloads.make_prefill_inputs(w, seed=8), w.name)
+        wr = w.replace(name=w.name + "-rawqk-weakdecay", qk="raw", decay="weak")
+        check(wr, workloads.make_prefill_inputs(wr, seed=8), wr.name)
 
 
 def test_prefill_split_continues_from_the_pool():
