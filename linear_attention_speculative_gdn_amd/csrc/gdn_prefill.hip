@@ -905,7 +905,10 @@ __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, in
   return c;
 }
 
-template <typename ST, int CH, int RING>
+// SEG: the later segments of a segmented chain (each from the start state that the segment
+// maps composed into its predecessor's slot, the last one storing the final state), instead
+// of whole sequences (from the pool).
+template <typename ST, int CH, int RING, bool SEG>
 __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const PrefillArgs p) {
   constexpr int kStBytes = st_bytes(CH), kStLoads = st_loads(CH);
   // the copying wave's loads newer than chunk j + 3's when it waits: RING - 3 chunks'. Its
@@ -923,15 +926,18 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
   const int64_t unit = int64_t(rest / per) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
   const int h = int(unit % p.Hv), kh = h / p.G;
-  const int32_t entry = segment_table(p)[unit / p.Hv];
-  if (entry < 0 || (entry >> 16) != 0) return;  // no segment has this id (one per sequence here)
-  const int row = entry & 0xFFFF;
+  const int64_t sid = unit / p.Hv;
+  const int32_t entry = segment_table(p)[sid];
+  if (entry < 0) return;  // no segment has this id
+  const int row = entry & 0xFFFF, g = entry >> 16;
+  if (SEG ? g == 0 : g != 0) return;  // segment 0 runs with the maps (or is the whole sequence)
   if (row >= p.B) return;  // (only a table left by inconsistent cu_seqlens)
   const int32_t slot = p.idx[row];
   const int t0 = p.cu[row], t1 = p.cu[row + 1];
   const int c0 = (CH * grp + chain) * 16;  // the chain's first value column
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
+    if (SEG) return;  // (zeroed with segment 0)
     uint16_t* og = static_cast<uint16_t*>(p.o);
     for (int e = int(threadIdx.x); e < (t1 - t0) * 2 * CH; e += kThreads) {
       const int t = t0 + e / (2 * CH);
@@ -941,20 +947,30 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     return;
   }
   const int nchunks = (t1 - t0 + kC - 1) / kC;
-  const int64_t rid0 = record_id(t0, row, 0);
   // chunks with a record (all of them unless the workspace is too small for the tokens)
-  const int jb = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - rid0)));
+  const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - record_id(t0, row, 0))));
+  // this workgroup's chunks: ja .. ja + jb - 1 of the sequence, j = 0 .. jb - 1 below
+  const int ja = SEG ? g * seg_chunks(p) : 0;
+  const int jb = max(0, (SEG ? min(ja + seg_chunks(p), nrun) : nrun) - ja);
+  const int64_t rid0 = record_id(t0, row, ja);
+  const int ts = t0 + ja * kC;  // the first token of chunk ja
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   auto slot_of = [&](int j) -> lds_char* { return (lds_char*)&L.ring[j % RING][0]; };
 
   if (wid < CH) {  // ---- the state waves
     ST* const my_state = static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + c0 + l16) * kDK + 4 * l4;
-    const int32_t fresh = p.fresh ? p.fresh[row] : 0;
     f32x4 S[kKT];
+    if constexpr (SEG) {
+      const f32x4* src = slot_block(p, sid - 1, h, c0 / 16);  // the segment's start state
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
-      S[kt] = fresh ? zero4 : s;
+      for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
+    } else {
+      const int32_t fresh = p.fresh ? p.fresh[row] : 0;
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) {
+        const f32x4 s = load_state<ST>(my_state + 16 * kt);  // unconditional, then masked
+        S[kt] = fresh ? zero4 : s;
+      }
     }
     if (jb > 0) {
       ScanLds<1>& H = L.hand[chain];
@@ -998,9 +1014,12 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
         step(cb, ca, j + 1);
       }
     }
-    // the final state back to the slot (rounded once for a bf16 pool)
+    // the final state back to the slot (rounded once for a bf16 pool), by the sequence's
+    // last segment
+    if (!SEG || g == seg_count(p, nchunks) - 1) {
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+      for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
+    }
     return;
   }
   if (jb == 0) return;
@@ -1025,7 +1044,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     barrier_lds();  // B(-1)
     OutSt c = read_out(0);
     for (int j = 0; j < jb; ++j) {
-      const int buf = j & 1, cs = t0 + j * kC, n = min(kC, t1 - cs);
+      const int buf = j & 1, cs = ts + j * kC, n = min(kC, t1 - cs);
       barrier_lds();  // B(j): chunk j's S_0 and U are in buffer j & 1
       s16x8 sA[kKT / 2];
 #pragma unroll
@@ -1073,7 +1092,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     to_lds4(rec + kRecF + 4 * l, s + kStSmall);
 #pragma unroll
     for (int vo = 0; vo < CH / 2; ++vo) {
-      const int tok = min(t0 + c * kC + vo * (32 / CH) + l / (2 * CH), last);
+      const int tok = min(ts + c * kC + vo * (32 / CH) + l / (2 * CH), last);
       to_lds16(vg + size_t(tok) * vrow_b, s + kStV + 1024 * vo);
     }
   };
@@ -1164,6 +1183,14 @@ hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename ST, int CH, int RING, bool SEG>
+hipError_t launch_group(const PrefillArgs& p, hipStream_t stream) {
+  const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((group_chain_kernel<ST, CH, RING, SEG>), dim3(unsigned(units * (p.DV / (16 * CH)))),
+                     dim3(64 * (2 * CH + 1)), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   // Every sequence one segment: the chains stage their records in LDS, four per workgroup
@@ -1172,17 +1199,17 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   // of 64 in the wide case; the segmented chain runs one chain per two-wave workgroup.
   const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;
   const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
+  // four chains per workgroup when two-chain workgroups would exceed one per CU (one per CU
+  // fits in LDS at a time): 4 x 4096 tokens with 32 v-heads, the later segments of one long
+  // prompt
+  const bool quads = p.DV % 64 == 0 && p.segments * p.Hv * (p.DV / 32) > 256;
   hipError_t e;
-  if (wide && p.DV % 64 == 0) {  // four chains per workgroup, one workgroup per CU at a time
-    const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((group_chain_kernel<ST, 4, 5>), dim3(unsigned(units * (p.DV / 64))), dim3(576), 0, stream, p);
-    e = hipGetLastError();
+  if (whole && quads) {
+    e = launch_group<ST, 4, 5, false>(p, stream);
   } else if (wide) {
     e = launch_scan<ST, 0, 2>(p, stream);
   } else if (whole) {
-    const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((group_chain_kernel<ST, 2, 6>), dim3(unsigned(units * (p.DV / 32))), dim3(320), 0, stream, p);
-    e = hipGetLastError();
+    e = launch_group<ST, 2, 6, false>(p, stream);
   } else {
     e = launch_scan<ST, 0, 1>(p, stream);
   }
@@ -1193,7 +1220,8 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
     hipLaunchKernelGGL(combine_kernel, dim3(unsigned(units * (p.DV / 16))), dim3(64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (p.tokens > (int64_t(1) << p.seg_shift)) e = launch_scan<ST, 2, 1>(p, stream);
+  if (p.tokens > (int64_t(1) << p.seg_shift))
+    e = quads ? launch_group<ST, 4, 5, true>(p, stream) : launch_group<ST, 2, 6, true>(p, stream);
   return e;
 }
 
