@@ -905,12 +905,81 @@ __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, in
   return c;
 }
 
-// SEG: the later segments of a segmented chain (each from the start state that the segment
-// maps composed into its predecessor's slot, the last one storing the final state), instead
-// of whole sequences (from the pool).
-template <typename ST, int CH, int RING, bool SEG>
+// The chain of one column block over the staged chunks 0 .. jb - 1 (chunk j in slot j % RING),
+// with S in MFMA accumulators: U = Tm diag(beta) V - W S_0 (WITH_V: the values term, off for
+// a segment map), then S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U. HANDOFF: bf16 S_0 and U
+// go to the chain's output wave through buffer j & 1 before B(j). One barrier per chunk,
+// B(-1) first, as every wave of the workgroup.
+template <int CH, int RING, bool WITH_V, bool HANDOFF>
+__device__ __forceinline__ void staged_chain(GroupLds<CH, RING>& L, f32x4 (&S)[kKT], int chain, int jb) {
+  const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  auto slot_of = [&](int j) -> lds_char* { return (lds_char*)&L.ring[j % RING][0]; };
+  ScanLds<1>& H = L.hand[chain];
+  const s16x4 eye = identity_b(l16, l4);
+  // the next chunk's operands, U of chunk j, the handover, B(j), the update
+  auto step = [&](const StOps& c, StOps& next, int j) {
+    const int buf = j & 1;
+    next = read_state_ops<CH>(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
+    __builtin_amdgcn_sched_barrier(0);  // they go out first
+    f32x4 tvv = zero4;
+    if constexpr (WITH_V) {
+      // Tm diag(beta) V (V transposed by the identity product); the asm keeps the
+      // state-independent products in this step
+      s16x4 v = c.v, tv = c.tv;
+      asm volatile("" : "+v"(v), "+v"(tv));
+      tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
+    }
+    // -W S_0 in two interleaved accumulators (half the dependent chain); the 16x16x16
+    // product above joins them through a vector add
+    f32x4 u0 = zero4, u1 = zero4;
+#pragma unroll
+    for (int m = 0; m < kKT / 2; ++m) {
+      const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
+      if constexpr (HANDOFF) H.s[buf][0][m][l] = sB;
+      if (m & 1)
+        u1 = mfma32(c.w[m], sB, u1);
+      else
+        u0 = mfma32(c.w[m], sB, u0);
+    }
+    const f32x4 u = (u0 + u1) + tvv;
+    if constexpr (HANDOFF) H.u[buf][0][l] = bf16x4(u);
+    // Gam_C S_0 before the barrier, where it overlaps the products and the wait; placed
+    // after it, between the update's products, it measured slower
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) S[kt] = S[kt] * c.gc;
+    asm volatile("" : "+v"(S[0]), "+v"(S[1]), "+v"(S[2]), "+v"(S[3]), "+v"(S[4]), "+v"(S[5]), "+v"(S[6]), "+v"(S[7]));
+    barrier_lds();  // B(j)
+    // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
+    const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt]);
+  };
+  barrier_lds();  // B(-1)
+  StOps ca = read_state_ops<CH>(slot_of(0), chain, l, l16, l4), cb;
+  for (int j = 0; j < jb; j += 2) {
+    step(ca, cb, j);
+    if (j + 1 >= jb) break;
+    step(cb, ca, j + 1);
+  }
+}
+
+// A wave of the workgroup with no chain to run still takes part in every barrier.
+__device__ __forceinline__ void barriers_only(int jb) {
+  barrier_lds();  // B(-1)
+  for (int j = 0; j < jb; ++j) barrier_lds();
+}
+
+// MODE 0: whole sequences, from the pool. MODE 1: the first phase of a segmented chain:
+// segment 0 from the pool with outputs (its end state to the segment's slot, or to the pool
+// when it is the only segment), and for every middle segment the map F(S) = M S + N: the
+// state waves run N (the value columns, from zero), the waves that would be output waves
+// run M (d_k columns, from the identity, without the values), neither with outputs. MODE 2:
+// the later segments, each from the start state that the maps composed into its
+// predecessor's slot, with outputs, the last one storing the final state.
+template <typename ST, int CH, int RING, int MODE>
 __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const PrefillArgs p) {
-  constexpr int kStBytes = st_bytes(CH), kStLoads = st_loads(CH);
+  constexpr int kStLoads = st_loads(CH);
   // the copying wave's loads newer than chunk j + 3's when it waits: RING - 3 chunks'. Its
   // counter of vector-memory operations in flight holds at most 63, so it never has more
   // than RING - 2 chunks' loads in flight.
@@ -921,7 +990,9 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chain = wid % CH;
-  const int per = p.DV / (16 * CH);  // groups of column blocks per (sequence, v-head)
+  // groups of column blocks per (segment, v-head); the first phase also covers the d_k
+  // columns of the maps
+  const int per = (MODE == 1 ? max(p.DV, kDK) : p.DV) / (16 * CH);
   const int rest = int(blockIdx.x) / kXcds, grp = rest % per;
   const int64_t unit = int64_t(rest / per) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
@@ -930,14 +1001,19 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
   const int32_t entry = segment_table(p)[sid];
   if (entry < 0) return;  // no segment has this id
   const int row = entry & 0xFFFF, g = entry >> 16;
-  if (SEG ? g == 0 : g != 0) return;  // segment 0 runs with the maps (or is the whole sequence)
+  if (MODE == 0 ? g != 0 : MODE == 2 ? g == 0 : false) return;
   if (row >= p.B) return;  // (only a table left by inconsistent cu_seqlens)
   const int32_t slot = p.idx[row];
   const int t0 = p.cu[row], t1 = p.cu[row + 1];
-  const int c0 = (CH * grp + chain) * 16;  // the chain's first value column
+  const int c0 = (CH * grp + chain) * 16;  // the chain's first column
+  const int nchunks = (t1 - t0 + kC - 1) / kC;
+  const int nseg = seg_count(p, nchunks);
+  if (MODE == 1 && g > 0 && g == nseg - 1) return;  // the last segment has no map to compose
+  const bool outputs = MODE != 1 || g == 0;         // state and output waves, as opposed to N and M
+  if (outputs && 16 * CH * grp >= p.DV) return;     // (map columns past the value columns)
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
-    if (SEG) return;  // (zeroed with segment 0)
+    if (MODE == 2) return;        // (zeroed with segment 0)
     uint16_t* og = static_cast<uint16_t*>(p.o);
     for (int e = int(threadIdx.x); e < (t1 - t0) * 2 * CH; e += kThreads) {
       const int t = t0 + e / (2 * CH);
@@ -946,21 +1022,54 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     }
     return;
   }
-  const int nchunks = (t1 - t0 + kC - 1) / kC;
   // chunks with a record (all of them unless the workspace is too small for the tokens)
   const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - record_id(t0, row, 0))));
   // this workgroup's chunks: ja .. ja + jb - 1 of the sequence, j = 0 .. jb - 1 below
-  const int ja = SEG ? g * seg_chunks(p) : 0;
-  const int jb = max(0, (SEG ? min(ja + seg_chunks(p), nrun) : nrun) - ja);
+  const int ja = MODE == 0 ? 0 : g * seg_chunks(p);
+  const int jb = max(0, (MODE == 0 ? nrun : min(ja + seg_chunks(p), nrun)) - ja);
   const int64_t rid0 = record_id(t0, row, ja);
   const int ts = t0 + ja * kC;  // the first token of chunk ja
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   auto slot_of = [&](int j) -> lds_char* { return (lds_char*)&L.ring[j % RING][0]; };
 
+  if (MODE == 1 && !outputs && wid < 2 * CH) {  // ---- N (waves 0 .. CH-1) and M of a middle segment
+    const bool is_map = wid >= CH;
+    if (c0 >= (is_map ? kDK : p.DV)) {  // no such column block
+      if (jb > 0) barriers_only(jb);
+      return;
+    }
+    f32x4 S[kKT];
+    if (!is_map) {
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) S[kt] = zero4;
+      if (jb > 0) staged_chain<CH, RING, true, false>(L, S, chain, jb);
+      f32x4* dst = slot_block(p, sid, h, c0 / 16);
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
+    } else {
+      const int J = c0 / 16;  // columns 16 J .. 16 J + 15 of M
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[kt][i] = (16 * kt + 4 * l4 + i == 16 * J + l16) ? 1.f : 0.f;
+      if (jb > 0) staged_chain<CH, RING, false, false>(L, S, chain, jb);
+      // Tile (kt, J) read as an A operand is its transpose; the identity product turns that
+      // back into the tile itself in the A layout, exactly (bf16 in, single terms).
+      const s16x4 eye = identity_b(l16, l4);
+      char* dst = reinterpret_cast<char*>(slot_map(p, sid, h));
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) {
+        const s16x4 tA = bf16x4(mfma(bf16x4(S[kt]), eye, zero4));
+        *reinterpret_cast<s16x4*>(dst + ((kt * (kKT / 2) + (J >> 1)) * 64 + l) * 16 + (J & 1) * 8) = tA;
+      }
+    }
+    return;
+  }
+
   if (wid < CH) {  // ---- the state waves
     ST* const my_state = static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + c0 + l16) * kDK + 4 * l4;
     f32x4 S[kKT];
-    if constexpr (SEG) {
+    if constexpr (MODE == 2) {
       const f32x4* src = slot_block(p, sid - 1, h, c0 / 16);  // the segment's start state
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
@@ -972,51 +1081,14 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
         S[kt] = fresh ? zero4 : s;
       }
     }
-    if (jb > 0) {
-      ScanLds<1>& H = L.hand[chain];
-      const s16x4 eye = identity_b(l16, l4);
-      // the next chunk's operands, U of chunk j, the handover, B(j), the update
-      auto step = [&](const StOps& c, StOps& next, int j) {
-        const int buf = j & 1;
-        next = read_state_ops<CH>(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
-        __builtin_amdgcn_sched_barrier(0);  // they go out first
-        // Tm diag(beta) V (V transposed by the identity product); the asm keeps the
-        // state-independent products in this step
-        s16x4 v = c.v, tv = c.tv;
-        asm volatile("" : "+v"(v), "+v"(tv));
-        const f32x4 tvv = mfma(tv, bf16x4(mfma(v, eye, zero4)), zero4);
-        // -W S_0 in two interleaved accumulators (half the dependent chain); the
-        // 16x16x16 product above joins them through a vector add
-        f32x4 u0 = zero4, u1 = zero4;
+    if (jb > 0) staged_chain<CH, RING, true, true>(L, S, chain, jb);
+    if (MODE == 1 && nseg > 1) {  // segment 0's end state, for the maps to carry forward
+      f32x4* dst = slot_block(p, sid, h, c0 / 16);
 #pragma unroll
-        for (int m = 0; m < kKT / 2; ++m) {
-          const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
-          H.s[buf][0][m][l] = sB;
-          if (m & 1)
-            u1 = mfma32(c.w[m], sB, u1);
-          else
-            u0 = mfma32(c.w[m], sB, u0);
-        }
-        const f32x4 u = (u0 + u1) + tvv;
-        H.u[buf][0][l] = bf16x4(u);
-        barrier_lds();  // B(j)
-        // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
-        const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-          S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt] * c.gc);
-      };
-      barrier_lds();  // B(-1)
-      StOps ca = read_state_ops<CH>(slot_of(0), chain, l, l16, l4), cb;
-      for (int j = 0; j < jb; j += 2) {
-        step(ca, cb, j);
-        if (j + 1 >= jb) break;
-        step(cb, ca, j + 1);
-      }
-    }
-    // the final state back to the slot (rounded once for a bf16 pool), by the sequence's
-    // last segment
-    if (!SEG || g == seg_count(p, nchunks) - 1) {
+      for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
+    } else if (MODE != 2 || g == nseg - 1) {
+      // the final state back to the slot (rounded once for a bf16 pool), by the sequence's
+      // last segment
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * kt, S[kt]);
     }
@@ -1072,7 +1144,9 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
   // ---- the copying wave
   const int last = t1 - 1;
   // value columns: lane l loads 16 bytes (piece l % 2CH) of token l / 2CH of each 1 KiB block
-  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV + 16 * CH * grp) +
+  // (a group of map columns only, past the value columns, loads the last group's values)
+  const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + size_t(h) * p.DV +
+                                                 min(16 * CH * grp, p.DV - 16 * CH)) +
                    16 * (l % (2 * CH));
   const size_t vrow_b = size_t(p.Hv) * p.DV * 2;
   // chunk c (records clamped into the workspace, tokens to the sequence: the chunks past
@@ -1183,35 +1257,35 @@ hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename ST, int CH, int RING, bool SEG>
+template <typename ST, int CH, int RING, int MODE>
 hipError_t launch_group(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((group_chain_kernel<ST, CH, RING, SEG>), dim3(unsigned(units * (p.DV / (16 * CH)))),
-                     dim3(64 * (2 * CH + 1)), 0, stream, p);
+  const int per = (MODE == 1 ? std::max(p.DV, kDK) : p.DV) / (16 * CH);
+  hipLaunchKernelGGL((group_chain_kernel<ST, CH, RING, MODE>), dim3(unsigned(units * per)), dim3(64 * (2 * CH + 1)), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
-  // Every sequence one segment: the chains stage their records in LDS, four per workgroup
-  // when they number at least two per SIMD (>= 2048 chain waves), else two. Chain waves of
-  // two 16-column tiles that load their own records remain for a d_v that is not a multiple
-  // of 64 in the wide case; the segmented chain runs one chain per two-wave workgroup.
+  // The chains stage their records in LDS, four per workgroup when two-chain workgroups
+  // would exceed one per CU (one per CU fits in LDS at a time; 4 x 4096 tokens with 32
+  // v-heads, the segments of one long prompt), else two. Chain waves of two 16-column tiles
+  // that load their own records remain for many whole sequences with a d_v that is not a
+  // multiple of 64.
   const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;
   const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
-  // four chains per workgroup when two-chain workgroups would exceed one per CU (one per CU
-  // fits in LDS at a time): 4 x 4096 tokens with 32 v-heads, the later segments of one long
-  // prompt
   const bool quads = p.DV % 64 == 0 && p.segments * p.Hv * (p.DV / 32) > 256;
+  const bool quads1 = p.DV % 64 == 0 && p.segments * p.Hv * (std::max(p.DV, kDK) / 32) > 256;
   hipError_t e;
   if (whole && quads) {
-    e = launch_group<ST, 4, 5, false>(p, stream);
+    e = launch_group<ST, 4, 5, 0>(p, stream);
   } else if (wide) {
     e = launch_scan<ST, 0, 2>(p, stream);
   } else if (whole) {
-    e = launch_group<ST, 2, 6, false>(p, stream);
+    e = launch_group<ST, 2, 6, 0>(p, stream);
   } else {
-    e = launch_scan<ST, 0, 1>(p, stream);
+    e = quads1 ? launch_group<ST, 4, 5, 1>(p, stream) : launch_group<ST, 2, 6, 1>(p, stream);
   }
   if (e != hipSuccess) return e;
   // a sequence has at least three segments only if it is longer than two of them
@@ -1221,7 +1295,7 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.tokens > (int64_t(1) << p.seg_shift))
-    e = quads ? launch_group<ST, 4, 5, true>(p, stream) : launch_group<ST, 2, 6, true>(p, stream);
+    e = quads ? launch_group<ST, 4, 5, 2>(p, stream) : launch_group<ST, 2, 6, 2>(p, stream);
   return e;
 }
 
