@@ -646,38 +646,25 @@ __device__ __forceinline__ s16x8* slot_map(const PrefillArgs& p, int64_t sid, in
   return reinterpret_cast<s16x8*>(segment_slot(p, sid, h) + size_t(p.DV) * kDK * 4);
 }
 
-// Pass 2 runs the chunk chain of each sequence in segments of 2^seg_shift tokens. With
-// F_g the map from the state at the start of segment g to the state at its end,
-// F_g(S) = M_g S + N_g: N_g is the chain from a zero state, M_g (d_k x d_k) the chain from
-// the identity with zero values. Three launches:
-// - PH 0: segment 0 from the slot's state, with outputs (its end state goes to the
-//   segment slot, or to the pool if it is the only segment); for every middle segment
-//   1 .. n-2, N_g (wave 0) and M_g (wave 1) into its slot;
-// - combine_kernel: the start states S_{g+1} = M_g S_g + N_g, in sequence, into the slot
-//   of segment g (over N_g);
-// - PH 2: every later segment again from its start state (the slot of segment g - 1),
-//   with outputs; the last one stores the final state to the pool.
-// The chain is sequential within a segment only: two segments' chunk steps and n - 2
-// small products instead of one chunk step per chunk.
-// Two waves per column block (a state wave and an output wave); 1-D grid, XCD-aware: the
-// column blocks of a (segment, v-head) read the same records, so they get ids on one XCD
-// (id % 8 equal) and share its L2. Unit u (= segment * Hv + h) and column block cb take id
-// (u % 8) + 8 (cb + ncb (u / 8)).
-template <typename ST, int PH, int NCB>
+// Whole sequences on chain waves of NCB 16-column tiles that load their own records, a state
+// wave and an output wave per block of 16 NCB value columns: kept for batches with two or
+// more chains per SIMD whose d_v is not a multiple of 64, where the staged groups of four
+// chains do not apply. 1-D grid, XCD-aware: the column blocks of a (sequence, v-head) read
+// the same records, so they get ids on one XCD (id % 8 equal) and share its L2. Unit u
+// (= sequence * Hv + h) and column block cb take id (u % 8) + 8 (cb + nb (u / 8)).
+template <typename ST, int NCB>
 __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   __shared__ ScanLds<NCB> L;
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: the state wave, 1: the output wave
-  const int nb = p.DV / (16 * NCB);                    // blocks of 16 NCB value columns
-  const int ncb = PH == 0 ? max(nb, kKT / NCB) : nb;   // phase 0 also covers the d_k map columns
-  const int rest = int(blockIdx.x) / kXcds, cb = rest % ncb;
-  const int64_t unit = int64_t(rest / ncb) * kXcds + int(blockIdx.x) % kXcds;
+  const int nb = p.DV / (16 * NCB);  // blocks of 16 NCB value columns
+  const int rest = int(blockIdx.x) / kXcds, cb = rest % nb;
+  const int64_t unit = int64_t(rest / nb) * kXcds + int(blockIdx.x) % kXcds;
   if (unit >= p.segments * p.Hv) return;  // the padding of the last group of 8 units
   const int h = int(unit % p.Hv);
-  const int64_t sid = unit / p.Hv;
-  const int32_t entry = segment_table(p)[sid];
-  if (entry < 0) return;  // no segment has this id
-  const int row = entry & 0xFFFF, g = entry >> 16;
+  const int32_t entry = segment_table(p)[unit / p.Hv];
+  if (entry < 0 || (entry >> 16) != 0) return;  // no segment has this id (one per sequence here)
+  const int row = entry & 0xFFFF;
   if (row >= p.B) return;  // (only a table left by inconsistent cu_seqlens)
   const int32_t slot = p.idx[row];
   ChainArgs a;
@@ -688,123 +675,44 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   a.c0 = cb * 16 * NCB;
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
-    if (PH == 0 && g == 0 && cb < nb) {
-      uint16_t* og = static_cast<uint16_t*>(p.o);
-      const int n16 = (a.t1 - a.t0) * 2 * NCB;  // 16-byte pieces of the block's outputs
-      for (int e = wave * 64 + l; e < n16; e += 128) {
-        const int t = a.t0 + e / (2 * NCB), c = e % (2 * NCB);
-        *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + a.c0 + 8 * c) = u32x4{0u, 0u, 0u, 0u};
-      }
+    uint16_t* og = static_cast<uint16_t*>(p.o);
+    const int n16 = (a.t1 - a.t0) * 2 * NCB;  // 16-byte pieces of the block's outputs
+    for (int e = wave * 64 + l; e < n16; e += 128) {
+      const int t = a.t0 + e / (2 * NCB), c = e % (2 * NCB);
+      *reinterpret_cast<u32x4*>(og + (size_t(t) * p.Hv + h) * p.DV + a.c0 + 8 * c) = u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
 
   const int nchunks = (a.t1 - a.t0 + kC - 1) / kC;
-  const int nseg = seg_count(p, nchunks);
   a.rid0 = record_id(a.t0, row, 0);
-  // chunks with a record (all of them unless the workspace is too small for the tokens)
-  const int nrun = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - a.rid0)));
-  const int ja = g * seg_chunks(p), jb = min(ja + seg_chunks(p), nrun);
-  // Every load is unconditional: the record index and the tokens are clamped into range
-  // (a load in a branch is waited on at the branch end). Operands of tokens past the end
-  // meet zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
+  // chunks with a record (all of them unless the workspace is too small for the tokens).
+  // Every load is unconditional: the record index and the tokens are clamped into range (a
+  // load in a branch is waited on at the branch end). Operands of tokens past the end meet
+  // zero columns of Tm diag(beta) and of P, zero rows of K^T, or outputs not stored.
+  const int jb = int(max<int64_t>(0, min<int64_t>(nchunks, p.records - a.rid0)));
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  // column tile ct of the block: value rows c0 + 16 ct + l16 of the slot's state
-  ST* const my_state =
-      static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + a.c0 + l16) * kDK + 4 * l4;
-
-  if constexpr (PH == 0) {
-    if (g == 0) {
-      if (cb >= nb) return;
-      if (wave == 0) {
-        const int32_t fresh = p.fresh ? p.fresh[row] : 0;
-        f32x4 S[NCB][kKT];
+  if (wave == 0) {
+    // column tile ct of the block: value rows c0 + 16 ct + l16 of the slot's state
+    ST* const my_state =
+        static_cast<ST*>(p.pool) + ((size_t(slot) * p.Hv + h) * p.DV + a.c0 + l16) * kDK + 4 * l4;
+    const int32_t fresh = p.fresh ? p.fresh[row] : 0;
+    f32x4 S[NCB][kKT];
 #pragma unroll
-        for (int ct = 0; ct < NCB; ++ct)
+    for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
-          for (int kt = 0; kt < kKT; ++kt) {
-            const f32x4 s = load_state<ST>(my_state + 16 * ct * kDK + 16 * kt);  // unconditional, then masked
-            S[ct][kt] = fresh ? zero4 : s;
-          }
-        state_chain<true, true, NCB>(p, L, a, S, 0, jb);
-        if (nseg == 1) {  // the final state back to the slot (rounded once for a bf16 pool)
-#pragma unroll
-          for (int ct = 0; ct < NCB; ++ct)
-#pragma unroll
-            for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * ct * kDK + 16 * kt, S[ct][kt]);
-        } else {
-#pragma unroll
-          for (int ct = 0; ct < NCB; ++ct) {
-            f32x4* dst = slot_block(p, sid, h, cb * NCB + ct);
-#pragma unroll
-            for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[ct][kt];
-          }
-        }
-      } else {
-        output_chain<NCB>(p, L, a, 0, jb);
+      for (int kt = 0; kt < kKT; ++kt) {
+        const f32x4 s = load_state<ST>(my_state + 16 * ct * kDK + 16 * kt);  // unconditional, then masked
+        S[ct][kt] = fresh ? zero4 : s;
       }
-      return;
-    }
-    if (g > nseg - 2) return;  // the last segment has no map to compose
-    if (wave == 0) {
-      if (cb >= nb) return;
-      f32x4 S[NCB][kKT];  // N_g: from zero, with the values
+    state_chain<true, true, NCB>(p, L, a, S, 0, jb);
+    // the final state back to the slot (rounded once for a bf16 pool)
 #pragma unroll
-      for (int ct = 0; ct < NCB; ++ct)
+    for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) S[ct][kt] = zero4;
-      state_chain<true, false, NCB>(p, L, a, S, ja, jb);
-#pragma unroll
-      for (int ct = 0; ct < NCB; ++ct) {
-        f32x4* dst = slot_block(p, sid, h, cb * NCB + ct);
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[ct][kt];
-      }
-    } else {
-      if (cb >= kKT / NCB) return;
-      f32x4 S[NCB][kKT];  // columns 16 J .. 16 J + 15 of M_g (J = cb NCB + ct): from the identity, no values
-#pragma unroll
-      for (int ct = 0; ct < NCB; ++ct)
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            S[ct][kt][i] = (16 * kt + 4 * l4 + i == 16 * (cb * NCB + ct) + l16) ? 1.f : 0.f;
-      state_chain<false, false, NCB>(p, L, a, S, ja, jb);
-      // Tile (kt, J) read as an A operand is its transpose; the identity product turns
-      // that back into the tile itself in the A layout, exactly (bf16 in, single terms).
-      const s16x4 eye = identity_b(l16, l4);
-      char* dst = reinterpret_cast<char*>(slot_map(p, sid, h));
-#pragma unroll
-      for (int ct = 0; ct < NCB; ++ct) {
-        const int J = cb * NCB + ct;
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
-          const s16x4 tA = bf16x4(mfma(bf16x4(S[ct][kt]), eye, zero4));
-          *reinterpret_cast<s16x4*>(dst + ((kt * (kKT / 2) + (J >> 1)) * 64 + l) * 16 + (J & 1) * 8) = tA;
-        }
-      }
-    }
+      for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * ct * kDK + 16 * kt, S[ct][kt]);
   } else {
-    if (g == 0 || cb >= nb) return;
-    if (wave == 0) {
-      f32x4 S[NCB][kKT];
-#pragma unroll
-      for (int ct = 0; ct < NCB; ++ct) {
-        const f32x4* src = slot_block(p, max<int64_t>(sid - 1, 0), h, cb * NCB + ct);  // segment g's start
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) S[ct][kt] = src[kt * 64];
-      }
-      state_chain<true, true, NCB>(p, L, a, S, ja, jb);
-      if (g == nseg - 1) {
-#pragma unroll
-        for (int ct = 0; ct < NCB; ++ct)
-#pragma unroll
-          for (int kt = 0; kt < kKT; ++kt) store_state(my_state + 16 * ct * kDK + 16 * kt, S[ct][kt]);
-      }
-    } else {
-      output_chain<NCB>(p, L, a, ja, jb);
-    }
+    output_chain<NCB>(p, L, a, 0, jb);
   }
 }
 
@@ -1248,12 +1156,10 @@ __global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
   }
 }
 
-template <typename ST, int PH, int NCB>
+template <typename ST, int NCB>
 hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
-  const int nb = p.DV / (16 * NCB);
-  const int ncb = PH == 0 ? std::max(nb, kKT / NCB) : nb;
-  hipLaunchKernelGGL((scan_kernel<ST, PH, NCB>), dim3(unsigned(units * ncb)), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL((scan_kernel<ST, NCB>), dim3(unsigned(units * (p.DV / (16 * NCB)))), dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1266,6 +1172,13 @@ hipError_t launch_group(const PrefillArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Pass 2. A sequence longer than one segment of 2^seg_shift tokens runs its chain in
+// segments: with F_g the map from the state at the start of segment g to the state at its
+// end, F_g(S) = M_g S + N_g (N_g the chain from a zero state, M_g, d_k x d_k, the chain from
+// the identity with zero values). Three launches then: segment 0 with outputs and the maps of
+// the middle segments (MODE 1); combine_kernel, the start states S_{g+1} = M_g S_g + N_g in
+// sequence; every later segment again from its start state with outputs (MODE 2). The chain
+// is sequential within a segment only.
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   // The chains stage their records in LDS, four per workgroup when two-chain workgroups
@@ -1281,7 +1194,7 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   if (whole && quads) {
     e = launch_group<ST, 4, 5, 0>(p, stream);
   } else if (wide) {
-    e = launch_scan<ST, 0, 2>(p, stream);
+    e = launch_scan<ST, 2>(p, stream);
   } else if (whole) {
     e = launch_group<ST, 2, 6, 0>(p, stream);
   } else {
