@@ -1097,9 +1097,15 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
 
 // The start states of the segments after the first: S_1 is segment 0's end state, and
 // S_{g+1} = M_g S_g + N_g for g = 1 .. n-2, stored over N_g in the slot of segment g. One
-// wave per (sequence, v-head, 16 value columns); S_g and M_g enter the products in bf16,
-// as the chain's own S_0 does. 1-D grid, XCD-aware as in scan_kernel (unit = row * Hv + h).
-__global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
+// workgroup of eight waves per (sequence, v-head, 16 value columns): wave r computes row tile
+// r (16 rows) of each S_{g+1}, from row tile r of M_g and all of S_g, which the waves share
+// in bf16 through LDS (double-buffered, one barrier per composition). S_g and M_g enter the
+// products in bf16, as the chain's own S_0 does; each row tile sums N_g and the four 32-key
+// blocks in that order. With one wave per column block doing all eight row tiles, the 14
+// compositions of one 16384-token prompt took 16 us. 1-D grid, XCD-aware as in the chains
+// (unit = row * Hv + h).
+__global__ __launch_bounds__(512) void combine_kernel(const PrefillArgs p) {
+  __shared__ s16x8 sh[2][kKT / 2][64];  // S_g in the B layout of 16x16x32, by 32-key block
   const int nb = p.DV / 16;
   const int rest = int(blockIdx.x) / kXcds, cb = rest % nb;
   const int64_t unit = int64_t(rest / nb) * kXcds + int(blockIdx.x) % kXcds;
@@ -1112,48 +1118,57 @@ __global__ __launch_bounds__(64) void combine_kernel(const PrefillArgs p) {
   const int nseg = seg_count(p, nchunks);
   if (nseg < 3) return;
   const int l = threadIdx.x & 63;
+  const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the wave's row tile
   const int64_t sid0 = segment_id(p, t0, row, 0);
-  f32x4 S[kKT];
-  {
-    const f32x4* src = slot_block(p, min(sid0, p.segments - 1), h, cb);
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) S[kt] = src[kt * 64];
-  }
-  // The maps and N do not depend on the running state: those of step g + 1 load while
-  // step g computes (the step is otherwise one load round trip long).
+  // row tile r of S_g holds rows 32 (r / 2) + 16 (r % 2) + 4 l4 + i: the low or high half
+  // of B-operand block r / 2
+  auto share = [&](int buf, const f32x4& s) {
+    reinterpret_cast<s16x4*>(&sh[buf][r / 2][l])[r & 1] = bf16x4(s);
+  };
+  share(1, slot_block(p, min(sid0, p.segments - 1), h, cb)[r * 64]);  // S_1
+  // the map's row tiles and N of the next four compositions load while one computes (one
+  // ahead, each composition waited for its loads: 14.2 us for the 14 of one 16384-token
+  // prompt)
   struct Ops {
-    s16x8 map[kKT * kKT / 2];
-    f32x4 n[kKT];
+    s16x8 map[kKT / 2];
+    f32x4 n;
   };
   auto fetch = [&](int g) -> Ops {
     Ops o;
     const int64_t sid = min(sid0 + min(g, nseg - 2), p.segments - 1);
     const s16x8* map = slot_map(p, sid, h) + l;
-    const f32x4* blk = slot_block(p, sid, h, cb);
 #pragma unroll
-    for (int i = 0; i < kKT * kKT / 2; ++i) o.map[i] = map[i * 64];
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) o.n[kt] = blk[kt * 64];
+    for (int m = 0; m < kKT / 2; ++m) o.map[m] = map[(r * (kKT / 2) + m) * 64];
+    o.n = slot_block(p, sid, h, cb)[r * 64];
     return o;
   };
-  Ops cur = fetch(1);
-  for (int g = 1; g <= nseg - 2; ++g) {
-    const Ops nxt = fetch(g + 1);  // clamped to the last map: a repeat load at the end
+  auto step = [&](const Ops& c, int g) {
     s16x8 sB[kKT / 2];
 #pragma unroll
-    for (int m = 0; m < kKT / 2; ++m) sB[m] = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
+    for (int m = 0; m < kKT / 2; ++m) sB[m] = sh[g & 1][m][l];
+    f32x4 acc = c.n;
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      f32x4 acc = cur.n[kt];
+    for (int m = 0; m < kKT / 2; ++m) acc = mfma32(c.map[m], sB[m], acc);
+    slot_block(p, min(sid0 + g, p.segments - 1), h, cb)[r * 64] = acc;
+    share((g + 1) & 1, acc);
+    barrier_lds();  // S_{g+1} shared; every read of buffer g & 1 done
+  };
+  constexpr int D = 4;
+  barrier_lds();
+  Ops c[D];  // a ring indexed at compile time (the loop is unrolled D times): no copies
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) acc = mfma32(cur.map[kt * (kKT / 2) + m], sB[m], acc);
-      S[kt] = acc;
+  for (int i = 0; i < D; ++i) c[i] = fetch(1 + i);  // clamped to the last map past the end
+  int g = 1;
+  for (; g + D - 1 <= nseg - 2; g += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      step(c[i], g + i);
+      c[i] = fetch(g + i + D);
     }
-    f32x4* blk = slot_block(p, min(sid0 + g, p.segments - 1), h, cb);
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) blk[kt * 64] = S[kt];
-    cur = nxt;
   }
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i)
+    if (g + i <= nseg - 2) step(c[i], g + i);
 }
 
 template <typename ST, int NCB>
@@ -1204,7 +1219,7 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   // a sequence has at least three segments only if it is longer than two of them
   if (p.tokens > (int64_t(2) << p.seg_shift)) {
     const int64_t units = (int64_t(p.B) * p.Hv + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(combine_kernel, dim3(unsigned(units * (p.DV / 16))), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(combine_kernel, dim3(unsigned(units * (p.DV / 16))), dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.tokens > (int64_t(1) << p.seg_shift))
