@@ -190,7 +190,7 @@ GDN_API gdn_status gdn_prefill(const gdn_dims* dims, const gdn_io* io, void* sta
  * GPU until the process ends. Everything else -- arguments, layouts, results, bit for bit,
  * and errors -- is gdn_prefill's. Calls whose workspace (gdn_prefill_workspace_bytes) would
  * exceed the array return GDN_ERR_TOO_LARGE before anything runs (at Hk = 4, Hv = 8, d_v =
- * 128: about 26,000 packed tokens in one sequence). The array's device address is looked up
+ * 128: about 34,000 packed tokens in one sequence). The array's device address is looked up
  * on the first call for a GPU (the GPU of `stream`, or the current one for the NULL stream), so a caller
  * that captures graphs makes one call before capturing; a failed lookup returns
  * GDN_ERR_LAUNCH. No call allocates, frees or synchronises. Every call on one GPU shares
@@ -205,8 +205,8 @@ GDN_API gdn_status gdn_prefill_noalloc(const gdn_dims* dims, const gdn_io* io, v
 /* Workspace size of gdn_prefill, in three parts:
  * - per 16-token chunk, (floor(num_tokens / 16) + batch) of them, one 5376-byte record per
  *   v-head (a 4096-byte bf16 chunk x d_k operand, two 512-byte 16 x 16 bf16 matrices, the
- *   per-token factors, padding) and one 8192-byte record per k-head (the chunk's queries
- *   and transposed keys, shared by the k-head's v-heads);
+ *   per-token factors, padding) and one 4096-byte record per k-head (the chunk's
+ *   transposed keys, shared by the k-head's v-heads);
  * - a table of the segments of the chunk chain, 4 bytes each, padded to 256 bytes;
  * - per segment and v-head, a slot of 128 * d_v * 4 + 128 * 128 * 2 bytes (a state and a
  *   segment map).

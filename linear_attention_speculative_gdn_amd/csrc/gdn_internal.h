@@ -88,7 +88,7 @@ hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t s
 // that involve the gates) and then one per k-head (its queries and transposed keys, shared
 // by the k-head's v-heads). Both sizes are multiples of 256 bytes.
 constexpr int kPrefillRecordBytes = 5376;
-constexpr int kPrefillKeyRecordBytes = 8192;
+constexpr int kPrefillKeyRecordBytes = 4096;
 // The chunk chain runs in segments of 2^seg_shift tokens (seg_shift >= 8); after the
 // records the workspace holds a table of segment ids and, per (segment, v-head), a slot of
 // a d_k x d_v fp32 state and a d_k x d_k bf16 map.

@@ -66,9 +66,19 @@ constexpr int kRecGQ = 5184;   // Gam_t rq_t [16] fp32
 constexpr int kRecGC = 5248;   // Gam_C fp32
 static_assert(kRecGC + 4 <= kPrefillRecordBytes && kPrefillRecordBytes % 256 == 0, "record layout");
 // per (chunk, k-head), kPrefillKeyRecordBytes in total, after all the v-head records:
-constexpr int kKeyQ = 0;       // Q (stored values), A operand of 16x16x32, like -W
-constexpr int kKeyKT = 4096;   // K^T, A operand of 16x16x16, tiles 2m, 2m+1: [m][lane][2 x 4 bf16]
+constexpr int kKeyKT = 0;      // K^T, A operand of 16x16x16, tiles 2m, 2m+1: [m][lane][2 x 4 bf16]
 static_assert(kKeyKT + 4096 == kPrefillKeyRecordBytes, "key record layout");
+
+// The chain's output product (Q S_0)^T = S_0^T Q^T takes its queries straight from the q
+// tensor: the 32 keys 32 m .. 32 m + 31 of a 16x16x32 product sit as key 32 m + 8 g + e in
+// slot e of lane group g, so a lane's eight queries are 16 consecutive bytes of a row. The
+// state wave hands S_0 over in the same key order (the products with -W keep theirs).
+// s16x4 (4 bf16) of state tile kt (rows 16 kt + 4 l4 + i, column l16) into the handover
+// block of keys 32 (kt / 2) .. + 31, as the B operand in that key order
+__device__ __forceinline__ void hand_tile(s16x8* blk, int kt, int l16, int l4, const s16x4& x) {
+  char* b = reinterpret_cast<char*>(blk);
+  *reinterpret_cast<s16x4*>(b + 16 * (l16 + 16 * (2 * (kt & 1) + (l4 >> 1))) + 8 * (l4 & 1)) = x;
+}
 
 __device__ __forceinline__ f32x4 mfma(const s16x4& a, const s16x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -295,17 +305,14 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
       pA[vh] = bf16x4(pv[0], pv[1], pv[2], pv[3]);
     }
     // ---- 5a. K^T tiles by the identity product (lane (g, key 16kt + l16): tokens 4g ..),
-    //          and the k-head's record of K^T and Q, before the solve: the keys and queries
-    //          then need no registers across it
+    //          and the k-head's record of K^T, before the solve: the keys and queries then
+    //          need no registers across it
     s16x4 ktA[kKT];
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) {
       ktA[2 * m] = bf16x4(mfma(lo4(kA[m]), eye, zero4));
       ktA[2 * m + 1] = bf16x4(mfma(hi4(kA[m]), eye, zero4));
-      if (key_writer) {
-        *reinterpret_cast<s16x8*>(krec + kKeyKT + m * 1024 + l * 16) = cat8(ktA[2 * m], ktA[2 * m + 1]);
-        *reinterpret_cast<s16x8*>(krec + kKeyQ + m * 1024 + l * 16) = qA[m];  // zero past the end
-      }
+      if (key_writer) *reinterpret_cast<s16x8*>(krec + kKeyKT + m * 1024 + l * 16) = cat8(ktA[2 * m], ktA[2 * m + 1]);
     }
     lds_sync();
     // ---- 4. Tm = (I + A)^-1 by forward substitution, one column per lane (lanes < 16 VH),
@@ -542,7 +549,10 @@ __device__ __forceinline__ void state_chain(const PrefillArgs& p, ScanLds<NCB>& 
 #pragma unroll
       for (int ct = 0; ct < NCB; ++ct) {
         const s16x8 sB = cat8(bf16x4(S[ct][2 * m]), bf16x4(S[ct][2 * m + 1]));
-        if constexpr (HANDOFF) L.s[buf][ct][m][l] = sB;
+        if constexpr (HANDOFF) {
+          hand_tile(L.s[buf][ct][m], 2 * m, l16, l4, bf16x4(S[ct][2 * m]));
+          hand_tile(L.s[buf][ct][m], 2 * m + 1, l16, l4, bf16x4(S[ct][2 * m + 1]));
+        }
         if (m & 1)
           u1[ct] = mfma32(c.w[m], sB, u1[ct]);
         else
@@ -584,13 +594,16 @@ __device__ __forceinline__ void output_chain(const PrefillArgs& p, ScanLds<NCB>&
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   uint16_t* og = static_cast<uint16_t*>(p.o);
   const uint32_t o_gq = uint32_t(kRecGQ + 4 * l16);
+  const int last = max(a.t1 - 1, 0);
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + size_t(a.kh) * kDK + 8 * l4;
   auto fetch = [&](int j) -> OutOps {
     OutOps c;
     const int64_t rid = min(a.rid0 + j, p.records - 1);
     const char* rec = head_record(p, rid, a.h);
-    const char* krec = key_record(p, rid, a.kh);
+    // queries of token l16 (clamped: rows past the end only reach outputs not stored)
+    const uint16_t* qrow = qg + size_t(min(a.t0 + j * kC + l16, last)) * p.Hk * kDK;
 #pragma unroll
-    for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(krec + kKeyQ + m * 1024 + o_l);
+    for (int m = 0; m < kKT / 2; ++m) c.q[m] = *reinterpret_cast<const s16x8*>(qrow + 32 * m);
     c.pm = *reinterpret_cast<const s16x4*>(rec + kRecTP + o_l + 8);  // the upper half
     c.gq = *reinterpret_cast<const float*>(rec + o_gq);
     return c;
@@ -750,7 +763,7 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
 //   B(j + 1) publishes it.
 constexpr int kStW = 0;          // -W: 4 x 1 KiB, as in the v-head record
 constexpr int kStKT = 4096;      // K^T: 4 x 1 KiB, as in the k-head record
-constexpr int kStQ = 8192;       // Q: 4 x 1 KiB, as in the k-head record
+constexpr int kStQ = 8192;       // Q: 4 x 1 KiB, from q, keys in the order of the handover
 constexpr int kStTP = 12288;     // Tm diag(beta) and P: 1 KiB
 constexpr int kStSmall = 13312;  // record bytes kRecF .. kRecF + 255: f, Gam rq, Gam_C
 constexpr int kStV = 13568;      // V of the group's 16 CH columns, token t at byte 32 CH t
@@ -844,7 +857,10 @@ __device__ __forceinline__ void staged_chain(GroupLds<CH, RING>& L, f32x4 (&S)[k
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) {
       const s16x8 sB = cat8(bf16x4(S[2 * m]), bf16x4(S[2 * m + 1]));
-      if constexpr (HANDOFF) H.s[buf][0][m][l] = sB;
+      if constexpr (HANDOFF) {
+        hand_tile(H.s[buf][0][m], 2 * m, l16, l4, bf16x4(S[2 * m]));
+        hand_tile(H.s[buf][0][m], 2 * m + 1, l16, l4, bf16x4(S[2 * m + 1]));
+      }
       if (m & 1)
         u1 = mfma32(c.w[m], sB, u1);
       else
@@ -1057,6 +1073,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
                                                  min(16 * CH * grp, p.DV - 16 * CH)) +
                    16 * (l % (2 * CH));
   const size_t vrow_b = size_t(p.Hv) * p.DV * 2;
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + size_t(kh) * kDK + 8 * (l >> 4);
   // chunk c (records clamped into the workspace, tokens to the sequence: the chunks past
   // the end that the ring reaches are loaded but never used)
   auto issue = [&](int c) {
@@ -1064,11 +1081,14 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     const int64_t rid = min(rid0 + c, p.records - 1);
     const char* rec = head_record(p, rid, h);
     const char* krec = key_record(p, rid, kh) + 16 * l;
+    // queries of token l % 16, keys 32 m + 8 (l / 16) .. + 7 (clamped: rows past the end only
+    // reach outputs not stored)
+    const uint16_t* qrow = qg + size_t(min(ts + c * kC + (l & 15), last)) * p.Hk * kDK;
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) {
       to_lds16(rec + kRecW + m * 1024 + 16 * l, s + kStW + m * 1024);
       to_lds16(krec + kKeyKT + m * 1024, s + kStKT + m * 1024);
-      to_lds16(krec + kKeyQ + m * 1024, s + kStQ + m * 1024);
+      to_lds16(qrow + 32 * m, s + kStQ + m * 1024);
     }
     to_lds16(rec + kRecTP + 16 * l, s + kStTP);
     to_lds4(rec + kRecF + 4 * l, s + kStSmall);

@@ -82,7 +82,7 @@ def test_noalloc_graph_replay():
 
 
 def test_noalloc_refuses_calls_beyond_the_array():
-    w = PrefillWorkload("noalloc-too-large", seqlens=(27000,), Hk=4, Hv=8, dk=128, dv=128, pool=1,
+    w = PrefillWorkload("noalloc-too-large", seqlens=(36000,), Hk=4, Hv=8, dk=128, dv=128, pool=1,
                         state_dtype="bf16", io_dtype="bf16")
     need = gdn.gdn_prefill_workspace_bytes(w.batch, w.tokens, w.Hk, w.Hv, w.dk, w.dv, torch.bfloat16)
     assert need > gdn.GDN_PREFILL_NOALLOC_BYTES
