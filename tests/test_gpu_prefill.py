@@ -145,6 +145,20 @@ def test_prefill_segment_boundaries(state):
     check(w, x, w.name)
 
 
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+def test_prefill_segments_in_four_chain_groups(state):
+    """A long sequence next to short ones, d_v = 64 and 8 v-heads: the chain runs in segments
+    whose groups hold four chains (more than one two-chain workgroup per CU), and in the
+    first phase the groups past the value columns carry only map columns (their value-column
+    waves take part in the barriers alone). A fresh row, a padding row and slow decay, so
+    that the composed maps carry weight."""
+    w = PrefillWorkload(f"segments-quads-{state}", seqlens=(8000, 0, 37, 300), Hk=4, Hv=8, dk=128, dv=64, pool=6,
+                        state_dtype=state, io_dtype="bf16", n_fresh=1, n_pad=1, qk="raw")
+    x = workloads.make_prefill_inputs(w, seed=9)
+    x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
+    check(w, x, w.name)
+
+
 def test_prefill_wide_column_tiles():
     """Batches with two or more chains per SIMD (2 B Hv d_v/16 >= 2048 waves) and a d_v that
     is not a multiple of 64 run the chain on waves of two 16-column tiles: d_v = 96 (three such blocks per head), ragged
