@@ -729,11 +729,11 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
   }
 }
 
-// ============================================================ pass 2, one segment per sequence:
-// two or four chains per workgroup with their records staged in LDS
+// ============================================================ pass 2: the chains in groups of
+// two or four per workgroup, with their records staged in LDS
 //
 // A workgroup of 2 CH + 1 waves runs the chains of CH neighbouring 16-column blocks of one
-// (sequence, v-head): waves 0 .. CH-1 are their state waves, CH .. 2CH-1 their output
+// (sequence or segment, v-head): waves 0 .. CH-1 are their state waves, CH .. 2CH-1 their output
 // waves, and wave 2CH copies each chunk's records and the group's 16 CH value columns from
 // the workspace into a ring of LDS slots with direct-to-LDS loads (global_load_lds_dwordx4),
 // once for all the chains. The chains read their operands out of LDS, so each record byte
@@ -743,11 +743,11 @@ __global__ __launch_bounds__(128) void scan_kernel(const PrefillArgs p) {
 // wave loaded its own operands. Only the copying wave issues direct-to-LDS loads, so the
 // other waves' LDS reads need no wait on vector memory; it waits for its own loads with
 // explicit vmcnt counts before the barrier that publishes them.
-// CH = 2 (one chain wave per SIMD) when the chains are fewer than two per SIMD; CH = 4 (two
-// per SIMD, four chains sharing each record read) when there are more: 4 x 4096 tokens
-// with 32 v-heads, pass 2 231 -> 177 us against waves of two column tiles loading their own
-// records; two-chain workgroups there, one per CU at a time, took 232 us, and two per CU
-// (a ring of four slots to fit LDS) 274 us.
+// CH = 2 (one chain wave per SIMD) while two-chain workgroups fit one per CU (one fits in LDS
+// at a time); CH = 4 (two chain waves per SIMD, four chains sharing each record read) when
+// there are more: 4 x 4096 tokens with 32 v-heads, pass 2 231 -> 177 us against waves of two
+// column tiles loading their own records; two-chain workgroups there, one per CU at a time,
+// took 232 us, and two per CU (a ring of four slots to fit LDS) 274 us.
 //
 // Schedule, with B(j) the barrier of chunk j that all the waves reach once per chunk
 // (B(-1) before the first chunk). Chunk c is published at B(c - 2), so that every wave reads
