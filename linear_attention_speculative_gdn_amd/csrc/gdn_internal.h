@@ -85,7 +85,7 @@ struct ConvArgs {
 hipError_t launch_conv(Dt io, bool commit_only, const ConvArgs& p, hipStream_t stream);
 
 // The prefill workspace holds, per 16-token chunk, one record per v-head (the products
-// that involve the gates) and then one per k-head (its queries and transposed keys, shared
+// that involve the gates) and then one per k-head (its transposed keys, shared
 // by the k-head's v-heads). Both sizes are multiples of 256 bytes.
 constexpr int kPrefillRecordBytes = 5376;
 constexpr int kPrefillKeyRecordBytes = 4096;
