@@ -159,6 +159,17 @@ def test_prefill_segments_in_four_chain_groups(state):
     check(w, x, w.name)
 
 
+def test_prefill_two_v_heads_per_pass1_wave_g4():
+    """Pass 1 takes two v-heads of a k-head per wave once one wave per (chunk, v-head) would
+    exceed the chip (chunk records x v-heads > 4096): here with four v-heads per k-head, so
+    each k-head's pair of waves shares its keys and queries, ragged lengths, a fresh row and
+    unnormalised q/k with weak decay."""
+    w = PrefillWorkload("g4-vh2", seqlens=(2100, 1999, 17, 2048, 2300), Hk=2, Hv=8, dk=128, dv=128, pool=6,
+                        state_dtype="bf16", io_dtype="bf16", n_fresh=1, qk="raw", decay="weak")
+    assert (w.tokens // 16 + w.batch) * w.Hv > 4096 and (w.Hv // w.Hk) % 2 == 0
+    check(w, workloads.make_prefill_inputs(w, seed=10), w.name)
+
+
 def test_prefill_wide_column_tiles():
     """Batches with two or more chains per SIMD (2 B Hv d_v/16 >= 2048 waves) and a d_v that
     is not a multiple of 64 run the chain on waves of two 16-column tiles: d_v = 96 (three such blocks per head), ragged
