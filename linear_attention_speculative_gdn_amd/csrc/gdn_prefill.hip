@@ -937,7 +937,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
   if (outputs && 16 * CH * grp >= p.DV) return;     // (map columns past the value columns)
 
   if (slot < 0 || slot >= p.P) {  // padding row: o = 0 for its tokens, no state access
-    if (MODE == 2) return;        // (zeroed with segment 0)
+    if (g != 0) return;           // zeroed once, by segment 0's groups (of value columns only)
     uint16_t* og = static_cast<uint16_t*>(p.o);
     for (int e = int(threadIdx.x); e < (t1 - t0) * 2 * CH; e += kThreads) {
       const int t = t0 + e / (2 * CH);

@@ -159,6 +159,24 @@ def test_prefill_segments_in_four_chain_groups(state):
     check(w, x, w.name)
 
 
+@pytest.mark.parametrize("Hk,Hv,seqlens", [(1, 2, (1100, 40, 900)), (4, 8, (3000, 40, 2600))],
+                         ids=["two-chain-groups", "four-chain-groups"])
+def test_prefill_long_padding_rows_in_segments(Hk, Hv, seqlens):
+    """Padding rows long enough to have middle segments, with d_v = 64: the first phase's
+    groups of such a row include ones for the map columns past the value columns, and only
+    segment 0's groups (of value columns) write its zeros. The first padding row is followed
+    by a valid short row, whose outputs must survive; the last row, also padding, ends the
+    output buffer. Two- and four-chain groups, slow decay."""
+    for state in ("f32", "bf16"):
+        w = PrefillWorkload(f"long-padding-{Hv}-{state}", seqlens=seqlens, Hk=Hk, Hv=Hv, dk=128, dv=64, pool=4,
+                            state_dtype=state, io_dtype="bf16", qk="raw")
+        x = workloads.make_prefill_inputs(w, seed=11)
+        x["idx"][0] = -1
+        x["idx"][2] = -1
+        x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
+        check(w, x, w.name)
+
+
 def test_prefill_two_v_heads_per_pass1_wave_g4():
     """Pass 1 takes two v-heads of a k-head per wave once one wave per (chunk, v-head) would
     exceed the chip (chunk records x v-heads > 4096): here with four v-heads per k-head, so
