@@ -159,20 +159,23 @@ def test_prefill_segments_in_four_chain_groups(state):
     check(w, x, w.name)
 
 
-@pytest.mark.parametrize("Hk,Hv,seqlens", [(1, 2, (1100, 40, 900)), (4, 8, (3000, 40, 2600))],
+@pytest.mark.parametrize("Hk,Hv,seqlens", [(1, 2, (1100, 40, 700, 900)), (4, 8, (3000, 40, 1800, 2600))],
                          ids=["two-chain-groups", "four-chain-groups"])
-def test_prefill_long_padding_rows_in_segments(Hk, Hv, seqlens):
+def test_prefill_long_padding_and_fresh_rows_in_segments(Hk, Hv, seqlens):
     """Padding rows long enough to have middle segments, with d_v = 64: the first phase's
     groups of such a row include ones for the map columns past the value columns, and only
     segment 0's groups (of value columns) write its zeros. The first padding row is followed
     by a valid short row, whose outputs must survive; the last row, also padding, ends the
-    output buffer. Two- and four-chain groups, slow decay."""
+    output buffer. A fresh row of several segments starts its chain from zero and its later
+    segments from the composed states. Two- and four-chain groups, slow decay."""
     for state in ("f32", "bf16"):
         w = PrefillWorkload(f"long-padding-{Hv}-{state}", seqlens=seqlens, Hk=Hk, Hv=Hv, dk=128, dv=64, pool=4,
                             state_dtype=state, io_dtype="bf16", qk="raw")
         x = workloads.make_prefill_inputs(w, seed=11)
         x["idx"][0] = -1
-        x["idx"][2] = -1
+        x["idx"][3] = -1
+        x["fresh"][:] = 0
+        x["fresh"][2] = 1
         x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
         check(w, x, w.name)
 
