@@ -14,23 +14,26 @@
 //     O = scale (diag(Gam) Q^ S_0 + (M o Q^ K^T) U),  M_ts = Gam_t / Gam_s  (s <= t)
 //     S_C = Gam_C S_0 + K^T diag(Gam_C / Gam) U
 // which equals the token-by-token recurrence up to rounding. Every product is a dense
-// contraction, on v_mfma_f32_16x16x16_bf16 with fp32 accumulation.
+// contraction, on the 16x16x16 and 16x16x32 bf16 matrix-core products with fp32
+// accumulation.
 //
 // Design for gfx950:
 // - Pass 1 (chunk_kernel) computes, for every (chunk, v-head) in parallel, everything that
 //   does not depend on the state -- W = Tm diag(beta Gam rk) K, Tm diag(beta), the output
 //   mask P, K^T and the per-token factors -- into workspace records. That is most of a
-//   chunk's instructions, and none of it is sequential. Queries and K^T do not depend on
-//   the gates: they go to one record per k-head, written by its first v-head, which the
-//   other v-heads of the group read too.
-// - Pass 2 (group_chain_kernel, or scan_kernel for the segmented form) walks each
-//   sequence's chunks in order with the state in MFMA accumulators: U~ = Tm diag(beta) V,
-//   W S_0, Q S_0, P U and the state update only. Later chunks' records are loaded while the
-//   current chunk computes (in group_chain_kernel, copied into LDS once for its chains).
-// - One pass-2 wave per (sequence, v-head, block of NB value columns): columns are
+//   chunk's instructions, and none of it is sequential. K^T does not depend on the gates:
+//   it goes to one record per k-head, written by its first v-head, which the other
+//   v-heads of the group read too.
+// - Pass 2 walks each sequence's chunks in order with the state in MFMA accumulators:
+//   U~ = Tm diag(beta) V, W S_0, Q S_0, P U and the state update only. group_chain_kernel
+//   runs two or four chains per workgroup on records one wave copies into LDS ahead of
+//   use, for whole sequences or in segments whose maps are composed; scan_kernel's waves
+//   of two column tiles serve wide grids of whole sequences whose d_v is not a multiple
+//   of 64, loading their records themselves.
+// - One chain per (sequence or segment, v-head, block of 16 value columns): columns are
 //   independent given the record. A 16 x 16 accumulator tile holds, per lane, four
-//   consecutive rows of one column -- the B-operand layout -- so S_0 feeds W S_0 and
-//   Q S_0 after a bf16 conversion in registers.
+//   consecutive rows of one column -- the B-operand layout -- so S_0 feeds W S_0 after a
+//   bf16 conversion in registers, and goes to the output product through LDS.
 // - Keys and queries enter the products as their stored bf16 values; norms, gates and
 //   decays are fp32 diagonal scalings of the 16 x 16 chunk matrices.
 // - Records are numbered floor(cu[r] / 16) + j + r for chunk j of sequence r: distinct, and
