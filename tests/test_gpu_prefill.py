@@ -180,6 +180,24 @@ def test_prefill_long_padding_and_fresh_rows_in_segments(Hk, Hv, seqlens):
         check(w, x, w.name)
 
 
+@pytest.mark.parametrize("dv,Hk,Hv", [(32, 1, 1), (256, 1, 1), (256, 1, 3)],
+                         ids=["dv32", "dv256-two-chain-groups", "dv256-four-chain-groups"])
+def test_prefill_segments_narrow_and_wide_dv(dv, Hk, Hv):
+    """Segmented chains with d_v = 32 (one group of value columns, the others map columns
+    only) and d_v = 256 (twice d_k: groups past the map columns carry value columns only),
+    in two- and four-chain groups, ragged lengths of one to six segments, a padding row and
+    a fresh row, fp32 and bf16 pools, slow decay."""
+    for state in ("f32", "bf16"):
+        w = PrefillWorkload(f"segments-dv{dv}-hv{Hv}-{state}", seqlens=(700, 30, 1300, 260), Hk=Hk, Hv=Hv, dk=128,
+                            dv=dv, pool=4, state_dtype=state, io_dtype="bf16", qk="raw")
+        x = workloads.make_prefill_inputs(w, seed=12)
+        x["idx"][3] = -1
+        x["fresh"][:] = 0
+        x["fresh"][2] = 1
+        x["A_log"] = torch.full((w.Hv,), float(np.log(0.02)), dtype=torch.float32)
+        check(w, x, w.name)
+
+
 def test_prefill_two_v_heads_per_pass1_wave_g4():
     """Pass 1 takes two v-heads of a k-head per wave once one wave per (chunk, v-head) would
     exceed the chip (chunk records x v-heads > 4096): here with four v-heads per k-head, so
