@@ -204,7 +204,8 @@ GDN_API gdn_status gdn_prefill_noalloc(const gdn_dims* dims, const gdn_io* io, v
 
 /* Workspace size of gdn_prefill, in three parts:
  * - per 16-token chunk, (floor(num_tokens / 16) + batch) of them, one 5376-byte record per
- *   v-head (a 4096-byte bf16 chunk x d_k operand, two 512-byte 16 x 16 bf16 matrices, the
+ *   v-head (a 4096-byte bf16 chunk x d_k operand -- or, when the chain runs in segments, the
+ *   512-byte 16 x 16 factor it is formed from -- two 512-byte 16 x 16 bf16 matrices, the
  *   per-token factors, padding) and one 4096-byte record per k-head (the chunk's
  *   transposed keys, shared by the k-head's v-heads);
  * - a table of the segments of the chunk chain, 4 bytes each, padded to 256 bytes;

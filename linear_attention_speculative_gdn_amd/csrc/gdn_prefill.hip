@@ -62,7 +62,9 @@ constexpr int kKT = kDK / 16; // 16-row tiles of the key dimension
 // Workspace records: byte offsets. Every matrix is stored in the lane layout of the
 // matrix-core operand that reads it, so a pass-2 lane fetches its part with 16-byte loads
 // of contiguous 1 KiB blocks. Per (chunk, v-head), kPrefillRecordBytes in total:
-constexpr int kRecW = 0;       // -W, A operand of 16x16x32: [32-key block m][lane][8 bf16]
+constexpr int kRecW = 0;       // -W, A operand of 16x16x32: [32-key block m][lane][8 bf16]; for a chain in
+                               // segments the 16 x 16 factor -Tm diag(beta Gam rk) instead, A operand of
+                               // 16x16x16: [lane][4 bf16] (the chain forms -W from it and K^T)
 constexpr int kRecTP = 4096;   // Tm diag(beta) and P = M o (rq rk) Q K^T, A operands: [lane][2 x 4 bf16]
 constexpr int kRecF = 5120;    // f_t = rk_t Gam_C / Gam_t [16] fp32
 constexpr int kRecGQ = 5184;   // Gam_t rq_t [16] fp32
@@ -183,7 +185,7 @@ struct __attribute__((aligned(16))) ChunkLds {
 // matrix core already in the layout their A operands need. LDS holds only the 16 x 16 solves.
 // With VH = 2 the keys, queries, their norms, K K^T, K Q^T and K^T serve both v-heads, and
 // the two triangular solves run side by side, one per 16 lanes.
-template <int VH>
+template <int VH, bool WF>
 __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   __shared__ ChunkLds L[VH];
   const int h0 = blockIdx.y * VH, row = blockIdx.z;
@@ -364,12 +366,17 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
       char* rec = head_record(p, rid, h0 + vh);
       const s16x4 twA = ld4(L[vh].tw, l16, kC, 4 * l4), tvA = ld4(L[vh].tv, l16, kC, 4 * l4);
       // ---- 5b. -W^T = K^T (-TW)^T gives -W in the A layout (lane (t, g): keys 16kt + 4g ..),
-      //          stored by 32-key blocks
+      //          stored by 32-key blocks; WF: the factor -TW alone, from which the chain
+      //          forms the same -W with the same product (a eighth of the bytes)
+      if constexpr (WF) {
+        *reinterpret_cast<s16x4*>(rec + kRecW + l * 8) = twA;
+      } else {
 #pragma unroll
-      for (int m = 0; m < kKT / 2; ++m) {
-        const s16x4 w0 = bf16x4(mfma(ktA[2 * m], twA, zero4));
-        const s16x4 w1 = bf16x4(mfma(ktA[2 * m + 1], twA, zero4));
-        *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
+        for (int m = 0; m < kKT / 2; ++m) {
+          const s16x4 w0 = bf16x4(mfma(ktA[2 * m], twA, zero4));
+          const s16x4 w1 = bf16x4(mfma(ktA[2 * m + 1], twA, zero4));
+          *reinterpret_cast<s16x8*>(rec + kRecW + m * 1024 + l * 16) = cat8(w0, w1);
+        }
       }
       // ---- 6. Tm diag(beta) and P, the per-token factors
       *reinterpret_cast<s16x8*>(rec + kRecTP + l * 16) = cat8(tvA, pA[vh]);
@@ -773,7 +780,7 @@ constexpr int kStV = 13568;      // V of the group's 16 CH columns, token t at b
 static_assert(kRecF + 256 <= kPrefillRecordBytes && kRecGQ - kRecF == 64 && kRecGC - kRecF == 128, "small fields");
 // bytes of a slot and direct-to-LDS loads per chunk for CH chains
 constexpr int st_bytes(int CH) { return kStV + 512 * CH; }
-constexpr int st_loads(int CH) { return 14 + CH / 2; }
+constexpr int st_loads(int CH, bool WF) { return (WF ? 11 : 14) + CH / 2; }
 
 // RING slots: chunks j .. j + RING - 1 around chunk j
 template <int CH, int RING>
@@ -809,19 +816,21 @@ __device__ __forceinline__ void wait_vm() {
 struct StOps {
   s16x8 w[kKT / 2];   // -W, A layout of 16x16x32
   s16x8 kt[kKT / 2];  // K^T tiles 2m, 2m+1, A layout of 16x16x16
+  s16x4 tw;           // WF: -Tm diag(beta Gam rk), A layout of 16x16x16
   s16x4 tv;           // Tm diag(beta), A layout
   s16x4 v;            // V of token l16, columns 4 l4 .. + 3 of the chain's block
   f32x4 f;            // f of tokens 4 l4 .. 4 l4 + 3
   float gc;           // Gam_C
 };
-template <int CH>
+template <int CH, bool WF>
 __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, int l, int l16, int l4) {
   StOps c;
 #pragma unroll
   for (int m = 0; m < kKT / 2; ++m) {
-    c.w[m] = lds_ld<s16x8>(s + kStW + m * 1024 + 16 * l);
+    if constexpr (!WF) c.w[m] = lds_ld<s16x8>(s + kStW + m * 1024 + 16 * l);
     c.kt[m] = lds_ld<s16x8>(s + kStKT + m * 1024 + 16 * l);
   }
+  if constexpr (WF) c.tw = lds_ld<s16x4>(s + kStW + 8 * l);
   c.tv = lds_ld<s16x4>(s + kStTP + 16 * l);  // the lower half
   c.v = lds_ld<s16x4>(s + kStV + 32 * CH * l16 + 32 * chain + 8 * l4);
   c.f = lds_ld<f32x4>(s + kStSmall + 16 * l4);
@@ -829,12 +838,26 @@ __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, in
   return c;
 }
 
+// -W from K^T and the factor: pass 1's own product of the same bf16 operands, so the same bits.
+// Halves h0 .. h1 - 1 of two 32-key blocks each, so that at most four products' fp32 results
+// are live (all eight at once pushed four-chain workgroups past their register budget).
+__device__ __forceinline__ void build_w(StOps& c, int h0, int h1) {
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = h0; h < h1; ++h) {
+#pragma unroll
+    for (int m = 2 * h; m < 2 * h + 2; ++m)
+      c.w[m] = cat8(bf16x4(mfma(lo4(c.kt[m]), c.tw, zero4)), bf16x4(mfma(hi4(c.kt[m]), c.tw, zero4)));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // The chain of one column block over the staged chunks 0 .. jb - 1 (chunk j in slot j % RING),
 // with S in MFMA accumulators: U = Tm diag(beta) V - W S_0 (WITH_V: the values term, off for
 // a segment map), then S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U. HANDOFF: bf16 S_0 and U
 // go to the chain's output wave through buffer j & 1 before B(j). One barrier per chunk,
 // B(-1) first, as every wave of the workgroup.
-template <int CH, int RING, bool WITH_V, bool HANDOFF>
+template <int CH, int RING, bool WITH_V, bool HANDOFF, bool WF>
 __device__ __forceinline__ void staged_chain(GroupLds<CH, RING>& L, f32x4 (&S)[kKT], int chain, int jb) {
   const int l = threadIdx.x & 63, l16 = l & 15, l4 = l >> 4;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -844,7 +867,7 @@ __device__ __forceinline__ void staged_chain(GroupLds<CH, RING>& L, f32x4 (&S)[k
   // the next chunk's operands, U of chunk j, the handover, B(j), the update
   auto step = [&](const StOps& c, StOps& next, int j) {
     const int buf = j & 1;
-    next = read_state_ops<CH>(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
+    next = read_state_ops<CH, WF>(slot_of(j + 1), chain, l, l16, l4);  // published at B(j - 1)
     __builtin_amdgcn_sched_barrier(0);  // they go out first
     f32x4 tvv = zero4;
     if constexpr (WITH_V) {
@@ -871,6 +894,10 @@ __device__ __forceinline__ void staged_chain(GroupLds<CH, RING>& L, f32x4 (&S)[k
     }
     const f32x4 u = (u0 + u1) + tvv;
     if constexpr (HANDOFF) H.u[buf][0][l] = bf16x4(u);
+    // WF: the next chunk's -W, half here, where the matrix core has finished -W S_0, and
+    // half after the barrier, ahead of the update's products (all of it here, the long
+    // prompt took 114 us instead of 111)
+    if constexpr (WF) build_w(next, 0, 1);
     // Gam_C S_0 before the barrier, where it overlaps the products and the wait; placed
     // after it, between the update's products, it measured slower
 #pragma unroll
@@ -879,11 +906,13 @@ __device__ __forceinline__ void staged_chain(GroupLds<CH, RING>& L, f32x4 (&S)[k
     barrier_lds();  // B(j)
     // S <- Gam_C S_0 + K^T diag(rk Gam_C / Gam) U
     const s16x4 uB = bf16x4(c.f[0] * u[0], c.f[1] * u[1], c.f[2] * u[2], c.f[3] * u[3]);
+    if constexpr (WF) build_w(next, 1, 2);
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) S[kt] = mfma((kt & 1) ? hi4(c.kt[kt / 2]) : lo4(c.kt[kt / 2]), uB, S[kt]);
   };
   barrier_lds();  // B(-1)
-  StOps ca = read_state_ops<CH>(slot_of(0), chain, l, l16, l4), cb;
+  StOps ca = read_state_ops<CH, WF>(slot_of(0), chain, l, l16, l4), cb;
+  if constexpr (WF) build_w(ca, 0, 2);
   for (int j = 0; j < jb; j += 2) {
     step(ca, cb, j);
     if (j + 1 >= jb) break;
@@ -906,7 +935,9 @@ __device__ __forceinline__ void barriers_only(int jb) {
 // predecessor's slot, with outputs, the last one storing the final state.
 template <typename ST, int CH, int RING, int MODE>
 __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const PrefillArgs p) {
-  constexpr int kStLoads = st_loads(CH);
+  // chains in segments (MODE 1, 2) form -W from its factor (pass 1 wrote the factor then)
+  constexpr bool WF = MODE != 0;
+  constexpr int kStLoads = st_loads(CH, WF);
   // the copying wave's loads newer than chunk j + 3's when it waits: RING - 3 chunks'. Its
   // counter of vector-memory operations in flight holds at most 63, so it never has more
   // than RING - 2 chunks' loads in flight.
@@ -969,7 +1000,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     if (!is_map) {
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) S[kt] = zero4;
-      if (jb > 0) staged_chain<CH, RING, true, false>(L, S, chain, jb);
+      if (jb > 0) staged_chain<CH, RING, true, false, WF>(L, S, chain, jb);
       f32x4* dst = slot_block(p, sid, h, c0 / 16);
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) dst[kt * 64] = S[kt];
@@ -979,7 +1010,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[kt][i] = (16 * kt + 4 * l4 + i == 16 * J + l16) ? 1.f : 0.f;
-      if (jb > 0) staged_chain<CH, RING, false, false>(L, S, chain, jb);
+      if (jb > 0) staged_chain<CH, RING, false, false, WF>(L, S, chain, jb);
       // Tile (kt, J) read as an A operand is its transpose; the identity product turns that
       // back into the tile itself in the A layout, exactly (bf16 in, single terms).
       const s16x4 eye = identity_b(l16, l4);
@@ -1008,7 +1039,7 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
         S[kt] = fresh ? zero4 : s;
       }
     }
-    if (jb > 0) staged_chain<CH, RING, true, true>(L, S, chain, jb);
+    if (jb > 0) staged_chain<CH, RING, true, true, WF>(L, S, chain, jb);
     if (MODE == 1 && nseg > 1) {  // segment 0's end state, for the maps to carry forward
       f32x4* dst = slot_block(p, sid, h, c0 / 16);
 #pragma unroll
@@ -1089,10 +1120,11 @@ __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const Pr
     const uint16_t* qrow = qg + size_t(min(ts + c * kC + (l & 15), last)) * p.Hk * kDK;
 #pragma unroll
     for (int m = 0; m < kKT / 2; ++m) {
-      to_lds16(rec + kRecW + m * 1024 + 16 * l, s + kStW + m * 1024);
+      if constexpr (!WF) to_lds16(rec + kRecW + m * 1024 + 16 * l, s + kStW + m * 1024);
       to_lds16(krec + kKeyKT + m * 1024, s + kStKT + m * 1024);
       to_lds16(qrow + 32 * m, s + kStQ + m * 1024);
     }
+    if constexpr (WF) to_lds16(rec + kRecW + 16 * l, s + kStW);  // the factor: the first 512 bytes
     to_lds16(rec + kRecTP + 16 * l, s + kStTP);
     to_lds4(rec + kRecF + 4 * l, s + kStSmall);
 #pragma unroll
@@ -1262,10 +1294,19 @@ hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
   const int vh = (p.G % 2 == 0 && p.records * p.Hv > 4096) ? 2 : 1;  // v-heads per wave
   const int64_t heads = int64_t(p.B) * p.Hv;
   const unsigned strides = unsigned(std::min<int64_t>(1024, std::max<int64_t>(1, (8192 + heads - 1) / heads)));
-  if (vh == 2)
-    hipLaunchKernelGGL(chunk_kernel<2>, dim3(strides, unsigned(p.Hv / 2), unsigned(p.B)), dim3(64), 0, stream, p);
-  else
-    hipLaunchKernelGGL(chunk_kernel<1>, dim3(strides, unsigned(p.Hv), unsigned(p.B)), dim3(64), 0, stream, p);
+  // A chain in segments forms -W itself from its factor (pass 2 then stages 11 + CH/2 loads
+  // per chunk instead of 14 + CH/2; the long prompt 117.3 -> 110.9 us); whole-sequence chains,
+  // which share the matrix cores of a CU more (four chains of 4 x 4096 measured 253 -> 291 us
+  // that way), read -W.
+  const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;  // as pass 2 decides
+  const dim3 grid(strides, unsigned(p.Hv / vh), unsigned(p.B));
+  if (vh == 2) {
+    if (whole) hipLaunchKernelGGL((chunk_kernel<2, false>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_kernel<2, true>), grid, dim3(64), 0, stream, p);
+  } else {
+    if (whole) hipLaunchKernelGGL((chunk_kernel<1, false>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_kernel<1, true>), grid, dim3(64), 0, stream, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return state == Dt::F32 ? launch_pass2<float>(p, stream) : launch_pass2<bf16s>(p, stream);
