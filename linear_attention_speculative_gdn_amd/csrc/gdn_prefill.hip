@@ -933,10 +933,9 @@ __device__ __forceinline__ void barriers_only(int jb) {
 // run M (d_k columns, from the identity, without the values), neither with outputs. MODE 2:
 // the later segments, each from the start state that the maps composed into its
 // predecessor's slot, with outputs, the last one storing the final state.
-template <typename ST, int CH, int RING, int MODE>
+template <typename ST, int CH, int RING, int MODE, bool WF>
 __global__ __launch_bounds__(64 * (2 * CH + 1)) void group_chain_kernel(const PrefillArgs p) {
-  // chains in segments (MODE 1, 2) form -W from its factor (pass 1 wrote the factor then)
-  constexpr bool WF = MODE != 0;
+  // WF: the chains form -W from its factor (pass 1 wrote the factor in its place)
   constexpr int kStLoads = st_loads(CH, WF);
   // the copying wave's loads newer than chunk j + 3's when it waits: RING - 3 chunks'. Its
   // counter of vector-memory operations in flight holds at most 63, so it never has more
@@ -1233,11 +1232,11 @@ hipError_t launch_scan(const PrefillArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename ST, int CH, int RING, int MODE>
+template <typename ST, int CH, int RING, int MODE, bool WF = MODE != 0>
 hipError_t launch_group(const PrefillArgs& p, hipStream_t stream) {
   const int64_t units = (p.segments * p.Hv + kXcds - 1) / kXcds * kXcds;
   const int per = (MODE == 1 ? std::max(p.DV, kDK) : p.DV) / (16 * CH);
-  hipLaunchKernelGGL((group_chain_kernel<ST, CH, RING, MODE>), dim3(unsigned(units * per)), dim3(64 * (2 * CH + 1)), 0,
+  hipLaunchKernelGGL((group_chain_kernel<ST, CH, RING, MODE, WF>), dim3(unsigned(units * per)), dim3(64 * (2 * CH + 1)), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -1249,24 +1248,45 @@ hipError_t launch_group(const PrefillArgs& p, hipStream_t stream) {
 // the middle segments (MODE 1); combine_kernel, the start states S_{g+1} = M_g S_g + N_g in
 // sequence; every later segment again from its start state with outputs (MODE 2). The chain
 // is sequential within a segment only.
+//
+// The chains stage their records in LDS, four per workgroup when two-chain workgroups would
+// exceed one per CU (one per CU fits in LDS at a time; 4 x 4096 tokens with 32 v-heads, the
+// segments of one long prompt), else two. Chain waves of two 16-column tiles that load their
+// own records remain for many whole sequences with a d_v that is not a multiple of 64.
+struct Pass2Plan {
+  bool whole, wide, quads, quads1;
+  // the chains form -W from its factor, which pass 1 then writes in its place: every chain
+  // in segments, and whole sequences in two-chain workgroups that average 1024 tokens or
+  // more. With such sequences every CU stages records for the whole call and its copying
+  // wave, paced by the CU's memory pipeline, takes as long per chunk as the state waves:
+  // 8 x 2048 80.6 -> 77.8 us with three fewer loads per chunk. The chains of shorter
+  // sequences outlast the others with the chip to themselves, the state waves alone set
+  // their step and the products that form -W lengthen it (the mixed batch of 1 .. 1000
+  // tokens 32.4 -> 34.5 us); four chains per workgroup share the CU's matrix pipes (4 x
+  // 4096 253 -> 291 us).
+  bool factor;
+};
+inline Pass2Plan plan_pass2(const PrefillArgs& p) {
+  Pass2Plan q;
+  q.whole = (int64_t(1) << p.seg_shift) > p.tokens;
+  q.wide = q.whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
+  q.quads = p.DV % 64 == 0 && p.segments * p.Hv * (p.DV / 32) > 256;
+  q.quads1 = p.DV % 64 == 0 && p.segments * p.Hv * (std::max(p.DV, kDK) / 32) > 256;
+  q.factor = !q.whole || (!q.quads && !q.wide && p.tokens >= int64_t(1024) * p.B);
+  return q;
+}
+
 template <typename ST>
 hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
-  // The chains stage their records in LDS, four per workgroup when two-chain workgroups
-  // would exceed one per CU (one per CU fits in LDS at a time; 4 x 4096 tokens with 32
-  // v-heads, the segments of one long prompt), else two. Chain waves of two 16-column tiles
-  // that load their own records remain for many whole sequences with a d_v that is not a
-  // multiple of 64.
-  const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;
-  const bool wide = whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
-  const bool quads = p.DV % 64 == 0 && p.segments * p.Hv * (p.DV / 32) > 256;
-  const bool quads1 = p.DV % 64 == 0 && p.segments * p.Hv * (std::max(p.DV, kDK) / 32) > 256;
+  const Pass2Plan q = plan_pass2(p);
+  const bool whole = q.whole, wide = q.wide, quads = q.quads, quads1 = q.quads1;
   hipError_t e;
   if (whole && quads) {
     e = launch_group<ST, 4, 5, 0>(p, stream);
   } else if (wide) {
     e = launch_scan<ST, 2>(p, stream);
   } else if (whole) {
-    e = launch_group<ST, 2, 6, 0>(p, stream);
+    e = q.factor ? launch_group<ST, 2, 6, 0, true>(p, stream) : launch_group<ST, 2, 6, 0, false>(p, stream);
   } else {
     e = quads1 ? launch_group<ST, 4, 5, 1>(p, stream) : launch_group<ST, 2, 6, 1>(p, stream);
   }
@@ -1294,18 +1314,17 @@ hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
   const int vh = (p.G % 2 == 0 && p.records * p.Hv > 4096) ? 2 : 1;  // v-heads per wave
   const int64_t heads = int64_t(p.B) * p.Hv;
   const unsigned strides = unsigned(std::min<int64_t>(1024, std::max<int64_t>(1, (8192 + heads - 1) / heads)));
-  // A chain in segments forms -W itself from its factor (pass 2 then stages 11 + CH/2 loads
-  // per chunk instead of 14 + CH/2; the long prompt 117.3 -> 110.9 us); whole-sequence chains,
-  // which share the matrix cores of a CU more (four chains of 4 x 4096 measured 253 -> 291 us
-  // that way), read -W.
-  const bool whole = (int64_t(1) << p.seg_shift) > p.tokens;  // as pass 2 decides
+  // Where the chains form -W themselves (plan_pass2), pass 1 writes its 16 x 16 factor
+  // instead (pass 2 then stages 11 + CH/2 loads per chunk instead of 14 + CH/2; the long
+  // prompt 117.3 -> 110.9 us).
+  const bool factor = plan_pass2(p).factor;
   const dim3 grid(strides, unsigned(p.Hv / vh), unsigned(p.B));
   if (vh == 2) {
-    if (whole) hipLaunchKernelGGL((chunk_kernel<2, false>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<2, true>), grid, dim3(64), 0, stream, p);
+    if (factor) hipLaunchKernelGGL((chunk_kernel<2, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_kernel<2, false>), grid, dim3(64), 0, stream, p);
   } else {
-    if (whole) hipLaunchKernelGGL((chunk_kernel<1, false>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<1, true>), grid, dim3(64), 0, stream, p);
+    if (factor) hipLaunchKernelGGL((chunk_kernel<1, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_kernel<1, false>), grid, dim3(64), 0, stream, p);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
