@@ -326,6 +326,39 @@ def test_prefill_caller_workspace_reused_and_graph_replay():
         assert torch.equal(o_g, o_ref) and torch.equal(pool_g, pool_ref), rep
 
 
+def test_prefill_segmented_graph_replay():
+    """A call whose chains run in segments (four launches: segment 0 and the maps, their
+    composition, the later segments; the records hold the factor of -W) replays from a HIP
+    graph bit for bit like the eager call, three times, with eager work in between."""
+    w = PrefillWorkload("seg-graph", seqlens=(1100, 40, 700), Hk=1, Hv=2, dk=128, dv=64, pool=4, state_dtype="f32",
+                        io_dtype="bf16", n_fresh=1, qk="raw")
+    x = workloads.make_prefill_inputs(w, seed=13)
+    g = {n: x[n].to(DEV) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "idx", "fresh", "cu_seqlens")}
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(w.batch, w.tokens, w.Hk, w.Hv, w.dk, w.dv, torch.float32),
+                     dtype=torch.uint8, device=DEV)
+
+    def call(pool, o):
+        gdn.gdn_prefill(g["q"], g["k"], g["v"], g["a"], g["b"], g["A_log"], g["dt_bias"], o, pool, g["idx"],
+                        g["cu_seqlens"], g["fresh"], scale=w.scale, workspace=ws)
+
+    pool_ref = to_device_state(x["pool"]).to(DEV)
+    o_ref = torch.empty((w.tokens, w.Hv, w.dv), dtype=torch.bfloat16, device=DEV)
+    call(pool_ref, o_ref)
+    torch.cuda.synchronize()
+    pool_g = to_device_state(x["pool"]).to(DEV)
+    o_g = torch.empty_like(o_ref)
+    graph, stream = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=stream):
+        call(pool_g, o_g)
+    for rep in range(3):
+        pool_g.copy_(to_device_state(x["pool"]).to(DEV))
+        o_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_ref) and torch.equal(pool_g, pool_ref), rep
+
+
 def test_fp32_grade_prefill_through_verify():
     """The route to an fp32-grade prefill of an fp32 pool: the tokens through gdn_verify with
     write-back, GDN_MAX_T at a time, match the float64 prefill to the recurrent path's fp32
