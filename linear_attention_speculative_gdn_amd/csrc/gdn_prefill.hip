@@ -178,22 +178,27 @@ struct __attribute__((aligned(16))) ChunkLds {
 // exp, log, reciprocal and reciprocal square root (a few ulp; every product it feeds is
 // rounded to bf16): 1500 instructions and 35.7 us with the library functions on 8 x 2048
 // tokens, 33.9 us then.
-// grid (chunk strides, groups of VH v-heads, sequences), one wave each; wave x handles chunks
-// x, x + gridDim.x, ... of its sequence for VH v-heads of one k-head. Every product takes its
+// One wave per (chunk stride x, group of VH v-heads, sequence); wave x handles chunks x, x + the
+// stride count, ... of its sequence for VH v-heads of one k-head (WF: with -W's factor in its
+// record; CHUNK_SLOW: the grid's order, below). Every product takes its
 // operands straight from registers: keys and queries are loaded in the operand layout, K^T
 // comes from the identity product, and W^T = K^T TW^T and (Q K^T)^T = K Q^T come out of the
 // matrix core already in the layout their A operands need. LDS holds only the 16 x 16 solves.
 // With VH = 2 the keys, queries, their norms, K K^T, K Q^T and K^T serve both v-heads, and
 // the two triangular solves run side by side, one per 16 lanes.
-template <int VH, bool WF>
+template <int VH, bool WF, bool CHUNK_SLOW>
 __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   __shared__ ChunkLds L[VH];
-  const int h0 = blockIdx.y * VH, row = blockIdx.z;
+  // grid (chunk strides, head groups, sequences), or with CHUNK_SLOW (head groups, sequences,
+  // chunk strides): the chunk index then varies slowest, so the waves that have a chunk are
+  // dispatched before those past their sequence's end
+  const int h0 = (CHUNK_SLOW ? blockIdx.x : blockIdx.y) * VH, row = CHUNK_SLOW ? blockIdx.y : blockIdx.z;
+  const int x0 = CHUNK_SLOW ? blockIdx.z : blockIdx.x, nx = CHUNK_SLOW ? gridDim.z : gridDim.x;
   const int l = threadIdx.x, l16 = l & 15, l4 = l >> 4;
   const int32_t slot = p.idx[row];
   const int32_t t0 = p.cu[row], t1 = p.cu[row + 1];
   const int nchunks = (t1 - t0 + kC - 1) / kC;
-  if (blockIdx.x == 0 && h0 == 0) {
+  if (x0 == 0 && h0 == 0) {
     // the segment table entries from this sequence's first segment id up to the next
     // sequence's (to the table's end for the last; from 0 for the first): each entry is
     // written by exactly one wave
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(64) void chunk_kernel(const PrefillArgs p) {
   // the solving lanes: 16 per v-head, lane 16 vh + c solves column c of v-head vh
   const int sv = VH == 2 ? (l >> 4) & 1 : 0;
 
-  for (int j = blockIdx.x; j < nchunks; j += gridDim.x) {
+  for (int j = x0; j < nchunks; j += nx) {
     const int64_t rid = record_id(t0, row, j);
     if (rid >= p.records) return;  // workspace too small for the tokens: write nothing
     char* krec = key_record(p, rid, kh);
@@ -1318,13 +1323,20 @@ hipError_t launch_prefill(Dt state, const PrefillArgs& p, hipStream_t stream) {
   // instead (pass 2 then stages 11 + CH/2 loads per chunk instead of 14 + CH/2; the long
   // prompt 117.3 -> 110.9 us).
   const bool factor = plan_pass2(p).factor;
-  const dim3 grid(strides, unsigned(p.Hv / vh), unsigned(p.B));
+  // When most waves would find no chunk (the strides cover more than twice the tokens: short
+  // sequences beside long ones), the chunk index varies slowest in the grid, so the waves
+  // with work are not queued behind empty ones: the mixed batch of 1 .. 1000 tokens 32.5 ->
+  // 29.7 us (a second round of dispatch had held its longest sequences back). Otherwise the
+  // grid keeps the chunks of a (sequence, head group) together (4 x 4096: 252 vs 257 us).
+  const bool slow = int64_t(strides) * p.B * kC > 2 * p.tokens;
+  const dim3 grid = slow ? dim3(unsigned(p.Hv / vh), unsigned(p.B), strides) : dim3(strides, unsigned(p.Hv / vh), unsigned(p.B));
+  auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, p); };
   if (vh == 2) {
-    if (factor) hipLaunchKernelGGL((chunk_kernel<2, true>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<2, false>), grid, dim3(64), 0, stream, p);
+    if (factor) slow ? launch(chunk_kernel<2, true, true>) : launch(chunk_kernel<2, true, false>);
+    else slow ? launch(chunk_kernel<2, false, true>) : launch(chunk_kernel<2, false, false>);
   } else {
-    if (factor) hipLaunchKernelGGL((chunk_kernel<1, true>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<1, false>), grid, dim3(64), 0, stream, p);
+    if (factor) slow ? launch(chunk_kernel<1, true, true>) : launch(chunk_kernel<1, true, false>);
+    else slow ? launch(chunk_kernel<1, false, true>) : launch(chunk_kernel<1, false, false>);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
