@@ -845,7 +845,8 @@ __device__ __forceinline__ StOps read_state_ops(const lds_char* s, int chain, in
 
 // -W from K^T and the factor: pass 1's own product of the same bf16 operands, so the same bits.
 // Halves h0 .. h1 - 1 of two 32-key blocks each, so that at most four products' fp32 results
-// are live (all eight at once pushed four-chain workgroups past their register budget).
+// are live (all eight at once pushed four-chain workgroups past their register budget, and
+// those spills had made 4 x 4096 take 291 us instead of 253 with -W records).
 __device__ __forceinline__ void build_w(StOps& c, int h0, int h1) {
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1261,14 +1262,14 @@ hipError_t launch_group(const PrefillArgs& p, hipStream_t stream) {
 struct Pass2Plan {
   bool whole, wide, quads, quads1;
   // the chains form -W from its factor, which pass 1 then writes in its place: every chain
-  // in segments, and whole sequences in two-chain workgroups that average 1024 tokens or
-  // more. With such sequences every CU stages records for the whole call and its copying
-  // wave, paced by the CU's memory pipeline, takes as long per chunk as the state waves:
-  // 8 x 2048 80.6 -> 77.8 us with three fewer loads per chunk. The chains of shorter
-  // sequences outlast the others with the chip to themselves, the state waves alone set
-  // their step and the products that form -W lengthen it (the mixed batch of 1 .. 1000
-  // tokens 32.4 -> 34.5 us); four chains per workgroup share the CU's matrix pipes (4 x
-  // 4096 253 -> 291 us).
+  // in segments or in four-chain workgroups, and whole sequences in two-chain workgroups
+  // that average 1024 tokens or more. With such batches every CU stages records for the
+  // whole call and its copying wave, paced by the CU's memory pipeline, takes as long per
+  // chunk as the state waves, and pass 1 writes an eighth of -W's bytes: 8 x 2048 80.6 ->
+  // 77.8 us, 4 x 4096 252.5 -> 217.3 us (pass 1 76.8 -> 62.2 us, pass 2 178.6 -> 162.6 us).
+  // The chains of shorter sequences outlast the others with the chip to themselves, the
+  // state waves alone set their step and the products that form -W lengthen it (the mixed
+  // batch of 1 .. 1000 tokens 32.4 -> 34.5 us).
   bool factor;
 };
 inline Pass2Plan plan_pass2(const PrefillArgs& p) {
@@ -1277,7 +1278,7 @@ inline Pass2Plan plan_pass2(const PrefillArgs& p) {
   q.wide = q.whole && int64_t(p.B) * p.Hv * (p.DV / 16) * 2 >= 2048;
   q.quads = p.DV % 64 == 0 && p.segments * p.Hv * (p.DV / 32) > 256;
   q.quads1 = p.DV % 64 == 0 && p.segments * p.Hv * (std::max(p.DV, kDK) / 32) > 256;
-  q.factor = !q.whole || (!q.quads && !q.wide && p.tokens >= int64_t(1024) * p.B);
+  q.factor = !q.whole || q.quads || (!q.wide && p.tokens >= int64_t(1024) * p.B);
   return q;
 }
 
@@ -1287,7 +1288,7 @@ hipError_t launch_pass2(const PrefillArgs& p, hipStream_t stream) {
   const bool whole = q.whole, wide = q.wide, quads = q.quads, quads1 = q.quads1;
   hipError_t e;
   if (whole && quads) {
-    e = launch_group<ST, 4, 5, 0>(p, stream);
+    e = launch_group<ST, 4, 5, 0, true>(p, stream);
   } else if (wide) {
     e = launch_scan<ST, 2>(p, stream);
   } else if (whole) {
