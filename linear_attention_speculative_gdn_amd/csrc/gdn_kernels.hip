@@ -645,8 +645,9 @@ hipError_t launch_dk(int shape, int mode, bool ntl, const RecurrentArgs& p, hipS
       case 64: return launch_rec<ST, IT, 64, 2, 8, 0, true>(p, stream);    // 256
       case 128:  // 128 value rows in every shape, chosen by T as measured: one row per
                  // lane and 16 waves above 4 tokens (T = 8: 255 -> 241 us against two rows
-                 // and 8 waves), four rows and 4 waves for 2-4 tokens (T = 4: 18.1 ->
-                 // 17.4 us), two rows and 8 waves for one token (11.0 us; 11.7 with four)
+                 // and 8 waves), four rows and 4 waves for 2-4 tokens (T = 4: 17.3 us; 18.1
+                 // with one row and 16 waves, 18.0 with two rows and 8), two rows and 8 waves
+                 // for one token (11.0 us; 11.7 with four)
         if (p.T > 4) return launch_rec<ST, IT, 128, 1, 16, 0, true>(p, stream);
         if (p.T > 1)
           return ntl ? launch_rec<ST, IT, 128, 4, 4, 0, true, true>(p, stream)
